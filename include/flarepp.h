@@ -1,0 +1,124 @@
+/*
+ * flarepp.h - C ABI of the FLARE++ token mixer forward pass on MI355X (gfx950).
+ *
+ * Source: "FLARE++: Low-rank attention with attention-synthesized routing" (arXiv 2608.11519 v2),
+ * Section 3.2, Eq. 5-8, restated as one block in Appendix A.1, Eq. 11. For each batch element b and
+ * head h the mixer makes three softmax routing calls:
+ *
+ *   synthesis : Qd = softmax(Qseed . N0(S)^T / sqrt(D)) . N0(S)   softmax over the N tokens
+ *                                                                   (Eq. 6 with the shared keys and
+ *                                                                   values of Eq. 5 / Appendix A.6,
+ *                                                                   Eq. 19)
+ *   gate      : Q  = N0(Qf) + g . Qd                                (Eq. 7 / Appendix A.4, Eq. 15)
+ *   encode    : Z  = softmax(Q . K^T / sqrt(D)) . V                 softmax over the N tokens (Eq. 8)
+ *   decode    : Y  = softmax(K . Q^T / sqrt(D)) . Z                 softmax over the M latents (Eq. 8;
+ *                                                                   the decode factor is the softmax
+ *                                                                   of the transposed scores, Eq. 4)
+ *
+ * N0 is RMS normalization without a learned scale over the head dimension D (Section 3.2):
+ * N0(x) = x / sqrt(mean(x^2) + 1e-6). The pages give no epsilon; 1e-6 is this library's constant.
+ * The learned-scale normalizations of the pages (on the seeds and on the routing keys) are the
+ * caller's: Qseed and K are taken as already normalized. The gate value g is passed directly
+ * (the pages parameterize it as a sigmoid of a learned logit). The N x N mixing matrix
+ * W_dec . W_enc (rank <= M, Eq. 9) is never formed.
+ *
+ * Layouts (all row-major and contiguous, element type given by `dtype`):
+ *   K, V, S, out : [B, H, N, D]   (S = synthesis keys before normalization)
+ *   Qseed, Qf    : [H, M, D]      shared over the batch
+ *   g            : [H] float32    gate values, normally in [0, 1]
+ * All pointers are device pointers on the current HIP device. Every tensor pointer must be 16-byte
+ * aligned. `out` must not overlap any input. Inputs are read-only.
+ *
+ * Supported: dtype FLAREPP_FP32 or FLAREPP_BF16 (out has the input dtype; accumulation is fp32),
+ * D in {16, 32}, 1 <= M <= 512, N >= 0, B >= 0, H >= 0, B*H <= 65535, gfx950 devices only.
+ * B*H*N == 0 is a valid call that does nothing.
+ *
+ * Semantics: every call is asynchronous on `stream` (no host synchronization, no device-to-host
+ * copies). Results are deterministic: no atomics, fixed reduction order. Calls on different
+ * streams may run concurrently when each has its own workspace. Validation happens before anything
+ * is enqueued, so a call that returns an error has enqueued nothing. Errors raised while kernels
+ * run surface at the caller's next synchronization of `stream`, as in HIP. No C++ exception or
+ * abort crosses this interface. Inputs holding NaN or Inf give NaN outputs; finite inputs whose
+ * values exceed about 1e22 in magnitude may overflow the fp32 accumulators.
+ */
+#ifndef FLAREPP_H
+#define FLAREPP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum flarepp_status {
+  FLAREPP_OK = 0,
+  FLAREPP_INVALID_ARGUMENT = 1, /* null pointer, negative size, size overflow, bad workspace size */
+  FLAREPP_UNSUPPORTED = 2,      /* D not in {16,32}, M outside [1,512], unknown dtype, B*H too
+                                   large, or a device that is not gfx950 */
+  FLAREPP_MISALIGNED = 3,       /* a tensor pointer that is not 16-byte aligned */
+  FLAREPP_OUT_OF_MEMORY = 4,    /* workspace allocation failed */
+  FLAREPP_LAUNCH_FAILED = 5,    /* a kernel launch was rejected by the runtime */
+  FLAREPP_DEVICE_ERROR = 6      /* the HIP runtime reported an error while querying the device */
+};
+
+/* Element types of K, V, S, Qseed, Qf and out. */
+enum flarepp_dtype { FLAREPP_FP32 = 0, FLAREPP_BF16 = 1 };
+
+/*
+ * Full mixer forward (Eq. 11): out[b,h] = decode(encode(gate(synthesis(Qseed[h], S[b,h]), Qf[h],
+ * g[h]), K[b,h], V[b,h])). The library allocates its workspace with hipMallocAsync on `stream`
+ * and frees it with hipFreeAsync on the same stream.
+ */
+int flarepp_mix(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
+                hipStream_t stream);
+
+/* Bytes of device workspace that flarepp_mix_ws and flarepp_mix_debug need for these sizes, or 0
+ * when the sizes are invalid or unsupported (or when B*H*N == 0). */
+size_t flarepp_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype);
+
+/*
+ * Same as flarepp_mix, with a caller-owned device workspace of at least
+ * flarepp_workspace_bytes(...) bytes, 256-byte aligned. The workspace holds the per-chunk
+ * online-softmax partials of the two token-axis softmaxes (the log-sum-exp merge of Appendix B,
+ * Eq. 29-33, applied across token chunks of one GPU) and the latent tensors Q and Z. Its contents
+ * need no initialization and are dead after the call's kernels finish.
+ */
+int flarepp_mix_ws(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                   const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * flarepp_mix_ws that also exports the per-(b,h) latent stages as fp32 device arrays of shape
+ * [B, H, M, D] before any cast to `dtype`: Qd (synthesis output, Eq. 6), Q (gated routing queries,
+ * Eq. 7) and Z (encoder output, Eq. 8). Any of the three may be NULL.
+ */
+int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Qseed,
+                      const void* Qf, const float* g, int B, int H, int64_t N, int M, int D,
+                      int dtype, void* out, float* Qd, float* Q, float* Z, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Kernel timing. While enabled, every mixer call records a HIP event pair around each of its
+ * kernels on the call's stream. flarepp_timing_read synchronizes those events, adds their elapsed
+ * times per kernel into ms[0..n-1] and launch counts into counts[0..n-1] (n <= number of kernel
+ * kinds, see flarepp_kernel_name), clears the record and returns the number of kernel kinds.
+ * Timing state is per process; concurrent timed calls from several threads are not supported. */
+int flarepp_timing_enable(int enable);
+int flarepp_timing_read(double* ms, long long* counts, int n);
+/* Name of kernel kind `i` (0 <= i < number of kinds), NULL otherwise. */
+const char* flarepp_kernel_name(int i);
+
+/* Human-readable text of a status code. Never NULL. */
+const char* flarepp_strerror(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int flarepp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLAREPP_H */

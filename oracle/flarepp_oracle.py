@@ -1,0 +1,177 @@
+"""Plain float64 CPU oracle of the FLARE++ mixer forward pass.
+
+TEST INFRASTRUCTURE ONLY. This module is the reference against which the GPU library is checked.
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark may import it; the
+mixer library never calls it and has no CPU fallback.
+
+It evaluates the definitions of "FLARE++: Low-rank attention with attention-synthesized routing"
+(arXiv 2608.11519 v2) literally, in numpy float64, and shares no code with the GPU path. Softmaxes
+are two-pass (row maximum, then the normalized exponentials); the routing factors are formed
+explicitly. The only blocking is over tokens when a factor would not fit in memory, and it keeps
+the same two-pass definition (see ``sdpa_tokens``).
+
+Readings where the pages leave a step open:
+* RMS normalization N0 uses epsilon 1e-6 inside the square root (the pages state none).
+* Qseed and K arrive already normalized by the caller (the learned-scale normalization N_a of
+  Section 3.2 / Appendix A.3-A.4 is outside the mixer); N0 is applied to S and to Qf only.
+* g is the gate value itself (the pages write g = sigmoid(gamma)).
+* Decode normalizes over the M latents (softmax of the transposed scores, Section 3.1, Eq. 4).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+#: Epsilon of the affine-free RMS normalization N0.
+RMS_EPS = 1e-6
+
+
+def rms_normalize(x: np.ndarray) -> np.ndarray:
+    """N0: divide each row (last axis, the head width D) by its root-mean-square.
+
+    Section 3.2 (definition of N0 next to Eq. 5) and Appendix A.4, Eq. 16: every row of N0(x) has
+    unit RMS (up to the epsilon).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + RMS_EPS)
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis, computed in two passes: subtract the row maximum, exponentiate,
+    divide by the row sum. The shift is the identity of Appendix B.3, Eq. 29."""
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Scaled dot-product attention, Section 3.1, Eq. 1: softmax(q k^T / sqrt(D)) v, with the
+    softmax over the rows of k (the keys). q: [Nq, D], k: [Nk, D], v: [Nk, Dv]."""
+    D = q.shape[-1]
+    return softmax_rows(q @ k.T / math.sqrt(D)) @ v
+
+
+def sdpa_tokens(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int) -> np.ndarray:
+    """Eq. 1 for a short query set against a long key set, with the keys taken in blocks of
+    ``block`` rows so that the [Nq, Nk] score matrix is never held whole. First pass: the row maxima
+    over all keys. Second pass: the exponentials shifted by those maxima, summed and applied to v.
+    Equal to ``sdpa`` up to summation order."""
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D)
+    n = k.shape[0]
+    row_max = np.full(q.shape[0], -np.inf)
+    for a in range(0, n, block):
+        row_max = np.maximum(row_max, (q @ k[a:a + block].T * scale).max(axis=1))
+    den = np.zeros(q.shape[0])
+    num = np.zeros((q.shape[0], v.shape[1]))
+    for a in range(0, n, block):
+        e = np.exp(q @ k[a:a + block].T * scale - row_max[:, None])
+        den += e.sum(axis=1)
+        num += e @ v[a:a + block]
+    return num / den[:, None]
+
+
+def synthesis(Qseed: np.ndarray, S: np.ndarray, block: int | None = None) -> np.ndarray:
+    """Routing-query correction Qd (Section 3.2, Eq. 5-6; Appendix A.6, Eq. 19): the seeds attend
+    over the N0-normalized synthesis keys, which are also the values. Qseed [M, D], S [N, D]."""
+    keys = rms_normalize(S)
+    if block is None:
+        return sdpa(Qseed, keys, keys)
+    return sdpa_tokens(Qseed, keys, keys, block)
+
+
+def gate(Qf: np.ndarray, Qd: np.ndarray, g: float) -> np.ndarray:
+    """Routing queries Q = N0(Qf) + g Qd (Section 3.2, Eq. 7; Appendix A.4, Eq. 15). Qd itself is
+    not normalized (Appendix A.4, "Why the synthesized query is not normalized")."""
+    return rms_normalize(Qf) + float(g) * np.asarray(Qd, dtype=np.float64)
+
+
+def encode(Q: np.ndarray, K: np.ndarray, V: np.ndarray, block: int | None = None) -> np.ndarray:
+    """Latent values Z = SDPA(Q, K, V) (Eq. 8, first call): softmax over the N tokens."""
+    if block is None:
+        return sdpa(Q, K, V)
+    return sdpa_tokens(Q, K, V, block)
+
+
+def decode(K: np.ndarray, Q: np.ndarray, Z: np.ndarray, block: int | None = None) -> np.ndarray:
+    """Token outputs Y = SDPA(K, Q, Z) (Eq. 8, second call): the keys K act as queries against the
+    M routing queries, softmax over the M latents. Rows are independent, so blocking over the
+    query tokens changes nothing."""
+    if block is None:
+        return sdpa(K, Q, Z)
+    return np.concatenate([sdpa(K[a:a + block], Q, Z) for a in range(0, K.shape[0], block)])
+
+
+def mix_head(K, V, S, Qseed, Qf, g, block: int | None = None) -> dict:
+    """One (batch, head) slice of the mixer, Appendix A.1, Eq. 11. Returns the stages
+    ``Qd`` [M, D], ``Q`` [M, D], ``Z`` [M, D] and the output ``Y`` [N, D]."""
+    Qd = synthesis(Qseed, S, block)
+    Q = gate(Qf, Qd, g)
+    Z = encode(Q, K, V, block)
+    Y = decode(K, Q, Z, block)
+    return {"Qd": Qd, "Q": Q, "Z": Z, "Y": Y}
+
+
+def mix(K, V, S, Qseed, Qf, g, block: int | None = None) -> dict:
+    """The mixer over all batch elements and heads. K, V, S: [B, H, N, D]; Qseed, Qf: [H, M, D]
+    (shared over the batch); g: [H]. Returns stacked stages Qd, Q, Z [B, H, M, D] and Y [B, H, N, D]."""
+    B, H = K.shape[:2]
+    out = {"Qd": [], "Q": [], "Z": [], "Y": []}
+    for b in range(B):
+        rows = {key: [] for key in out}
+        for h in range(H):
+            r = mix_head(K[b, h], V[b, h], S[b, h], Qseed[h], Qf[h], g[h], block)
+            for key in out:
+                rows[key].append(r[key])
+        for key in out:
+            out[key].append(np.stack(rows[key]))
+    return {key: np.stack(val) for key, val in out.items()}
+
+
+def routing_factors(Q: np.ndarray, K: np.ndarray):
+    """The two routing factors of Section 3.1, Eq. 3-4, for queries Q [M, D] and keys K [N, D]:
+    W_enc = softmax(S) [M, N] (over tokens) and W_dec = softmax(S^T) [N, M] (over latents), with
+    S = Q K^T / sqrt(D)."""
+    Sc = Q @ K.T / math.sqrt(Q.shape[-1])
+    return softmax_rows(Sc), softmax_rows(Sc.T)
+
+
+def mixing_matrix(Q: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """The N x N operator W_eff = W_dec W_enc of Eq. 4 / Eq. 9 (rank <= M). Small N only."""
+    W_enc, W_dec = routing_factors(Q, K)
+    return W_dec @ W_enc
+
+
+def flare(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Fixed-query FLARE, Section 3.1, Eq. 3: Z = SDPA(Q, K, V), Y = SDPA(K, Q, Z)."""
+    return decode(K, Q, encode(Q, K, V))
+
+
+def encode_sharded(Q: np.ndarray, K: np.ndarray, V: np.ndarray, bounds) -> tuple:
+    """The token-sharded encoder of Appendix B.2-B.3: each shard r (token range bounds[r]) gives
+    its local log-normalizer L_r (Eq. 25) and local output Z_r (Eq. 26); the stable schedule of
+    Eq. 30-33 merges them: L_max = max_r L_r, d_r = exp(L_r - L_max), U_r = d_r Z_r, d = sum d_r,
+    U = sum U_r, Z = U / d, L = L_max + log d. An empty shard returns L_r = -inf and Z_r = 0
+    (Appendix B.3). Returns (Z, L)."""
+    s = 1.0 / math.sqrt(Q.shape[-1])
+    Ls, Zs = [], []
+    for a, b in bounds:
+        if b <= a:
+            Ls.append(np.full(Q.shape[0], -np.inf))
+            Zs.append(np.zeros((Q.shape[0], V.shape[1])))
+            continue
+        Sr = s * Q @ K[a:b].T
+        m = Sr.max(axis=1)
+        Ls.append(m + np.log(np.exp(Sr - m[:, None]).sum(axis=1)))
+        Zs.append(softmax_rows(Sr) @ V[a:b])
+    L_max = np.max(np.stack(Ls), axis=0)
+    d_r = [np.exp(L - L_max) for L in Ls]
+    d = np.sum(d_r, axis=0)
+    U = np.sum([dr[:, None] * Zr for dr, Zr in zip(d_r, Zs)], axis=0)
+    return U / d[:, None], L_max + np.log(d)
+
+
+def decode_rows(K_rows: np.ndarray, Q: np.ndarray, Z: np.ndarray) -> np.ndarray:
+    """Decode (Eq. 8, second call) for a chosen subset of token rows only."""
+    return sdpa(K_rows, Q, Z)
