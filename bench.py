@@ -1,0 +1,166 @@
+"""Throughput of the FLARE++ mixer forward pass on one MI355X.
+
+A step is one full mixer call (synthesis, gate, encode, decode over every (b, h)) on the
+million-token workload: B=1, H=8, N=2^20 tokens on a random closed surface, M=512 latents, D=32,
+bf16 inputs with fp32 accumulation, inputs resident in HBM. The JSON line reports tokens*heads/s,
+the achieved TFLOP/s (12 N M D flops per head), per-kernel event timings, the roofline position of
+the dominant kernel and the float64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense).
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+# Measured v_exp_f32 issue rate on gfx950: 32 per clock per CU (quarter of the fp32 FMA rate).
+PEAK_EXP_PER_S = 256 * 2.4e9 * 32
+
+KERNELS = ["synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"]
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
+    return ap.parse_args()
+
+
+def kernel_flops(name, w):
+    """Algorithmic flops of one launch: each of the three routing calls costs 4 N M D per (b, h)
+    (2 for the scores, 2 for the probabilities times values); merges are not counted."""
+    per = 4.0 * w.N * w.M * w.D * w.B * w.H
+    return per if name in ("synthesis_partial", "encode_partial", "decode") else 0.0
+
+
+def cpu_baseline(w, ntok):
+    """The float64 oracle on one head of the same workload, first `ntok` tokens."""
+    import numpy as np
+    import oracle
+    from workloads import to_float64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    n = min(ntok, w.N)
+    args = [to_float64(w.K[0, 0, :n], w.dtype), to_float64(w.V[0, 0, :n], w.dtype),
+            to_float64(w.S[0, 0, :n], w.dtype), to_float64(w.Qseed[0], w.dtype), to_float64(w.Qf[0], w.dtype),
+            float(w.g[0])]
+    t0 = time.perf_counter()
+    oracle.mix_head(*args, block=65536)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"one head (b=0, h=0), first {n} of {w.N} tokens, M={w.M}, D={w.D}, float64 numpy; "
+                      f"{dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (the mixer shards over "
+              "(b, h) or over tokens, see DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_latent_routing_amd as fl
+    from workloads import make_workload
+
+    fl.lib()
+    w = make_workload(args.config)
+    dev = {}
+    for name in ("K", "V", "S", "Qseed", "Qf"):
+        arr = np.ascontiguousarray(getattr(w, name))
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" else torch.from_numpy(arr)
+        dev[name] = t.cuda()
+    dev["g"] = torch.from_numpy(w.g).cuda()
+    out = torch.empty_like(dev["K"])
+    dt_code = fl.FLAREPP_BF16 if w.dtype == "bf16" else fl.FLAREPP_FP32
+    ws = torch.empty(fl.flarepp_workspace_bytes(w.B, w.H, w.N, w.M, w.D, dt_code), dtype=torch.uint8, device="cuda")
+    call = lambda: fl.flarepp_mix_ws(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"], out=out,
+                                     workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps bracketed by synchronizations, with HIP events on the library's stream
+    # around each kernel (per-kernel durations) and around the whole region.
+    fl.flarepp_timing_enable(True)
+    fl.flarepp_timing_read()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fl.flarepp_timing_enable(False)
+    per_kernel = fl.flarepp_timing_read()
+    dev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(dev_ms, wall * 1e3) / args.steps
+
+    tok_heads = w.B * w.H * w.N
+    value = tok_heads / (ms_per_step * 1e-3)
+    flops = 12.0 * w.N * w.M * w.D * w.B * w.H
+    exps = 3.0 * w.N * w.M * w.B * w.H
+    es = 2 if w.dtype == "bf16" else 4
+    hbm_bytes = 5.0 * w.N * w.D * w.B * w.H * es + 2.0 * w.H * w.M * w.D * es
+    tflops = flops / (ms_per_step * 1e-3) * 1e-12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+
+    kern = {k: {"ms_avg": per_kernel[k][0] / max(per_kernel[k][1], 1), "launches": per_kernel[k][1]} for k in KERNELS}
+    dom = max(KERNELS, key=lambda k: kern[k]["ms_avg"])
+    dom_ms = kern[dom]["ms_avg"]
+    achieved = kernel_flops(dom, w) / (dom_ms * 1e-3) * 1e-12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel_ms": round(dom_ms, 4), "flops_per_launch": kernel_flops(dom, w),
+                "exp_frac": round((w.N * w.M * w.B * w.H) / (dom_ms * 1e-3) / PEAK_EXP_PER_S, 4)}
+
+    res = {
+        "metric": "FLARE++ mixer tokens*heads/s (N=1M, M=512)",
+        "value": value,
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"FLARE++ mixer forward, {w.name}", "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D,
+                   "inputs": "points on a random closed surface, sinusoidal-feature K/V/S" if args.config == 5 else "see workloads/gen.py"},
+        "tflops": tflops,
+        "mfma_frac": tflops / peak,
+        "hbm_frac": hbm_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "exp_frac": exps / (ms_per_step * 1e-3) / PEAK_EXP_PER_S,
+        "kernels": {k: round(v["ms_avg"], 4) for k, v in kern.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+"""Python binding of the FLARE++ mixer library (libflarepp.so, C ABI in include/flarepp.h).
+
+Argument marshalling only: torch tensors supply device memory and the stream; every step of the
+mixer runs in the library's HIP kernels. The functions carry the C entry points' names. There is
+no CPU fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libflarepp.so")
+
+FLAREPP_OK = 0
+FLAREPP_INVALID_ARGUMENT = 1
+FLAREPP_UNSUPPORTED = 2
+FLAREPP_MISALIGNED = 3
+FLAREPP_OUT_OF_MEMORY = 4
+FLAREPP_LAUNCH_FAILED = 5
+FLAREPP_DEVICE_ERROR = 6
+FLAREPP_FP32 = 0
+FLAREPP_BF16 = 1
+
+_lib = None
+
+
+class FlareppError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {flarepp_strerror(status)} (status {status})" if what else
+                         f"{flarepp_strerror(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with its C signatures declared. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rank_latent_routing_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    mix_args = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp]
+    L.flarepp_mix.argtypes = mix_args + [vp]
+    L.flarepp_mix.restype = i32
+    L.flarepp_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.flarepp_workspace_bytes.restype = sz
+    L.flarepp_mix_ws.argtypes = mix_args + [vp, sz, vp]
+    L.flarepp_mix_ws.restype = i32
+    L.flarepp_mix_debug.argtypes = mix_args + [vp, vp, vp, vp, sz, vp]
+    L.flarepp_mix_debug.restype = i32
+    L.flarepp_timing_enable.argtypes = [i32]
+    L.flarepp_timing_enable.restype = i32
+    L.flarepp_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), i32]
+    L.flarepp_timing_read.restype = i32
+    L.flarepp_kernel_name.argtypes = [i32]
+    L.flarepp_kernel_name.restype = ctypes.c_char_p
+    L.flarepp_strerror.argtypes = [i32]
+    L.flarepp_strerror.restype = ctypes.c_char_p
+    L.flarepp_version.argtypes = []
+    L.flarepp_version.restype = i32
+    _lib = L
+    return L
+
+
+def flarepp_strerror(status: int) -> str:
+    return lib().flarepp_strerror(int(status)).decode()
+
+
+def flarepp_version() -> int:
+    return int(lib().flarepp_version())
+
+
+def flarepp_kernel_name(i: int):
+    r = lib().flarepp_kernel_name(int(i))
+    return None if r is None else r.decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FLAREPP_FP32
+    if t.dtype == torch.bfloat16:
+        return FLAREPP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _shapes(K, V, S, Qseed, Qf, g):
+    import torch
+    if K.dim() != 4:
+        raise ValueError("K, V, S must be [B, H, N, D]")
+    B, H, N, D = K.shape
+    if V.shape != K.shape or S.shape != K.shape:
+        raise ValueError("K, V, S must have the same shape")
+    if Qseed.dim() != 3 or Qseed.shape[0] != H or Qseed.shape[2] != D or Qf.shape != Qseed.shape:
+        raise ValueError("Qseed and Qf must be [H, M, D]")
+    if g.shape != (H,) or g.dtype != torch.float32:
+        raise ValueError("g must be a float32 tensor of shape [H]")
+    for t in (K, V, S, Qseed, Qf, g):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    for t in (V, S, Qseed, Qf):
+        if t.dtype != K.dtype:
+            raise ValueError("K, V, S, Qseed, Qf must share one dtype")
+    return B, H, N, Qseed.shape[1], D
+
+
+def _stream_ptr(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != FLAREPP_OK:
+        raise FlareppError(status, what)
+
+
+def flarepp_workspace_bytes(B: int, H: int, N: int, M: int, D: int, dtype: int) -> int:
+    return int(lib().flarepp_workspace_bytes(B, H, N, M, D, dtype))
+
+
+def flarepp_mix(K, V, S, Qseed, Qf, g, out=None, stream=None):
+    """FLARE++ mixer forward. K, V, S: [B, H, N, D]; Qseed, Qf: [H, M, D] (float32 or bfloat16,
+    one dtype, on one GPU); g: [H] float32 gate values. Returns out [B, H, N, D]. The library
+    allocates its workspace stream-ordered."""
+    import torch
+    B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    if out is None:
+        out = torch.empty_like(K)
+    st = lib().flarepp_mix(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D,
+                           _dtype_code(K), _ptr(out), _stream_ptr(stream, K.device))
+    _check(st, "flarepp_mix")
+    return out
+
+
+def _workspace(B, H, N, M, D, dt, device, workspace):
+    import torch
+    need = flarepp_workspace_bytes(B, H, N, M, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def flarepp_mix_ws(K, V, S, Qseed, Qf, g, out=None, workspace=None, stream=None):
+    """flarepp_mix with a torch-owned workspace (a uint8 tensor of flarepp_workspace_bytes bytes;
+    allocated here when not given)."""
+    import torch
+    B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    dt = _dtype_code(K)
+    if out is None:
+        out = torch.empty_like(K)
+    workspace, _ = _workspace(B, H, N, M, D, dt, K.device, workspace)
+    st = lib().flarepp_mix_ws(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D, dt,
+                              _ptr(out), _ptr(workspace), workspace.numel(), _stream_ptr(stream, K.device))
+    _check(st, "flarepp_mix_ws")
+    return out
+
+
+def flarepp_mix_debug(K, V, S, Qseed, Qf, g, out=None, workspace=None, stream=None):
+    """flarepp_mix_ws that also returns the fp32 latent stages Qd, Q, Z, each [B, H, M, D]."""
+    import torch
+    B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    dt = _dtype_code(K)
+    if out is None:
+        out = torch.empty_like(K)
+    workspace, _ = _workspace(B, H, N, M, D, dt, K.device, workspace)
+    Qd, Q, Z = (torch.empty((B, H, M, D), dtype=torch.float32, device=K.device) for _ in range(3))
+    st = lib().flarepp_mix_debug(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D, dt,
+                                 _ptr(out), _ptr(Qd), _ptr(Q), _ptr(Z), _ptr(workspace), workspace.numel(),
+                                 _stream_ptr(stream, K.device))
+    _check(st, "flarepp_mix_debug")
+    return out, Qd, Q, Z
+
+
+def flarepp_timing_enable(enable: bool = True) -> None:
+    lib().flarepp_timing_enable(1 if enable else 0)
+
+
+def flarepp_timing_read() -> dict:
+    """Per-kernel event timings accumulated since the last read: {name: (total_ms, launches)}."""
+    n = 16
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_longlong * n)()
+    k = lib().flarepp_timing_read(ms, cnt, n)
+    if k < 0:
+        raise FlareppError(-k, "flarepp_timing_read")
+    return {flarepp_kernel_name(i): (ms[i], cnt[i]) for i in range(k)}
+
+
+__all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
+           "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
+           "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

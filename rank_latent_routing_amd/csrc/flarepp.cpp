@@ -1,0 +1,306 @@
+// Host side of the FLARE++ mixer library: argument validation, launch planning, workspace layout,
+// the C ABI declared in include/flarepp.h, and optional per-kernel event timing.
+//
+// The mixer (arXiv 2608.11519 v2, Appendix A.1 Eq. 11) runs as five kernels on the caller's
+// stream: synthesis partials, merge + gate, encode partials, merge, decode. The two token-axis
+// softmaxes are split over token chunks whose online-softmax partials are combined with the
+// log-sum-exp merge of Appendix B.3 (Eq. 29-33), chunks standing in for the pages' ranks.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "flarepp.h"
+#include "kernels.h"
+
+namespace {
+
+using flarepp::kStage;
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kNumKinds = 5;
+const char* const kKindNames[kNumKinds] = {"synthesis_partial", "merge_gate", "encode_partial",
+                                           "merge", "decode"};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Launch plan and workspace layout for one problem shape. The same function serves
+// flarepp_workspace_bytes and the launches, so both always agree.
+struct Plan {
+  int BH = 0;
+  int Mp16 = 0, Mp32 = 0;
+  int part_plan = 0;  // kernel variant: 0 (16 latents/wave, 4 waves) .. 3 (64 latents/wave, 8 waves)
+  int nlg = 1;        // latent groups (workgroups per chunk)
+  int64_t chunk = 0;
+  int nchunk = 0;
+  int dec_gx = 0;
+  int64_t dec_tpw = 0;
+  size_t off_acc = 0, off_l = 0, off_m = 0, off_q = 0, off_z = 0, total = 0;
+};
+
+Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
+  Plan p;
+  p.BH = B * H;
+  p.Mp16 = (M + 15) / 16 * 16;
+  p.Mp32 = (M + 31) / 32 * 32;
+  int lpw, nw;
+  if (p.Mp16 <= 64) { p.part_plan = 0; lpw = 16; nw = 4; }
+  else if (p.Mp16 <= 128) { p.part_plan = 1; lpw = 32; nw = 4; }
+  else if (p.Mp16 <= 256) { p.part_plan = 2; lpw = 64; nw = 4; }
+  else { p.part_plan = 3; lpw = 64; nw = 8; }
+  p.nlg = (int)ceil_div(p.Mp16, (int64_t)lpw * nw);
+  // Enough workgroups to fill 256 CUs about twice (8-wave workgroups) or four times (4-wave).
+  const int64_t target = nw == 8 ? 512 : 1024;
+  int64_t nchunk = ceil_div(target, (int64_t)p.BH * p.nlg);
+  nchunk = nchunk < 1 ? 1 : nchunk;
+  const int64_t max_chunks = ceil_div(N, kStage);
+  if (nchunk > max_chunks) nchunk = max_chunks;
+  p.chunk = ceil_div(ceil_div(N, nchunk), kStage) * kStage;
+  p.nchunk = (int)ceil_div(N, p.chunk);
+  // Decode: about 512 workgroups of kDecodeWaves waves, token ranges a multiple of 64.
+  int64_t gx = ceil_div(512, p.BH);
+  const int64_t max_gx = ceil_div(N, 64 * flarepp::kDecodeWaves);
+  if (gx > max_gx) gx = max_gx;
+  if (gx < 1) gx = 1;
+  p.dec_tpw = ceil_div(ceil_div(N, gx), 64) * 64;
+  p.dec_gx = (int)ceil_div(N, p.dec_tpw);
+
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t nrow = (size_t)p.BH * p.nchunk * p.Mp16;
+  size_t off = 0;
+  p.off_acc = off; off = align256(off + nrow * D * sizeof(float));
+  p.off_l = off;   off = align256(off + nrow * sizeof(float));
+  p.off_m = off;   off = align256(off + nrow * sizeof(float));
+  const size_t qparts = dtype == FLAREPP_BF16 ? 2 : 1;  // bf16 routing queries as a hi/lo pair
+  p.off_q = off;   off = align256(off + (size_t)p.BH * p.Mp32 * qparts * D * es);
+  p.off_z = off;   off = align256(off + (size_t)p.BH * p.Mp32 * D * es);
+  p.total = off;
+  return p;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Size-only validation. Returns OK, or the status to report. Sets *empty when B*H*N == 0.
+int validate_sizes(int B, int H, int64_t N, int M, int D, int dtype, bool* empty) {
+  *empty = false;
+  if (dtype != FLAREPP_FP32 && dtype != FLAREPP_BF16) return FLAREPP_UNSUPPORTED;
+  if (B < 0 || H < 0 || N < 0 || M < 1) return FLAREPP_INVALID_ARGUMENT;
+  if (D != 16 && D != 32) return FLAREPP_UNSUPPORTED;
+  if (M > 512) return FLAREPP_UNSUPPORTED;
+  if ((int64_t)B * H > 65535) return FLAREPP_UNSUPPORTED;
+  // Element counts must stay far from int64 overflow (the kernels index with int64).
+  if (N > ((int64_t)1 << 40) || (int64_t)B * H * N > ((int64_t)1 << 50)) return FLAREPP_INVALID_ARGUMENT;
+  if ((int64_t)B * H * N == 0) *empty = true;
+  return FLAREPP_OK;
+}
+
+// Device check, cached per device ordinal.
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLAREPP_DEVICE_ERROR;
+  static std::mutex mu;
+  static std::vector<int> cache;  // 0 unknown, 1 gfx950, 2 other
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLAREPP_DEVICE_ERROR;
+    cache[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return cache[dev] == 1 ? FLAREPP_OK : FLAREPP_UNSUPPORTED;
+}
+
+// ---- per-kernel event timing
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  struct Rec { int kind; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+template <typename F>
+hipError_t run_kernel(int kind, hipStream_t st, F&& launch) {
+  Timing& t = timing();
+  if (!t.enabled) return launch();
+  std::lock_guard<std::mutex> lock(t.mu);
+  hipEvent_t a = t.get(), b = t.get();
+  if (a) (void)hipEventRecord(a, st);
+  hipError_t e = launch();
+  if (b) (void)hipEventRecord(b, st);
+  if (a && b) t.pending.push_back({kind, a, b});
+  return e;
+}
+
+int validate_pointers(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                      const float* g, int B, int H, int64_t N, int M, int D, int dtype, const void* out) {
+  if (!K || !V || !S || !Qseed || !Qf || !g || !out) return FLAREPP_INVALID_ARGUMENT;
+  const void* ptrs[] = {K, V, S, Qseed, Qf, g, out};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return FLAREPP_MISALIGNED;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t nbig = (size_t)B * H * N * D * es, nq = (size_t)H * M * D * es;
+  if (overlaps(out, nbig, K, nbig) || overlaps(out, nbig, V, nbig) || overlaps(out, nbig, S, nbig) ||
+      overlaps(out, nbig, Qseed, nq) || overlaps(out, nbig, Qf, nq) || overlaps(out, nbig, g, H * sizeof(float)))
+    return FLAREPP_INVALID_ARGUMENT;
+  return FLAREPP_OK;
+}
+
+int enqueue(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
+            int B, int H, int64_t N, int M, int D, int dtype, void* out, float* dQd, float* dQ, float* dZ,
+            void* ws, const Plan& p, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(w + p.off_acc);
+  float* pl = reinterpret_cast<float*>(w + p.off_l);
+  float* pm = reinterpret_cast<float*>(w + p.off_m);
+  void* qbuf = w + p.off_q;
+  void* zbuf = w + p.off_z;
+  const int gx_part = p.nchunk * p.nlg;
+
+  flarepp::PartialArgs pa{};
+  pa.K = S; pa.V = S; pa.Q = Qseed; pa.H = H; pa.Mq = M; pa.Mp = p.Mp16; pa.N = N;
+  pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.part_acc = acc; pa.part_l = pl; pa.part_m = pm;
+  if (run_kernel(0, st, [&] { return flarepp::launch_partial(pa, dtype, D, true, p.part_plan, gx_part, p.BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  flarepp::MergeArgs ma{};
+  ma.part_acc = acc; ma.part_l = pl; ma.part_m = pm; ma.nchunk = p.nchunk; ma.Mp = p.Mp16; ma.M = M;
+  ma.Mout = p.Mp32; ma.H = H; ma.Qf = Qf; ma.g = g; ma.out = qbuf; ma.dbg_qd = dQd; ma.dbg_out = dQ;
+  if (run_kernel(1, st, [&] { return flarepp::launch_merge(ma, dtype, D, true, p.BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  pa.K = K; pa.V = V; pa.Q = qbuf; pa.Mq = p.Mp32;
+  if (run_kernel(2, st, [&] { return flarepp::launch_partial(pa, dtype, D, false, p.part_plan, gx_part, p.BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  ma.Qf = nullptr; ma.g = nullptr; ma.out = zbuf; ma.dbg_qd = nullptr; ma.dbg_out = dZ;
+  if (run_kernel(3, st, [&] { return flarepp::launch_merge(ma, dtype, D, false, p.BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  flarepp::DecodeArgs da{};
+  da.K = K; da.Q = qbuf; da.Z = zbuf; da.out = out; da.N = N; da.M = M; da.Mp = p.Mp32; da.tokens_per_wg = p.dec_tpw;
+  if (run_kernel(4, st, [&] { return flarepp::launch_decode(da, dtype, D, p.dec_gx, p.BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  return FLAREPP_OK;
+}
+
+int mix_common(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
+               int B, int H, int64_t N, int M, int D, int dtype, void* out, float* dQd, float* dQ, float* dZ,
+               void* ws, size_t ws_bytes, bool own_ws, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  rc = validate_pointers(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out);
+  if (rc != FLAREPP_OK) return rc;
+  const Plan p = make_plan(B, H, N, M, D, dtype);
+  if (!own_ws) {
+    if (!ws || ws_bytes < p.total) return FLAREPP_INVALID_ARGUMENT;
+    if ((uintptr_t)ws & 255) return FLAREPP_MISALIGNED;
+  }
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  if (own_ws) {
+    if (hipMallocAsync(&ws, p.total, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLAREPP_OUT_OF_MEMORY;
+    }
+  }
+  rc = enqueue(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, dQd, dQ, dZ, ws, p, st);
+  if (own_ws) (void)hipFreeAsync(ws, st);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flarepp_mix(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
+                int B, int H, int64_t N, int M, int D, int dtype, void* out, hipStream_t stream) {
+  return mix_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, nullptr, nullptr, nullptr, nullptr, 0,
+                    true, stream);
+}
+
+size_t flarepp_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype) {
+  bool empty = false;
+  if (validate_sizes(B, H, N, M, D, dtype, &empty) != FLAREPP_OK || empty) return 0;
+  return make_plan(B, H, N, M, D, dtype).total;
+}
+
+int flarepp_mix_ws(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
+                   int B, int H, int64_t N, int M, int D, int dtype, void* out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return mix_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, nullptr, nullptr, nullptr, workspace,
+                    workspace_bytes, false, stream);
+}
+
+int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                      const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out, float* Qd,
+                      float* Q, float* Z, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const void* dbg[] = {Qd, Q, Z};
+  for (const void* p : dbg)
+    if ((uintptr_t)p & 15) return FLAREPP_MISALIGNED;
+  return mix_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, Qd, Q, Z, workspace, workspace_bytes,
+                    false, stream);
+}
+
+int flarepp_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.enabled = enable != 0;
+  return FLAREPP_OK;
+}
+
+int flarepp_timing_read(double* ms, long long* counts, int n) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  int rc = FLAREPP_OK;
+  for (auto& r : t.pending) {
+    float e = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&e, r.a, r.b) != hipSuccess) {
+      rc = FLAREPP_DEVICE_ERROR;
+    } else if (r.kind < n) {
+      if (ms) ms[r.kind] += e;
+      if (counts) counts[r.kind] += 1;
+    }
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  return rc == FLAREPP_OK ? kNumKinds : -rc;
+}
+
+const char* flarepp_kernel_name(int i) { return (i >= 0 && i < kNumKinds) ? kKindNames[i] : nullptr; }
+
+const char* flarepp_strerror(int status) {
+  switch (status) {
+    case FLAREPP_OK: return "ok";
+    case FLAREPP_INVALID_ARGUMENT: return "invalid argument";
+    case FLAREPP_UNSUPPORTED: return "unsupported shape, dtype or device";
+    case FLAREPP_MISALIGNED: return "tensor pointer not 16-byte aligned (workspace: 256-byte)";
+    case FLAREPP_OUT_OF_MEMORY: return "workspace allocation failed";
+    case FLAREPP_LAUNCH_FAILED: return "kernel launch failed";
+    case FLAREPP_DEVICE_ERROR: return "HIP runtime error while querying the device";
+    default: return "unknown status";
+  }
+}
+
+int flarepp_version(void) { return kVersion; }
+
+}  // extern "C"

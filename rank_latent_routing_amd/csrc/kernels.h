@@ -1,0 +1,67 @@
+// Internal interface between the host library (flarepp.cpp) and the HIP kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace flarepp {
+
+// Tokens per LDS stage of the split-N partial kernels.
+constexpr int kStage = 128;
+// Waves per decode workgroup.
+constexpr int kDecodeWaves = 8;
+
+// One split-N softmax pass (synthesis or encode) over [BH, N, D] keys/values.
+struct PartialArgs {
+  const void* K;   // keys [BH][N][D] (synthesis: the un-normalized synthesis keys S)
+  const void* V;   // values [BH][N][D] (unused by synthesis: values are the normalized keys)
+  const void* Q;   // query rows: synthesis Qseed [H][Mq][D]; encode c*Q [BH][Mq][P][D]
+                   // (P = 2 parts hi, lo for bf16; 1 for fp32)
+  int H;           // heads (synthesis queries are indexed by bh % H)
+  int Mq;          // rows per query block (rows >= Mq read as zero)
+  int Mp;          // latent rows in the partial buffers (M rounded up to 16)
+  int64_t N;       // tokens
+  int64_t chunk;   // tokens per chunk, a multiple of kStage
+  int nchunk;      // chunks per (b, h)
+  float* part_acc; // [BH][nchunk][Mp][D]
+  float* part_l;   // [BH][nchunk][Mp]
+  float* part_m;   // [BH][nchunk][Mp]
+};
+
+// Log-sum-exp merge of the chunk partials, with or without the gate.
+struct MergeArgs {
+  const float* part_acc;
+  const float* part_l;
+  const float* part_m;
+  int nchunk;
+  int Mp;          // rows of the partial buffers
+  int M;           // valid latents
+  int Mout;        // rows of the output block per (b, h) (M rounded up to 32; extra rows zero)
+  int H;
+  const void* Qf;  // gate only: [H][M][D] dtype
+  const float* g;  // gate only: [H]
+  void* out;       // gate: c*Q [BH][Mout][P][D] (P parts as above); merge: Z [BH][Mout][D]
+  float* dbg_qd;   // optional fp32 [BH][M][D] (gate only): Qd
+  float* dbg_out;  // optional fp32 [BH][M][D]: Q (gate) or Z (merge)
+};
+
+struct DecodeArgs {
+  const void* K;   // [BH][N][D]
+  const void* Q;   // c*Q [BH][Mp][P][D]
+  const void* Z;   // Z [BH][Mp][D]
+  void* out;       // [BH][N][D]
+  int64_t N;
+  int M;
+  int Mp;          // M rounded up to 32
+  int64_t tokens_per_wg;
+};
+
+hipError_t launch_partial(const PartialArgs& a, int dtype, int D, bool synth, int plan, int grid_x,
+                          int grid_y, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int grid_x, int grid_y,
+                         hipStream_t stream);
+size_t decode_lds_bytes(int dtype, int D, int Mp);
+
+}  // namespace flarepp

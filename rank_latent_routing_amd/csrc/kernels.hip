@@ -1,0 +1,875 @@
+// HIP kernels of the FLARE++ mixer forward pass for gfx950 (CDNA4).
+//
+// Method: "FLARE++: Low-rank attention with attention-synthesized routing" (arXiv 2608.11519 v2),
+// Section 3.2 Eq. 5-8 (one block: Appendix A.1 Eq. 11). Three softmax routing calls per
+// (batch, head): synthesis and encode normalize over the N tokens, decode over the M latents.
+//
+// Kernel plan (one launch each, in stream order):
+//   partial<SYNTH>  split-N online-softmax partials of the synthesis call; the RMS normalization
+//                   of S is fused into the tile load and S serves as both keys and values.
+//   merge_gate      log-sum-exp merge of the chunk partials (Appendix B.3 Eq. 29-33, chunks in the
+//                   role of the pages' ranks) then Q = N0(Qf) + g Qd in fp32 (Eq. 7).
+//   partial<ENC>    the same engine for the encode call, keys K, values V.
+//   merge           log-sum-exp merge -> Z.
+//   decode          Q and Z resident in LDS; every token's scores against all M latents, softmax
+//                   over M, product with Z.
+//
+// Numerics. Every logit is computed directly in log2 units: the query operand of each call
+// carries the factor c = log2(e)/sqrt(D) (folded into the normalized synthesis keys, and into Q
+// when merge_gate casts it), so one v_exp_f32 per score evaluates exp(q.k/sqrt(D)). A softmax is
+// invariant to the shift subtracted from its logits (Appendix B.3 Eq. 29); when the Cauchy-Schwarz
+// bound |logit| <= ||c q|| ||k|| of a tile is at most kFastBound (in log2 units) the kernels use
+// shift 0, which keeps every exponential in [2^-30, 2^30] and needs no running maximum. Tiles
+// beyond that bound switch to the exact running-maximum update (online softmax) for the rest of
+// the chunk (partials) or to a two-pass maximum over M (decode).
+//
+// Routing queries in bf16 runs are carried as a pair hi + lo of bf16 values (hi = bf16(c q),
+// lo = bf16(c q - hi)) and every score is the sum of two chained MFMAs, so the queries keep about
+// 16 significant bits in the logits; the keys, values and probabilities are bf16 operands with fp32
+// accumulation.
+//
+// MFMA layouts (checked on gfx950): for v_mfma_f32_16x16x{32,16}_bf16 and 16x16x4_f32, lane l
+// supplies row (l % 16) of A and column (l % 16) of B with the k-slice selected by g = l / 16, and
+// receives column (l % 16), rows 4g..4g+3 of the 16x16 result. Score tiles are computed with the
+// keys as A so that the result lands with one latent per lane column and eight consecutive tokens
+// per lane, which is exactly the A (or B) operand layout of the following P.V product: the
+// probabilities never leave registers.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace flarepp {
+namespace {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRmsEps = 1e-6f;
+// Largest |logit| (log2 units) for which the zero-shift path is used.
+constexpr float kFastBound = 30.0f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
+
+// Score MFMAs start from a zero accumulator, so the register allocator may place their destination
+// on top of an A or B operand that dies there. Operands that feed several score MFMAs are kept live
+// until all of them have been issued: the MFMAs stay above a scheduling barrier that only they may
+// not cross, and an empty asm statement below it uses the operands.
+__device__ __forceinline__ void keep_live(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep_live(const bf16x4& x) { asm volatile("" ::"v"(x)); }
+template <typename S>  // fp32 operand structs: one register per element
+__device__ __forceinline__ void keep_live(const S& x) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(S) / sizeof(float)); i++) asm volatile("" ::"v"(x.v[i]));
+}
+// sched_barrier mask: every instruction class except MFMA may be scheduled across.
+constexpr int kAllButMfma = 0x7F6;  // 0x1 (all ALU) and 0x8 (MFMA) cleared
+
+__device__ __forceinline__ f32x4 mfma_32k(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16k(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_4k(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// Per-dtype operand helpers. A "slice" is the D/4 consecutive elements of a row that one lane
+// feeds to the score MFMA (k = g*D/4 ... g*D/4 + D/4 - 1). An "oct" is the 8 consecutive tokens
+// (or latents) one lane feeds to the P.V MFMA.
+template <typename T, int D>
+struct Ops;
+
+template <>
+struct Ops<bf16, 32> {
+  using Slice = bf16x8;
+  using Oct = bf16x8;
+  __device__ static Slice zero_slice() { return Slice{}; }
+  __device__ static Slice load_slice(const bf16* row, int g) {
+    return *reinterpret_cast<const bf16x8*>(row + 8 * g);
+  }
+  __device__ static f32x4 qk(Slice a, Slice b, f32x4 c) { return mfma_32k(a, b, c); }
+  __device__ static float sumsq(Slice a) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) s += (float)a[i] * (float)a[i];
+    return s;
+  }
+  __device__ static Oct load_oct(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ static Oct pack(f32x4 lo, f32x4 hi) {
+    Oct r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      r[i] = (bf16)lo[i];
+      r[4 + i] = (bf16)hi[i];
+    }
+    return r;
+  }
+  // Sum of the eight (rounded) probabilities, two per v_dot2.
+  __device__ static float osum(Oct p, float acc) {
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      bf16x2 q = {p[2 * i], p[2 * i + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(q, one, acc, false);
+    }
+    return acc;
+  }
+  __device__ static f32x4 pv(Oct a, Oct b, f32x4 c) { return mfma_32k(a, b, c); }
+};
+
+template <>
+struct Ops<bf16, 16> {
+  using Slice = bf16x4;
+  using Oct = bf16x8;
+  __device__ static Slice zero_slice() { return Slice{}; }
+  __device__ static Slice load_slice(const bf16* row, int g) {
+    return *reinterpret_cast<const bf16x4*>(row + 4 * g);
+  }
+  __device__ static f32x4 qk(Slice a, Slice b, f32x4 c) { return mfma_16k(a, b, c); }
+  __device__ static float sumsq(Slice a) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) s += (float)a[i] * (float)a[i];
+    return s;
+  }
+  __device__ static Oct load_oct(const bf16* p) { return Ops<bf16, 32>::load_oct(p); }
+  __device__ static Oct pack(f32x4 lo, f32x4 hi) { return Ops<bf16, 32>::pack(lo, hi); }
+  __device__ static float osum(Oct p, float acc) { return Ops<bf16, 32>::osum(p, acc); }
+  __device__ static f32x4 pv(Oct a, Oct b, f32x4 c) { return Ops<bf16, 32>::pv(a, b, c); }
+};
+
+template <int D>
+struct Ops<float, D> {
+  struct Slice {
+    float v[D / 4];
+  };
+  struct Oct {
+    float v[8];
+  };
+  __device__ static Slice zero_slice() {
+    Slice s;
+#pragma unroll
+    for (int i = 0; i < D / 4; i++) s.v[i] = 0.f;
+    return s;
+  }
+  __device__ static Slice load_slice(const float* row, int g) {
+    Slice s;
+    const f32x4* p = reinterpret_cast<const f32x4*>(row + (D / 4) * g);
+#pragma unroll
+    for (int i = 0; i < D / 16; i++) {
+      f32x4 t = p[i];
+#pragma unroll
+      for (int j = 0; j < 4; j++) s.v[4 * i + j] = t[j];
+    }
+    return s;
+  }
+  __device__ static f32x4 qk(const Slice& a, const Slice& b, f32x4 c) {
+#pragma unroll
+    for (int s = 0; s < D / 4; s++) c = mfma_4k(a.v[s], b.v[s], c);
+    return c;
+  }
+  __device__ static float sumsq(const Slice& a) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 4; i++) s += a.v[i] * a.v[i];
+    return s;
+  }
+  __device__ static Oct load_oct(const float* p) {
+    Oct o;
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+    f32x4 a = q[0], b = q[1];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      o.v[j] = a[j];
+      o.v[4 + j] = b[j];
+    }
+    return o;
+  }
+  __device__ static Oct pack(f32x4 lo, f32x4 hi) {
+    Oct r;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      r.v[i] = lo[i];
+      r.v[4 + i] = hi[i];
+    }
+    return r;
+  }
+  __device__ static float osum(const Oct& p, float acc) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc += p.v[i];
+    return acc;
+  }
+  __device__ static f32x4 pv(const Oct& a, const Oct& b, f32x4 c) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) c = mfma_4k(a.v[j], b.v[j], c);
+    return c;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+// Parts per routing-query row in the workspace: bf16 keeps a hi/lo pair, fp32 one exact value.
+template <typename T>
+constexpr int kQParts = sizeof(T) == 2 ? 2 : 1;
+
+// 16-byte global/LDS chunk and its element view.
+struct alignas(16) Chunk {
+  uint32_t w[4];
+};
+
+template <typename T>
+__device__ __forceinline__ void chunk_to_float(const Chunk& c, float* out) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      out[2 * i] = __uint_as_float(c.w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(c.w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++) out[i] = __uint_as_float(c.w[i]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ Chunk float_to_chunk(const float* v) {
+  Chunk c;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      bf16x2 p = {(bf16)v[2 * i], (bf16)v[2 * i + 1]};
+      c.w[i] = __builtin_bit_cast(uint32_t, p);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++) c.w[i] = __float_as_uint(v[i]);
+  }
+  return c;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// Token order inside a 32-token subtile: score MFMA `half` row r holds token 8*(r/4)+4*half+r%4,
+// so that lane group g receives tokens 8g..8g+7 across the two halves.
+__device__ __forceinline__ int perm_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// ------------------------------------------------------------------------------------------
+// Split-N partial kernel (synthesis and encode).
+//
+// Workgroup = NW waves; wave w owns latents [lat0, lat0 + LPW) as NLB blocks of 16. The workgroup
+// streams its token chunk through LDS in stages of kStage tokens (double-buffered): a row-major key
+// tile (A operand of the score MFMA) and a transposed value tile (B operand of the P.V MFMA). For
+// each latent row it accumulates the shift m, the sum l of exp2(logit - m) and the P.V product.
+template <typename T, int D, int LPW, int NW, bool SYNTH>
+__global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
+  using O = Ops<T, D>;
+  using Slice = typename O::Slice;
+  using Oct = typename O::Oct;
+  constexpr int NLB = LPW / 16;
+  constexpr int NDB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int CH = 16 / sizeof(T);    // elements per 16-byte chunk
+  constexpr int CPR = D / CH;           // chunks per token row
+  constexpr int NCH = kStage * CPR;     // chunks per stage per tensor
+  constexpr int PER = (NCH + NT - 1) / NT;
+  constexpr int RS = D + CH;            // key tile row stride (elements)
+  constexpr int VS = kStage + CH;       // transposed value tile row stride (elements)
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* ks = reinterpret_cast<T*>(smem);                       // [2][kStage][RS]
+  T* vt = ks + 2 * kStage * RS;                              // [2][D][VS]
+  float* kmax_s = reinterpret_cast<float*>(vt + 2 * D * VS); // [2][NW]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int bh = blockIdx.y;
+  const int chunk_id = blockIdx.x % a.nchunk;
+  const int lg = blockIdx.x / a.nchunk;
+  const int64_t n_begin = (int64_t)chunk_id * a.chunk;
+  const int64_t n_end = (n_begin + a.chunk < a.N) ? n_begin + a.chunk : a.N;
+  const int lat0 = (lg * NW + wave) * LPW;
+  const bool active = lat0 < a.Mp;
+
+  const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
+  const T* vbase = reinterpret_cast<const T*>(a.V) + (int64_t)bh * a.N * D;
+  // Synthesis queries are the seeds (one exact part); encode queries are the workspace hi/lo pair.
+  constexpr int QP = SYNTH ? 1 : kQParts<T>;
+  const T* qbase = reinterpret_cast<const T*>(a.Q) +
+                   (SYNTH ? (int64_t)(bh % a.H) * a.Mq * D : (int64_t)bh * a.Mq * QP * D);
+
+  // Query operands (B of the score MFMA): lane (c, g) holds slice g of latent lat0 + 16 lb + c.
+  Slice qb[NLB], qlo[NLB];
+  float qss = 0.f;
+#pragma unroll
+  for (int lb = 0; lb < NLB; lb++) {
+    const int row = lat0 + 16 * lb + c;
+    qb[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QP * D, g) : O::zero_slice();
+    if constexpr (QP == 2) qlo[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QP * D + D, g) : O::zero_slice();
+    float ss = O::sumsq(qb[lb]);
+    ss += shfl_xor(ss, 16);
+    ss += shfl_xor(ss, 32);
+    qss = fmaxf(qss, ss);
+  }
+  // Norm of the hi part; the lo part adds at most 2^-8 relative (covered by the 1.01 margin).
+  const float qnorm = sqrtf(wave_max(qss)) * 1.01f;
+  // Synthesis keys are c * N0(S): their norm is at most c * sqrt(D) (plus bf16 rounding).
+  const float c_scale = kLog2e * rsqrtf((float)D);
+  const bool syn_fast = qnorm * c_scale * sqrtf((float)D) * 1.01f <= kFastBound;
+
+  f32x4 zacc[NLB][NDB];
+  float lsum[NLB], mrow[NLB];
+#pragma unroll
+  for (int lb = 0; lb < NLB; lb++) {
+    lsum[lb] = 0.f;
+    mrow[lb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; db++) zacc[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool slow = false;      // running-maximum mode (wave-uniform)
+  bool seen_fast = false; // a zero-shift stage has been accumulated
+
+  Chunk kreg[PER], vreg[PER];
+  auto load_stage = [&](int64_t s0) {
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int q = tid + i * NT;
+      Chunk ck{}, cv{};
+      if (q < NCH) {
+        const int t = q / CPR, part = q % CPR;
+        const int64_t n = s0 + t;
+        if (n < n_end) {
+          ck = *reinterpret_cast<const Chunk*>(kbase + n * D + part * CH);
+          if constexpr (!SYNTH) cv = *reinterpret_cast<const Chunk*>(vbase + n * D + part * CH);
+        }
+      }
+      kreg[i] = ck;
+      vreg[i] = cv;
+    }
+  };
+  auto store_stage = [&](int buf) {
+    T* kdst = ks + buf * kStage * RS;
+    T* vdst = vt + buf * D * VS;
+    float kmx = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int q = tid + i * NT;
+      float x[CH];
+      chunk_to_float<T>(kreg[i], x);
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < CH; j++) ss += x[j] * x[j];
+#pragma unroll
+      for (int m = 1; m < CPR; m <<= 1) ss += shfl_xor(ss, m);
+      if (q < NCH) {
+        const int t = q / CPR, part = q % CPR;
+        if constexpr (SYNTH) {
+          // N0 of the synthesis key row (Section 3.2, Eq. 5): keys c*N0(s), values N0(s).
+          const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kRmsEps);
+          float kx[CH];
+#pragma unroll
+          for (int j = 0; j < CH; j++) {
+            x[j] *= inv;
+            kx[j] = x[j] * c_scale;
+          }
+          *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = float_to_chunk<T>(kx);
+#pragma unroll
+          for (int j = 0; j < CH; j++) vdst[(part * CH + j) * VS + t] = (T)x[j];
+        } else {
+          kmx = fmaxf(kmx, ss);
+          *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kreg[i];
+          float v[CH];
+          chunk_to_float<T>(vreg[i], v);
+#pragma unroll
+          for (int j = 0; j < CH; j++) vdst[(part * CH + j) * VS + t] = (T)v[j];
+        }
+      }
+    }
+    if constexpr (!SYNTH) {
+      kmx = wave_max(kmx);
+      if (lane == 0) kmax_s[buf * NW + wave] = kmx;
+    }
+  };
+
+  const int nstage = (int)((n_end - n_begin + kStage - 1) / kStage);
+  load_stage(n_begin);
+  store_stage(0);
+  __syncthreads();
+
+  for (int s = 0; s < nstage; s++) {
+    const int buf = s & 1;
+    const int64_t s0 = n_begin + (int64_t)s * kStage;
+    if (s + 1 < nstage) load_stage(s0 + kStage);
+
+    if (active) {
+      bool fast;
+      if constexpr (SYNTH) {
+        fast = syn_fast;
+      } else {
+        float km = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) km = fmaxf(km, kmax_s[buf * NW + w]);
+        fast = qnorm * sqrtf(km) <= kFastBound;
+      }
+      if (!slow && !fast) {
+        slow = true;
+        if (!seen_fast) {
+#pragma unroll
+          for (int lb = 0; lb < NLB; lb++) mrow[lb] = -INFINITY;
+        }
+      }
+      if (!slow) seen_fast = true;
+
+      const T* kt = ks + buf * kStage * RS;
+      const T* vtt = vt + buf * D * VS;
+      const int nvalid = (int)((n_end - s0 < kStage) ? (n_end - s0) : kStage);
+      const int nsub = (nvalid + 31) / 32;
+      for (int st = 0; st < nsub; st++) {
+        const Slice ka0 = O::load_slice(kt + (32 * st + perm_row(c, 0)) * RS, g);
+        const Slice ka1 = O::load_slice(kt + (32 * st + perm_row(c, 1)) * RS, g);
+        f32x4 s0v[NLB], s1v[NLB];
+#pragma unroll
+        for (int lb = 0; lb < NLB; lb++) {
+          s0v[lb] = O::qk(ka0, qb[lb], f32x4{0.f, 0.f, 0.f, 0.f});
+          s1v[lb] = O::qk(ka1, qb[lb], f32x4{0.f, 0.f, 0.f, 0.f});
+          if constexpr (QP == 2) {
+            s0v[lb] = O::qk(ka0, qlo[lb], s0v[lb]);
+            s1v[lb] = O::qk(ka1, qlo[lb], s1v[lb]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(kAllButMfma);
+        keep_live(ka0);
+        keep_live(ka1);
+        // Tokens past the end of the chunk do not enter the softmax.
+        if (32 * st + 32 > nvalid) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const bool ok0 = 32 * st + 8 * g + i < nvalid;
+            const bool ok1 = 32 * st + 8 * g + 4 + i < nvalid;
+#pragma unroll
+            for (int lb = 0; lb < NLB; lb++) {
+              if (!ok0) s0v[lb][i] = -INFINITY;
+              if (!ok1) s1v[lb][i] = -INFINITY;
+            }
+          }
+        }
+        if (slow) {
+#pragma unroll
+          for (int lb = 0; lb < NLB; lb++) {
+            float tm = fmaxf(fmaxf(fmaxf(s0v[lb][0], s0v[lb][1]), fmaxf(s0v[lb][2], s0v[lb][3])),
+                             fmaxf(fmaxf(s1v[lb][0], s1v[lb][1]), fmaxf(s1v[lb][2], s1v[lb][3])));
+            tm = fmaxf(tm, shfl_xor(tm, 16));
+            tm = fmaxf(tm, shfl_xor(tm, 32));
+            const float mold = mrow[lb];
+            const float mnew = fmaxf(mold, tm);
+            const float alpha = (mnew == mold) ? 1.0f : exp2_fast(mold - mnew);
+            const float shift = (mnew == -INFINITY) ? 0.0f : mnew;
+            mrow[lb] = mnew;
+            lsum[lb] *= alpha;
+            // Accumulator row 4g+i of this block belongs to the latent held by lane column 4g+i.
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const float ai = shfl(alpha, 4 * g + i);
+#pragma unroll
+              for (int db = 0; db < NDB; db++) zacc[lb][db][i] *= ai;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              s0v[lb][i] = exp2_fast(s0v[lb][i] - shift);
+              s1v[lb][i] = exp2_fast(s1v[lb][i] - shift);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int lb = 0; lb < NLB; lb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              s0v[lb][i] = exp2_fast(s0v[lb][i]);
+              s1v[lb][i] = exp2_fast(s1v[lb][i]);
+            }
+        }
+        Oct vb[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; db++) vb[db] = O::load_oct(vtt + (16 * db + c) * VS + 32 * st + 8 * g);
+#pragma unroll
+        for (int lb = 0; lb < NLB; lb++) {
+          const Oct pa = O::pack(s0v[lb], s1v[lb]);
+          lsum[lb] = O::osum(pa, lsum[lb]);
+#pragma unroll
+          for (int db = 0; db < NDB; db++) zacc[lb][db] = O::pv(pa, vb[db], zacc[lb][db]);
+        }
+      }
+    }
+    if (s + 1 < nstage) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // Partials of this chunk: l and m per latent, the P.V accumulator per latent and channel.
+  const int64_t pbase = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp;
+#pragma unroll
+  for (int lb = 0; lb < NLB; lb++) {
+    float l = lsum[lb];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const int row = lat0 + 16 * lb + c;
+    if (g == 0 && row < a.Mp) {
+      a.part_l[pbase + row] = l;
+      a.part_m[pbase + row] = slow ? mrow[lb] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = lat0 + 16 * lb + 4 * g + i;
+      if (r < a.Mp) {
+#pragma unroll
+        for (int db = 0; db < NDB; db++) a.part_acc[(pbase + r) * D + 16 * db + c] = zacc[lb][db][i];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Merge of the chunk partials (Appendix B.3, Eq. 30-33): m = max_c m_c, d = sum_c 2^(m_c - m) l_c,
+// U = sum_c 2^(m_c - m) A_c, result U / d. With GATE, Q = N0(Qf) + g * Qd (Eq. 7) in fp32, cast
+// with the factor c = log2(e)/sqrt(D) folded in; otherwise Z is cast unscaled. One thread per
+// (latent, channel); rows in [M, Mout) are written as zeros.
+template <typename T, int D, bool GATE>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int row = idx / D, d = idx % D;
+  if (row >= a.Mout) return;  // whole D-groups exit together
+  float res = 0.f, qd = 0.f;
+  if (row < a.M) {
+    const int64_t base = (int64_t)bh * a.nchunk * a.Mp;
+    float m = -INFINITY;
+    for (int ch = 0; ch < a.nchunk; ch++) m = fmaxf(m, a.part_m[base + (int64_t)ch * a.Mp + row]);
+    float den = 0.f, num = 0.f;
+    for (int ch = 0; ch < a.nchunk; ch++) {
+      const int64_t o = base + (int64_t)ch * a.Mp + row;
+      const float w = exp2_fast(a.part_m[o] - m);
+      den += w * a.part_l[o];
+      num += w * a.part_acc[o * D + d];
+    }
+    qd = num / den;
+    res = qd;
+  }
+  if constexpr (GATE) {
+    const int h = bh % a.H;
+    const float f = (row < a.M) ? to_f(reinterpret_cast<const T*>(a.Qf)[((int64_t)h * a.M + row) * D + d]) : 0.f;
+    float ss = f * f;
+#pragma unroll
+    for (int m = 1; m < D; m <<= 1) ss += shfl_xor(ss, m);
+    const float gv = a.g[h];
+    res = (row < a.M) ? f / sqrtf(ss * (1.0f / D) + kRmsEps) + gv * qd : 0.f;
+    if (a.dbg_qd && row < a.M) a.dbg_qd[((int64_t)bh * a.M + row) * D + d] = qd;
+    if (a.dbg_out && row < a.M) a.dbg_out[((int64_t)bh * a.M + row) * D + d] = res;
+    // c*Q as hi (and, for bf16, lo = the rounding residual of hi).
+    const float cq = res * (kLog2e * rsqrtf((float)D));
+    constexpr int QP = kQParts<T>;
+    T* qo = reinterpret_cast<T*>(a.out) + ((int64_t)bh * a.Mout + row) * QP * D + d;
+    const T hi = (T)cq;
+    qo[0] = hi;
+    if constexpr (QP == 2) qo[D] = (T)(cq - to_f(hi));
+  } else {
+    if (a.dbg_out && row < a.M) a.dbg_out[((int64_t)bh * a.M + row) * D + d] = res;
+    reinterpret_cast<T*>(a.out)[((int64_t)bh * a.Mout + row) * D + d] = (T)res;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode: every token's scores against all M routing queries, softmax over M, times Z
+// (Eq. 8, second call). The workgroup keeps c*Q (row-major, A operand of the score MFMA) and Z
+// (transposed, A operand of the P.V MFMA) in LDS; each wave takes groups of 64 tokens whose K
+// rows it reads straight from HBM as B operands.
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  using O = Ops<T, D>;
+  using Slice = typename O::Slice;
+  using Oct = typename O::Oct;
+  constexpr int NDB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int CPR = D / CH;
+  constexpr int QP = kQParts<T>;
+  constexpr int RQ = QP * D + CH;  // a row holds the hi part then (bf16) the lo part
+  constexpr int TB = 4;  // 16-token blocks per wave group
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;  // multiple of 32
+  const int RZ = Mp + CH;
+  T* qs = reinterpret_cast<T*>(smem);     // [Mp][RQ]
+  T* zt = qs + Mp * RQ;                    // [D][RZ]
+  float* qn_s = reinterpret_cast<float*>(zt + D * RZ);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int bh = blockIdx.y;
+  const T* qsrc = reinterpret_cast<const T*>(a.Q) + (int64_t)bh * Mp * QP * D;
+  const T* zsrc = reinterpret_cast<const T*>(a.Z) + (int64_t)bh * Mp * D;
+
+  float qmx = 0.f;
+  for (int q0 = 0; q0 < Mp * CPR; q0 += NT) {
+    const int q = q0 + tid;
+    float ss = 0.f;
+    if (q < Mp * CPR) {
+      const int row = q / CPR, part = q % CPR;
+      const Chunk cq = *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + part * CH);
+      *reinterpret_cast<Chunk*>(qs + row * RQ + part * CH) = cq;
+      if constexpr (QP == 2)
+        *reinterpret_cast<Chunk*>(qs + row * RQ + D + part * CH) =
+            *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + D + part * CH);
+      float x[CH];
+      chunk_to_float<T>(cq, x);
+#pragma unroll
+      for (int j = 0; j < CH; j++) ss += x[j] * x[j];
+      const Chunk cz = *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * CH);
+      chunk_to_float<T>(cz, x);
+#pragma unroll
+      for (int j = 0; j < CH; j++) zt[(part * CH + j) * RZ + row] = (T)x[j];
+    }
+#pragma unroll
+    for (int m = 1; m < CPR; m <<= 1) ss += shfl_xor(ss, m);
+    qmx = fmaxf(qmx, ss);
+  }
+  qmx = wave_max(qmx);
+  if (lane == 0) qn_s[wave] = qmx;
+  __syncthreads();
+  float qm = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; w++) qm = fmaxf(qm, qn_s[w]);
+  const float qnorm = sqrtf(qm) * 1.01f;  // hi part; lo adds at most 2^-8 relative
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
+  T* obase = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.N * D;
+  const int nlb = Mp / 32;
+  const bool ragged = (a.M & 31) != 0;
+
+  for (int64_t base = t_begin + (int64_t)wave * 64; base < t_end; base += (int64_t)NW * 64) {
+    Slice kb[TB];
+    float kss = 0.f;
+#pragma unroll
+    for (int t = 0; t < TB; t++) {
+      const int64_t tok = base + 16 * t + c;
+      kb[t] = (tok < a.N) ? O::load_slice(kbase + tok * D, g) : O::zero_slice();
+      float ss = O::sumsq(kb[t]);
+      ss += shfl_xor(ss, 16);
+      ss += shfl_xor(ss, 32);
+      kss = fmaxf(kss, ss);
+    }
+    const bool fast = qnorm * sqrtf(wave_max(kss)) <= kFastBound;
+
+    // Scores of latent block lb for every token block t: lane (c, g) gets token 16t + c and
+    // latents 32 lb + 8g .. 32 lb + 8g + 7 (s0[t]: first four, s1[t]: last four).
+    auto scores_all = [&](int lb, f32x4* s0, f32x4* s1) {
+      const Slice qa0 = O::load_slice(qs + (32 * lb + perm_row(c, 0)) * RQ, g);
+      const Slice qa1 = O::load_slice(qs + (32 * lb + perm_row(c, 1)) * RQ, g);
+      Slice ql0, ql1;
+      if constexpr (QP == 2) {
+        ql0 = O::load_slice(qs + (32 * lb + perm_row(c, 0)) * RQ + D, g);
+        ql1 = O::load_slice(qs + (32 * lb + perm_row(c, 1)) * RQ + D, g);
+      }
+#pragma unroll
+      for (int t = 0; t < TB; t++) {
+        s0[t] = O::qk(qa0, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
+        s1[t] = O::qk(qa1, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
+        if constexpr (QP == 2) {
+          s0[t] = O::qk(ql0, kb[t], s0[t]);
+          s1[t] = O::qk(ql1, kb[t], s1[t]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(kAllButMfma);
+      keep_live(qa0);
+      keep_live(qa1);
+      if constexpr (QP == 2) {
+        keep_live(ql0);
+        keep_live(ql1);
+      }
+      if (ragged && lb == nlb - 1) {
+#pragma unroll
+        for (int t = 0; t < TB; t++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            if (32 * lb + 8 * g + i >= a.M) s0[t][i] = -INFINITY;
+            if (32 * lb + 8 * g + 4 + i >= a.M) s1[t][i] = -INFINITY;
+          }
+      }
+    };
+
+    float shift[TB];
+#pragma unroll
+    for (int t = 0; t < TB; t++) shift[t] = 0.f;
+    if (!fast) {
+      // Two-pass maximum over the M latents for each token.
+#pragma unroll
+      for (int t = 0; t < TB; t++) shift[t] = -INFINITY;
+      for (int lb = 0; lb < nlb; lb++) {
+        f32x4 s0[TB], s1[TB];
+        scores_all(lb, s0, s1);
+#pragma unroll
+        for (int t = 0; t < TB; t++)
+          shift[t] = fmaxf(shift[t], fmaxf(fmaxf(fmaxf(s0[t][0], s0[t][1]), fmaxf(s0[t][2], s0[t][3])),
+                                           fmaxf(fmaxf(s1[t][0], s1[t][1]), fmaxf(s1[t][2], s1[t][3]))));
+      }
+#pragma unroll
+      for (int t = 0; t < TB; t++) {
+        shift[t] = fmaxf(shift[t], shfl_xor(shift[t], 16));
+        shift[t] = fmaxf(shift[t], shfl_xor(shift[t], 32));
+      }
+    }
+
+    f32x4 yacc[TB][NDB];
+    float lsum[TB];
+#pragma unroll
+    for (int t = 0; t < TB; t++) {
+      lsum[t] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; db++) yacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int lb = 0; lb < nlb; lb++) {
+      Oct za[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; db++) za[db] = O::load_oct(zt + (16 * db + c) * RZ + 32 * lb + 8 * g);
+      f32x4 s0[TB], s1[TB];
+      scores_all(lb, s0, s1);
+#pragma unroll
+      for (int t = 0; t < TB; t++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          s0[t][i] = exp2_fast(s0[t][i] - shift[t]);
+          s1[t][i] = exp2_fast(s1[t][i] - shift[t]);
+        }
+        const Oct pb = O::pack(s0[t], s1[t]);
+        lsum[t] = O::osum(pb, lsum[t]);
+#pragma unroll
+        for (int db = 0; db < NDB; db++) yacc[t][db] = O::pv(za[db], pb, yacc[t][db]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TB; t++) {
+      float l = lsum[t];
+      l += shfl_xor(l, 16);
+      l += shfl_xor(l, 32);
+      const float inv = 1.0f / l;
+      const int64_t tok = base + 16 * t + c;
+      if (tok < t_end) {
+#pragma unroll
+        for (int db = 0; db < NDB; db++) {
+          T* dst = obase + tok * D + 16 * db + 4 * g;
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; i++) o[i] = (bf16)(yacc[t][db][i] * inv);
+            *reinterpret_cast<bf16x4*>(dst) = o;
+          } else {
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; i++) o[i] = yacc[t][db][i] * inv;
+            *reinterpret_cast<f32x4*>(dst) = o;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// Launchers.
+
+// Dynamic LDS above 64 KiB has to be allowed per kernel (gfx950 has 160 KiB per workgroup).
+template <typename F>
+static hipError_t allow_lds(F* fn, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <typename T, int D, int LPW, int NW, bool SYNTH>
+static hipError_t launch_partial_t(const PartialArgs& a, int grid_x, int grid_y, hipStream_t st) {
+  constexpr int CH = 16 / sizeof(T);
+  const size_t lds = (size_t)(2 * kStage * (D + CH) + 2 * D * (kStage + CH)) * sizeof(T) + 2 * NW * sizeof(float);
+  hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool SYNTH>
+static hipError_t launch_partial_d(const PartialArgs& a, int plan, int gx, int gy, hipStream_t st) {
+  switch (plan) {
+    case 0: return launch_partial_t<T, D, 16, 4, SYNTH>(a, gx, gy, st);
+    case 1: return launch_partial_t<T, D, 32, 4, SYNTH>(a, gx, gy, st);
+    case 2: return launch_partial_t<T, D, 64, 4, SYNTH>(a, gx, gy, st);
+    default: return launch_partial_t<T, D, 64, 8, SYNTH>(a, gx, gy, st);
+  }
+}
+
+hipError_t launch_partial(const PartialArgs& a, int dtype, int D, bool synth, int plan, int gx, int gy,
+                          hipStream_t st) {
+  if (dtype == 1) {
+    if (D == 32) return synth ? launch_partial_d<bf16, 32, true>(a, plan, gx, gy, st) : launch_partial_d<bf16, 32, false>(a, plan, gx, gy, st);
+    return synth ? launch_partial_d<bf16, 16, true>(a, plan, gx, gy, st) : launch_partial_d<bf16, 16, false>(a, plan, gx, gy, st);
+  }
+  if (D == 32) return synth ? launch_partial_d<float, 32, true>(a, plan, gx, gy, st) : launch_partial_d<float, 32, false>(a, plan, gx, gy, st);
+  return synth ? launch_partial_d<float, 16, true>(a, plan, gx, gy, st) : launch_partial_d<float, 16, false>(a, plan, gx, gy, st);
+}
+
+template <typename T, int D, bool GATE>
+static hipError_t launch_merge_t(const MergeArgs& a, int BH, hipStream_t st) {
+  const int gx = (a.Mout * D + 255) / 256;
+  hipLaunchKernelGGL((merge_kernel<T, D, GATE>), dim3(gx, BH), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH, hipStream_t st) {
+  if (dtype == 1) {
+    if (D == 32) return gate ? launch_merge_t<bf16, 32, true>(a, BH, st) : launch_merge_t<bf16, 32, false>(a, BH, st);
+    return gate ? launch_merge_t<bf16, 16, true>(a, BH, st) : launch_merge_t<bf16, 16, false>(a, BH, st);
+  }
+  if (D == 32) return gate ? launch_merge_t<float, 32, true>(a, BH, st) : launch_merge_t<float, 32, false>(a, BH, st);
+  return gate ? launch_merge_t<float, 16, true>(a, BH, st) : launch_merge_t<float, 16, false>(a, BH, st);
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, int gx, int gy, hipStream_t st) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int CH = 16 / sizeof(T);
+  const size_t lds = (size_t)(a.Mp * (kQParts<T> * D + CH) + D * (a.Mp + CH)) * sizeof(T) + NW * sizeof(float);
+  hipError_t e = allow_lds(decode_kernel<T, D, NW>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_kernel<T, D, NW>), dim3(gx, gy), dim3(NW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int gx, int gy, hipStream_t st) {
+  if (dtype == 1) return D == 32 ? launch_decode_t<bf16, 32>(a, gx, gy, st) : launch_decode_t<bf16, 16>(a, gx, gy, st);
+  return D == 32 ? launch_decode_t<float, 32>(a, gx, gy, st) : launch_decode_t<float, 16>(a, gx, gy, st);
+}
+
+size_t decode_lds_bytes(int dtype, int D, int Mp) {
+  const int es = dtype == 1 ? 2 : 4;
+  const int CH = 16 / es;
+  const int qp = dtype == 1 ? 2 : 1;
+  return (size_t)(Mp * (qp * D + CH) + D * (Mp + CH)) * es + kDecodeWaves * sizeof(float);
+}
+
+}  // namespace flarepp

@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point the header declares,
+and rejects bad arguments before it touches a GPU. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_latent_routing_amd as fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flarepp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flarepp_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fl.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert fl.flarepp_version() >= 100
+    for s in range(0, 8):
+        assert isinstance(fl.flarepp_strerror(s), str) and fl.flarepp_strerror(s)
+    assert [fl.flarepp_kernel_name(i) for i in range(5)] == [
+        "synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"]
+    assert fl.flarepp_kernel_name(5) is None
+
+
+def _mix(L, K=0x1000, V=0x2000, S=0x3000, Qs=0x4000, Qf=0x5000, g=0x6000, B=1, H=1, N=64, M=8, D=16,
+         dtype=1, out=0x7000000):
+    vp = ctypes.c_void_p
+    return L.flarepp_mix(vp(K), vp(V), vp(S), vp(Qs), vp(Qf), vp(g), B, H, N, M, D, dtype, vp(out), vp(0))
+
+
+def test_size_validation(L):
+    assert _mix(L, D=24) == fl.FLAREPP_UNSUPPORTED
+    assert _mix(L, D=64) == fl.FLAREPP_UNSUPPORTED
+    assert _mix(L, M=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _mix(L, M=513) == fl.FLAREPP_UNSUPPORTED
+    assert _mix(L, dtype=7) == fl.FLAREPP_UNSUPPORTED
+    assert _mix(L, N=-1) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _mix(L, B=-2) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _mix(L, B=300, H=300) == fl.FLAREPP_UNSUPPORTED
+
+
+def test_pointer_validation(L):
+    assert _mix(L, K=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _mix(L, g=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _mix(L, out=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _mix(L, V=0x2008) == fl.FLAREPP_MISALIGNED
+    assert _mix(L, out=0x7000004) == fl.FLAREPP_MISALIGNED
+    # out overlapping an input
+    assert _mix(L, out=0x1000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
+
+
+def test_empty_problem_is_a_no_op(L):
+    # B*H*N == 0: nothing to compute, nothing enqueued, no device needed.
+    assert _mix(L, N=0) == fl.FLAREPP_OK
+    assert _mix(L, B=0, K=0, V=0, S=0) == fl.FLAREPP_OK
+    assert fl.flarepp_workspace_bytes(1, 1, 0, 8, 16, 1) == 0
+
+
+def test_workspace_bytes(L):
+    # Invalid sizes give 0; valid ones hold the chunk partials and the two latent tensors.
+    assert fl.flarepp_workspace_bytes(1, 1, 100, 0, 16, 1) == 0
+    assert fl.flarepp_workspace_bytes(1, 1, 100, 8, 24, 1) == 0
+    for (B, H, N, M, D, dt) in [(1, 2, 1024, 32, 16, 0), (4, 8, 16384, 64, 16, 1), (32, 8, 4096, 128, 32, 1),
+                                (2, 8, 65536, 256, 32, 1), (1, 8, 1 << 20, 512, 32, 1), (3, 5, 1, 1, 32, 0)]:
+        ws = fl.flarepp_workspace_bytes(B, H, N, M, D, dt)
+        es = 2 if dt == 1 else 4
+        m32 = (M + 31) // 32 * 32
+        m16 = (M + 15) // 16 * 16
+        assert ws % 256 == 0
+        assert ws >= 2 * B * H * m32 * D * es + B * H * m16 * (D + 2) * 4
+        assert ws < 64 * 2 ** 20 + 2 * B * H * m32 * D * es  # partials stay small against the inputs
+
+
+def test_workspace_too_small_is_rejected(L):
+    vp = ctypes.c_void_p
+    need = fl.flarepp_workspace_bytes(1, 1, 64, 8, 16, 1)
+    rc = L.flarepp_mix_ws(vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), 1, 1, 64, 8,
+                          16, 1, vp(0x7000000), vp(0x9000000), need - 1, vp(0))
+    assert rc == fl.FLAREPP_INVALID_ARGUMENT
+    rc = L.flarepp_mix_ws(vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), 1, 1, 64, 8,
+                          16, 1, vp(0x7000000), vp(0x9000010), need, vp(0))
+    assert rc == fl.FLAREPP_MISALIGNED
+
+
+def test_timing_read_without_records(L):
+    fl.flarepp_timing_enable(False)
+    t = fl.flarepp_timing_read()
+    assert set(t) == {"synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"}
+    assert all(v == (0.0, 0) for v in t.values())

@@ -1,0 +1,202 @@
+"""GPU parity of the HIP mixer (through the C ABI) against the float64 oracle.
+
+Bars (per (b, h) slice): fp32 max|Y - Y_ref| / max|Y_ref| <= 1e-5; bf16 inputs with fp32
+accumulation max|Y - Y_ref| <= 2e-2 RMS(Y_ref). The latent stages Qd, Q, Z (exported in fp32 before
+any cast) are held to the same bars.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import oracle_head, run_gpu, say, slice_err, tol, to_device
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_routing_amd as fl
+    fl.lib()  # fails loudly when the library is missing
+
+
+def _check(w, heads=None, block=None, stages=True, label=""):
+    say(f"[parity] {label or w.name}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    Y, Qd, Q, Z = run_gpu(w, debug=True)
+    assert np.isfinite(Y).all()
+    worst = {}
+    pairs = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in pairs:
+        ref = oracle_head(w, b, h, block=block)
+        errs = {"Y": slice_err(Y[b, h], ref["Y"], w.dtype)}
+        if stages:
+            errs.update(Qd=slice_err(Qd[b, h], ref["Qd"], w.dtype), Q=slice_err(Q[b, h], ref["Q"], w.dtype),
+                        Z=slice_err(Z[b, h], ref["Z"], w.dtype))
+        for k, e in errs.items():
+            worst[k] = max(worst.get(k, 0.0), e)
+    say(f"[parity] {label or w.name}: worst {worst} (bar {tol(w.dtype)})")
+    for k, e in worst.items():
+        assert e <= tol(w.dtype), (k, e)
+    return Y
+
+
+def test_cfg1_fp32_full():
+    _check(make_workload(1))
+
+
+@pytest.mark.parametrize("N", [1, 31, 127, 128, 129, 1000, 3001])
+def test_cfg1_shapes_fp32_ragged_tokens(N):
+    _check(make_workload(1, N=N, seed=100 + N), label=f"cfg1 N={N}")
+
+
+def test_cfg2_bf16_ragged():
+    _check(make_workload(2, B=2, H=3, N=5000))
+
+
+def test_cfg3_bf16_and_gate_zero_head():
+    w = make_workload(3, B=2)
+    Y = _check(w)
+    # Head 0 has g = 0: the routing queries are N0(Qf) whatever S and Qseed hold, so the output
+    # is bitwise unchanged when they change (Section 3.2: g -> 0 is fixed-query routing).
+    w2 = make_workload(3, B=2)
+    rng = np.random.default_rng(5)
+    w2.S = (w.S ^ rng.integers(0, 4, size=w.S.shape, dtype=np.uint16)).astype(np.uint16)
+    w2.Qseed = w.Qseed[:, ::-1].copy()
+    Y2 = run_gpu(w2, debug=False)
+    assert np.array_equal(Y[:, 0], Y2[:, 0])
+    assert not np.array_equal(Y[:, 1], Y2[:, 1])
+
+
+def test_cfg4_bf16_reduced():
+    _check(make_workload(4, B=1, H=2, N=20000))
+
+
+def test_cfg4_peaked_bf16_reduced():
+    _check(make_workload(4, B=1, H=2, N=20000, peaked=True))
+
+
+def test_cfg5_bf16_reduced():
+    _check(make_workload(5, H=2, N=150000), block=32768)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [16, 32])
+@pytest.mark.parametrize("M", [1, 17, 33, 100, 200, 512])
+def test_latent_counts(dtype, D, M):
+    # Ragged latent counts on the mesh-like input family.
+    _check(make_workload(2, B=1, H=2, N=700, M=M, D=D, dtype=dtype, seed=7 * M + D), label=f"M={M} D={D} {dtype}")
+
+
+@pytest.mark.parametrize("M", [17, 100])
+def test_latent_counts_gaussian_inputs(M):
+    _check(make_workload(3, B=1, H=2, N=700, M=M, seed=3 * M), label=f"gauss M={M}")
+
+
+@pytest.mark.parametrize("dtype,kscale,qscale", [("fp32", 4.0, 4.0), ("bf16", 2.0, 3.0)])
+def test_wide_logits_take_the_exact_path(dtype, kscale, qscale):
+    # Scaled keys and seeds push the logit bounds past the zero-shift window, so the calls run with
+    # exact running maxima. The bf16 scales stay moderate: bf16 synthesis keys carry a relative
+    # rounding of 2^-9, which turns into a logit error proportional to the logit itself.
+    w = make_workload(3, B=1, H=2, N=3000, M=64, dtype=dtype, seed=11)
+    from workloads.gen import _store
+    w.K = _store(w.f64("K") * kscale, dtype)
+    w.Qseed = _store(w.f64("Qseed") * qscale, dtype)
+    c = np.log2(np.e) / np.sqrt(w.D)
+    syn_bound = np.linalg.norm(w.f64("Qseed"), axis=-1).max() * np.log2(np.e)
+    say(f"[parity] wide logits {dtype}: synthesis logit bound {syn_bound:.1f} (zero-shift window 30)")
+    assert syn_bound > 30.0
+    _check(w, label=f"wide logits {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_zero_shift_to_exact_switch_inside_a_chunk(dtype):
+    # Large keys only in a late token range and in a middle range: earlier stages of a chunk are
+    # accumulated with shift 0 and the later ones switch to the running maximum; decode token groups
+    # mix both paths.
+    w = make_workload(4, B=1, H=2, N=20000, dtype=dtype)
+    from workloads.gen import _store
+    K = w.f64("K")
+    K[:, :, 17000:17500] *= 6.0
+    K[:, :, 8000:8100] *= 5.0
+    w.K = _store(K, dtype)
+    _check(w, label=f"switch {dtype}")
+
+
+def test_gate_one_and_zero_everywhere():
+    for gval in (0.0, 1.0):
+        _check(make_workload(2, B=1, H=2, N=2000, g=gval), label=f"g={gval}")
+
+
+def test_determinism_and_entry_points_agree():
+    import rank_latent_routing_amd as fl
+    w = make_workload(4, B=1, H=2, N=30000)
+    dev = to_device(w)
+    args = (dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"])
+    a = fl.flarepp_mix(*args)
+    b = fl.flarepp_mix_ws(*args)
+    c, _, _, _ = fl.flarepp_mix_debug(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_empty_problem():
+    import rank_latent_routing_amd as fl
+    K = torch.zeros((1, 2, 0, 16), dtype=torch.bfloat16, device="cuda")
+    Qs = torch.zeros((2, 8, 16), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(2, dtype=torch.float32, device="cuda")
+    out = fl.flarepp_mix(K, K, K, Qs, Qs, g)
+    torch.cuda.synchronize()
+    assert out.shape == K.shape
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+
+def _full(cfg, heads, ntok=None, **kw):
+    w = make_workload(cfg, **kw)
+    say(f"[full] {w.name}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D}")
+    Y = run_gpu(w, debug=False)
+    assert np.isfinite(Y).all()
+    rng = np.random.default_rng(cfg)
+    for b, h in heads:
+        ref = oracle_head(w, b, h, block=65536)
+        if ntok is None:
+            e = slice_err(Y[b, h], ref["Y"], w.dtype)
+        else:
+            idx = rng.choice(w.N, size=ntok, replace=False)
+            e = np.abs(Y[b, h][idx] - ref["Y"][idx]).max() / np.sqrt(np.mean(ref["Y"] ** 2))
+        say(f"[full] {w.name} (b={b}, h={h}) err {e:.3g}")
+        assert e <= tol(w.dtype)
+    return w, Y
+
+
+def test_full_cfg2():
+    _full(2, [(0, 0), (1, 5), (3, 7)])
+
+
+def test_full_cfg3():
+    _full(3, [(0, 0), (17, 3), (31, 7)])
+
+
+def test_full_cfg4_and_peaked():
+    _full(4, [(0, 1), (1, 6)])
+    _full(4, [(1, 2)], peaked=True)
+
+
+def test_full_cfg5_one_head():
+    _full(5, [(0, 3)])
+
+
+def test_full_cfg5_constant_values_pass_through():
+    # A row-stochastic operator maps a constant value field to itself (Eq. 4), at every token.
+    w = make_workload(5)
+    from workloads.gen import _store
+    v = np.random.default_rng(3).standard_normal((w.H, w.D))
+    w.V = _store(np.broadcast_to(v[None, :, None, :], (w.B, w.H, w.N, w.D)), "bf16")
+    Y = run_gpu(w, debug=False)
+    ref = w.f64("V")[:, :, :1, :]
+    err = np.abs(Y - ref).max() / np.sqrt(np.mean(ref ** 2))
+    say(f"[full] cfg5 constant V err {err:.3g}")
+    assert err <= tol("bf16")

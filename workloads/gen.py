@@ -49,10 +49,11 @@ def workload_seed(cfg: int) -> int:
 def bf16_bits_from_float(x: np.ndarray) -> np.ndarray:
     """Round float values to bfloat16 (nearest, ties to even) and return the uint16 bit patterns."""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    nan = np.isnan(f)
+    u = f.view(np.uint32)
+    # Finite values never carry out of 32 bits here (largest finite magnitude 0xFF7FFFFF + 0x8000).
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
+    nan = np.isnan(f)
     if nan.any():
         out[nan] = 0x7FC0
     return out
