@@ -35,6 +35,9 @@ def _parse():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device-to-device copy before the timed region (a reference "
+                         "dispatch for scaling the HBM byte counters of a profile)")
     return ap.parse_args()
 
 
@@ -93,6 +96,14 @@ def main():
     ws = torch.empty(fl.flarepp_workspace_bytes(w.B, w.H, w.N, w.M, w.D, dt_code), dtype=torch.uint8, device="cuda")
     call = lambda: fl.flarepp_mix_ws(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"], out=out,
                                      workspace=ws)
+
+    if args.copy_calibration:
+        src = torch.empty(64 * 2 ** 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         call()

@@ -101,6 +101,12 @@ int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Q
                       int dtype, void* out, float* Qd, float* Q, float* Z, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* Test hook: while enabled (non-zero), every call skips the zero-shift pass and computes all three
+ * softmaxes with exact running maxima (the path the library otherwise takes only for rows whose
+ * zero-shift result fails its range check). Results agree with the default path to rounding.
+ * Process-wide; returns the previous setting. */
+int flarepp_debug_force_exact(int enable);
+
 /* Kernel timing. While enabled, every mixer call records a HIP event pair around each of its
  * kernels on the call's stream. flarepp_timing_read synchronizes those events, adds their elapsed
  * times per kernel into ms[0..n-1] and launch counts into counts[0..n-1] (n <= number of kernel

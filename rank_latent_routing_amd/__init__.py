@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.flarepp_mix_ws.restype = i32
     L.flarepp_mix_debug.argtypes = mix_args + [vp, vp, vp, vp, sz, vp]
     L.flarepp_mix_debug.restype = i32
+    L.flarepp_debug_force_exact.argtypes = [i32]
+    L.flarepp_debug_force_exact.restype = i32
     L.flarepp_timing_enable.argtypes = [i32]
     L.flarepp_timing_enable.restype = i32
     L.flarepp_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), i32]
@@ -179,6 +181,12 @@ def flarepp_mix_debug(K, V, S, Qseed, Qf, g, out=None, workspace=None, stream=No
     return out, Qd, Q, Z
 
 
+def flarepp_debug_force_exact(enable: bool = True) -> bool:
+    """Test hook: force the exact (running-maximum) softmax path for all later calls in this
+    process. Returns the previous setting."""
+    return bool(lib().flarepp_debug_force_exact(1 if enable else 0))
+
+
 def flarepp_timing_enable(enable: bool = True) -> None:
     lib().flarepp_timing_enable(1 if enable else 0)
 
@@ -195,5 +203,5 @@ def flarepp_timing_read() -> dict:
 
 
 __all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
-           "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
+           "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
            "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

@@ -7,7 +7,9 @@
 // log-sum-exp merge of Appendix B.3 (Eq. 29-33), chunks standing in for the pages' ranks.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -26,6 +28,15 @@ const char* const kKindNames[kNumKinds] = {"synthesis_partial", "merge_gate", "e
                                            "merge", "decode"};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Launch-plan overrides for tuning sweeps (read once per process).
+int env_int(const char* name, int fallback) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return fallback;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == 0 && x > 0 && x < (1 << 30)) ? (int)x : fallback;
+}
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Launch plan and workspace layout for one problem shape. The same function serves
@@ -33,10 +44,12 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Plan {
   int BH = 0;
   int Mp16 = 0, Mp32 = 0;
-  int part_plan = 0;  // kernel variant: 0 (16 latents/wave, 4 waves) .. 3 (64 latents/wave, 8 waves)
+  int part_plan = 0;  // kernel variant: 0 (16 latents/wave, 4 waves), 1 (32, 4), 2 (32, 8)
   int nlg = 1;        // latent groups (workgroups per chunk)
   int64_t chunk = 0;
   int nchunk = 0;
+  int part_gx = 0;    // grid x of the partial kernels
+  int dec_nw = 8;     // waves per decode workgroup
   int dec_gx = 0;
   int64_t dec_tpw = 0;
   size_t off_acc = 0, off_l = 0, off_m = 0, off_q = 0, off_z = 0, total = 0;
@@ -47,26 +60,35 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.BH = B * H;
   p.Mp16 = (M + 15) / 16 * 16;
   p.Mp32 = (M + 31) / 32 * 32;
+  // Partial-kernel variant: latents per wave x waves per workgroup, and latent groups per chunk.
   int lpw, nw;
   if (p.Mp16 <= 64) { p.part_plan = 0; lpw = 16; nw = 4; }
   else if (p.Mp16 <= 128) { p.part_plan = 1; lpw = 32; nw = 4; }
-  else if (p.Mp16 <= 256) { p.part_plan = 2; lpw = 64; nw = 4; }
-  else { p.part_plan = 3; lpw = 64; nw = 8; }
+  else { p.part_plan = 2; lpw = 32; nw = 8; }
   p.nlg = (int)ceil_div(p.Mp16, (int64_t)lpw * nw);
-  // Enough workgroups to fill 256 CUs about twice (8-wave workgroups) or four times (4-wave).
-  const int64_t target = nw == 8 ? 512 : 1024;
+  // About two rounds of resident workgroups over 256 CUs (8-wave groups: 2 per CU; 4-wave: 4).
+  const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", nw == 8 ? 1024 : 2048);
   int64_t nchunk = ceil_div(target, (int64_t)p.BH * p.nlg);
   nchunk = nchunk < 1 ? 1 : nchunk;
   const int64_t max_chunks = ceil_div(N, kStage);
   if (nchunk > max_chunks) nchunk = max_chunks;
   p.chunk = ceil_div(ceil_div(N, nchunk), kStage) * kStage;
   p.nchunk = (int)ceil_div(N, p.chunk);
-  // Decode: about 512 workgroups of kDecodeWaves waves, token ranges a multiple of 64.
-  int64_t gx = ceil_div(512, p.BH);
-  const int64_t max_gx = ceil_div(N, 64 * flarepp::kDecodeWaves);
+  // With several latent groups, grid x holds 8 chunks per XCD slot row (see partial_kernel).
+  p.part_gx = p.nlg == 1 ? p.nchunk : (int)(ceil_div(p.nchunk, 8) * 8 * p.nlg);
+  // Decode: wider workgroups when Q and Z need more than half of the CU's LDS.
+  p.dec_nw = flarepp::decode_lds_bytes(dtype, D, p.Mp32, flarepp::kDecodeWaves) > 80 * 1024
+                 ? flarepp::kDecodeWavesWide : flarepp::kDecodeWaves;
+  const int nw_env = env_int("FLAREPP_DECODE_WAVES", 0);
+  if (nw_env == 8 || nw_env == 12 || nw_env == 16) p.dec_nw = nw_env;
+  if (dtype == FLAREPP_FP32 && p.dec_nw == 12) p.dec_nw = 16;  // no 12-wave fp32 variant
+  const int64_t group = flarepp::decode_group_tokens(p.dec_nw);
+  const int64_t dec_target = env_int("FLAREPP_DECODE_WORKGROUPS", p.dec_nw == 8 ? 512 : 256);
+  int64_t gx = ceil_div(dec_target, p.BH);
+  const int64_t max_gx = ceil_div(N, group * p.dec_nw);
   if (gx > max_gx) gx = max_gx;
   if (gx < 1) gx = 1;
-  p.dec_tpw = ceil_div(ceil_div(N, gx), 64) * 64;
+  p.dec_tpw = ceil_div(ceil_div(N, gx), group) * group;
   p.dec_gx = (int)ceil_div(N, p.dec_tpw);
 
   const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
@@ -81,6 +103,8 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.total = off;
   return p;
 }
+
+std::atomic<int> g_force_exact{0};
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -172,11 +196,12 @@ int enqueue(const void* K, const void* V, const void* S, const void* Qseed, cons
   float* pm = reinterpret_cast<float*>(w + p.off_m);
   void* qbuf = w + p.off_q;
   void* zbuf = w + p.off_z;
-  const int gx_part = p.nchunk * p.nlg;
+  const int gx_part = p.part_gx;
 
   flarepp::PartialArgs pa{};
   pa.K = S; pa.V = S; pa.Q = Qseed; pa.H = H; pa.Mq = M; pa.Mp = p.Mp16; pa.N = N;
-  pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.part_acc = acc; pa.part_l = pl; pa.part_m = pm;
+  pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
+  pa.force_exact = g_force_exact.load(); pa.part_l = pl; pa.part_m = pm;
   if (run_kernel(0, st, [&] { return flarepp::launch_partial(pa, dtype, D, true, p.part_plan, gx_part, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
@@ -196,7 +221,8 @@ int enqueue(const void* K, const void* V, const void* S, const void* Qseed, cons
 
   flarepp::DecodeArgs da{};
   da.K = K; da.Q = qbuf; da.Z = zbuf; da.out = out; da.N = N; da.M = M; da.Mp = p.Mp32; da.tokens_per_wg = p.dec_tpw;
-  if (run_kernel(4, st, [&] { return flarepp::launch_decode(da, dtype, D, p.dec_gx, p.BH, st); }) != hipSuccess)
+  da.force_exact = pa.force_exact;
+  if (run_kernel(4, st, [&] { return flarepp::launch_decode(da, dtype, D, p.dec_nw, p.dec_gx, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
   return FLAREPP_OK;
 }
@@ -259,6 +285,8 @@ int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Q
   return mix_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, Qd, Q, Z, workspace, workspace_bytes,
                     false, stream);
 }
+
+int flarepp_debug_force_exact(int enable) { return g_force_exact.exchange(enable != 0); }
 
 int flarepp_timing_enable(int enable) {
   Timing& t = timing();

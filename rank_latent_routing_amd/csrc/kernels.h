@@ -9,8 +9,11 @@ namespace flarepp {
 
 // Tokens per LDS stage of the split-N partial kernels.
 constexpr int kStage = 128;
-// Waves per decode workgroup.
+// Waves per decode workgroup: 8, or 12 when the latent tensors in LDS allow one workgroup per CU
+// (16 is also built: 2 token blocks per wave group instead of 4). A wave group is 16 * TB tokens.
 constexpr int kDecodeWaves = 8;
+constexpr int kDecodeWavesWide = 12;
+inline int decode_group_tokens(int nw) { return nw == 16 ? 32 : 64; }
 
 // One split-N softmax pass (synthesis or encode) over [BH, N, D] keys/values.
 struct PartialArgs {
@@ -24,6 +27,8 @@ struct PartialArgs {
   int64_t N;       // tokens
   int64_t chunk;   // tokens per chunk, a multiple of kStage
   int nchunk;      // chunks per (b, h)
+  int nlg;         // latent groups per chunk (workgroups sharing one chunk's tokens)
+  int force_exact; // skip the zero-shift pass (test hook)
   float* part_acc; // [BH][nchunk][Mp][D]
   float* part_l;   // [BH][nchunk][Mp]
   float* part_m;   // [BH][nchunk][Mp]
@@ -55,13 +60,15 @@ struct DecodeArgs {
   int M;
   int Mp;          // M rounded up to 32
   int64_t tokens_per_wg;
+  int force_exact; // skip the zero-shift pass (test hook)
 };
 
 hipError_t launch_partial(const PartialArgs& a, int dtype, int D, bool synth, int plan, int grid_x,
                           int grid_y, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int grid_x, int grid_y,
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int grid_x, int grid_y,
                          hipStream_t stream);
-size_t decode_lds_bytes(int dtype, int D, int Mp);
+size_t decode_lds_bytes(int dtype, int D, int Mp, int nw);
+size_t partial_lds_bytes(int dtype, int D, int plan);
 
 }  // namespace flarepp

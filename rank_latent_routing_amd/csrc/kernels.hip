@@ -17,11 +17,12 @@
 // Numerics. Every logit is computed directly in log2 units: the query operand of each call
 // carries the factor c = log2(e)/sqrt(D) (folded into the normalized synthesis keys, and into Q
 // when merge_gate casts it), so one v_exp_f32 per score evaluates exp(q.k/sqrt(D)). A softmax is
-// invariant to the shift subtracted from its logits (Appendix B.3 Eq. 29); when the Cauchy-Schwarz
-// bound |logit| <= ||c q|| ||k|| of a tile is at most kFastBound (in log2 units) the kernels use
-// shift 0, which keeps every exponential in [2^-30, 2^30] and needs no running maximum. Tiles
-// beyond that bound switch to the exact running-maximum update (online softmax) for the rest of
-// the chunk (partials) or to a two-pass maximum over M (decode).
+// invariant to the shift subtracted from its logits (Appendix B.3 Eq. 29). The kernels first use
+// shift 0, which needs no running maximum, and check afterwards that it was exact: every row sum
+// in [2^-80, 2^100] and finite accumulators mean no exponential overflowed and no term within
+// 2^-24 of a row's largest was lost to underflow. Rows of a chunk (partials) or of a token group
+// (decode) that fail are recomputed with exact running maxima (online softmax over token stages,
+// or a two-pass maximum over the M latents).
 //
 // Routing queries in bf16 runs are carried as a pair hi + lo of bf16 values (hi = bf16(c q),
 // lo = bf16(c q - hi)) and every score is the sum of two chained MFMAs, so the queries keep about
@@ -33,9 +34,12 @@
 // receives column (l % 16), rows 4g..4g+3 of the 16x16 result. Score tiles are computed with the
 // keys as A so that the result lands with one latent per lane column and eight consecutive tokens
 // per lane, which is exactly the A (or B) operand layout of the following P.V product: the
-// probabilities never leave registers.
+// probabilities never leave registers. The P.V operand that runs along tokens (values) or latents
+// (Z) is read from a row-major LDS tile with ds_read_b64_tr_b16, whose 16-lane groups return
+// lane i, element j = element (i mod 4) of the 8 bytes addressed by group lane 4j + i/4.
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -46,12 +50,14 @@ typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRmsEps = 1e-6f;
-// Largest |logit| (log2 units) for which the zero-shift path is used.
-constexpr float kFastBound = 30.0f;
+// Synthesis seeds whose logit bound (log2 units) exceeds this go straight to the exact pass.
+constexpr float kFastBound = 90.0f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -59,9 +65,10 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor
 __device__ __forceinline__ float shfl(float v, int src) { return __shfl(v, src, 64); }
 
 // Score MFMAs start from a zero accumulator, so the register allocator may place their destination
-// on top of an A or B operand that dies there. Operands that feed several score MFMAs are kept live
-// until all of them have been issued: the MFMAs stay above a scheduling barrier that only they may
-// not cross, and an empty asm statement below it uses the operands.
+// on top of an A or B operand that dies there; the double-depth 16x16x32 bf16 form then returns
+// wrong products. Operands that feed several score MFMAs are kept live until all of them have been
+// issued: the MFMAs stay above a scheduling barrier that only they may not cross, and an empty asm
+// statement below it uses the operands.
 __device__ __forceinline__ void keep_live(const bf16x8& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void keep_live(const bf16x4& x) { asm volatile("" ::"v"(x)); }
 template <typename S>  // fp32 operand structs: one register per element
@@ -69,8 +76,8 @@ __device__ __forceinline__ void keep_live(const S& x) {
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(S) / sizeof(float)); i++) asm volatile("" ::"v"(x.v[i]));
 }
-// sched_barrier mask: every instruction class except MFMA may be scheduled across.
-constexpr int kAllButMfma = 0x7F6;  // 0x1 (all ALU) and 0x8 (MFMA) cleared
+// sched_barrier mask: VALU, SALU, memory and transcendental instructions may cross; MFMA may not.
+constexpr int kAllButMfma = 0x7F6;
 
 __device__ __forceinline__ f32x4 mfma_32k(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -82,6 +89,12 @@ __device__ __forceinline__ f32x4 mfma_4k(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Transposed LDS read of 4 bf16 (see the file header for the lane mapping). `p` points into LDS.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  lds_s16x4* q = (lds_s16x4*)(__attribute__((address_space(3))) char*)(p);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(q));
+}
+
 // ------------------------------------------------------------------------------------------
 // Per-dtype operand helpers. A "slice" is the D/4 consecutive elements of a row that one lane
 // feeds to the score MFMA (k = g*D/4 ... g*D/4 + D/4 - 1). An "oct" is the 8 consecutive tokens
@@ -89,22 +102,8 @@ __device__ __forceinline__ f32x4 mfma_4k(float a, float b, f32x4 c) {
 template <typename T, int D>
 struct Ops;
 
-template <>
-struct Ops<bf16, 32> {
-  using Slice = bf16x8;
+struct OpsBf16Common {
   using Oct = bf16x8;
-  __device__ static Slice zero_slice() { return Slice{}; }
-  __device__ static Slice load_slice(const bf16* row, int g) {
-    return *reinterpret_cast<const bf16x8*>(row + 8 * g);
-  }
-  __device__ static f32x4 qk(Slice a, Slice b, f32x4 c) { return mfma_32k(a, b, c); }
-  __device__ static float sumsq(Slice a) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) s += (float)a[i] * (float)a[i];
-    return s;
-  }
-  __device__ static Oct load_oct(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
   __device__ static Oct pack(f32x4 lo, f32x4 hi) {
     Oct r;
 #pragma unroll
@@ -125,16 +124,41 @@ struct Ops<bf16, 32> {
     return acc;
   }
   __device__ static f32x4 pv(Oct a, Oct b, f32x4 c) { return mfma_32k(a, b, c); }
+  // Oct of a row-major LDS tile along its rows: rows r0 + 8g .. r0 + 8g + 7 of column col0 + c
+  // for lane (c, g), read with two transposed loads (rows r0 + 8g + 4h + j for h = 0, 1).
+  __device__ static Oct load_oct_rows(const bf16* tile, int stride, int r0, int col0, int c, int g) {
+    const bf16* p = tile + (r0 + 8 * g + (c >> 2)) * stride + col0 + 4 * (c & 3);
+    const bf16x4 lo = lds_read_tr4(p);
+    const bf16x4 hi = lds_read_tr4(p + 4 * stride);
+    Oct o;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      o[i] = lo[i];
+      o[4 + i] = hi[i];
+    }
+    return o;
+  }
 };
 
 template <>
-struct Ops<bf16, 16> {
-  using Slice = bf16x4;
-  using Oct = bf16x8;
+struct Ops<bf16, 32> : OpsBf16Common {
+  using Slice = bf16x8;
   __device__ static Slice zero_slice() { return Slice{}; }
-  __device__ static Slice load_slice(const bf16* row, int g) {
-    return *reinterpret_cast<const bf16x4*>(row + 4 * g);
+  __device__ static Slice load_slice(const bf16* row, int g) { return *reinterpret_cast<const bf16x8*>(row + 8 * g); }
+  __device__ static f32x4 qk(Slice a, Slice b, f32x4 c) { return mfma_32k(a, b, c); }
+  __device__ static float sumsq(Slice a) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) s += (float)a[i] * (float)a[i];
+    return s;
   }
+};
+
+template <>
+struct Ops<bf16, 16> : OpsBf16Common {
+  using Slice = bf16x4;
+  __device__ static Slice zero_slice() { return Slice{}; }
+  __device__ static Slice load_slice(const bf16* row, int g) { return *reinterpret_cast<const bf16x4*>(row + 4 * g); }
   __device__ static f32x4 qk(Slice a, Slice b, f32x4 c) { return mfma_16k(a, b, c); }
   __device__ static float sumsq(Slice a) {
     float s = 0.f;
@@ -142,10 +166,6 @@ struct Ops<bf16, 16> {
     for (int i = 0; i < 4; i++) s += (float)a[i] * (float)a[i];
     return s;
   }
-  __device__ static Oct load_oct(const bf16* p) { return Ops<bf16, 32>::load_oct(p); }
-  __device__ static Oct pack(f32x4 lo, f32x4 hi) { return Ops<bf16, 32>::pack(lo, hi); }
-  __device__ static float osum(Oct p, float acc) { return Ops<bf16, 32>::osum(p, acc); }
-  __device__ static f32x4 pv(Oct a, Oct b, f32x4 c) { return Ops<bf16, 32>::pv(a, b, c); }
 };
 
 template <int D>
@@ -184,17 +204,6 @@ struct Ops<float, D> {
     for (int i = 0; i < D / 4; i++) s += a.v[i] * a.v[i];
     return s;
   }
-  __device__ static Oct load_oct(const float* p) {
-    Oct o;
-    const f32x4* q = reinterpret_cast<const f32x4*>(p);
-    f32x4 a = q[0], b = q[1];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      o.v[j] = a[j];
-      o.v[4 + j] = b[j];
-    }
-    return o;
-  }
   __device__ static Oct pack(f32x4 lo, f32x4 hi) {
     Oct r;
 #pragma unroll
@@ -214,6 +223,18 @@ struct Ops<float, D> {
     for (int j = 0; j < 8; j++) c = mfma_4k(a.v[j], b.v[j], c);
     return c;
   }
+  // fp32 tiles read along their rows are stored transposed: a stored row is a source column.
+  __device__ static Oct load_oct_rows(const float* tile_t, int stride, int r0, int col0, int c, int g) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(tile_t + (col0 + c) * stride + r0 + 8 * g);
+    const f32x4 a = q[0], b = q[1];
+    Oct o;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      o.v[j] = a[j];
+      o.v[4 + j] = b[j];
+    }
+    return o;
+  }
 };
 
 template <typename T>
@@ -223,22 +244,33 @@ __device__ __forceinline__ float to_f(T x) { return (float)x; }
 template <typename T>
 constexpr int kQParts = sizeof(T) == 2 ? 2 : 1;
 
-// 16-byte global/LDS chunk and its element view.
-struct alignas(16) Chunk {
-  uint32_t w[4];
+// LDS layout of a tile whose rows (tokens or latents) run along the k-range of a P.V operand:
+// bf16 keeps the rows (read with transposed loads), fp32 stores the transpose. The bf16 row stride
+// puts rows 4 apart 32 bytes apart modulo the LDS banks, so the transposed reads of a 16-lane
+// group (4 rows x 32 bytes) do not conflict.
+template <typename T, int D>
+struct RowTile {
+  static constexpr bool kTransposed = sizeof(T) == 4;
+  static constexpr int kRowStride = D + (D == 32 ? 16 : 8);
+  __host__ __device__ static constexpr int tstride(int rows) { return rows + 4; }
+  __host__ __device__ static constexpr int elems(int rows) { return kTransposed ? D * tstride(rows) : rows * kRowStride; }
+  __host__ __device__ static constexpr int stride(int rows) { return kTransposed ? tstride(rows) : kRowStride; }
 };
+
+// 16-byte global/LDS chunk.
+typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ void chunk_to_float(const Chunk& c, float* out) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      out[2 * i] = __uint_as_float(c.w[i] << 16);
-      out[2 * i + 1] = __uint_as_float(c.w[i] & 0xffff0000u);
+      out[2 * i] = __uint_as_float(c[i] << 16);
+      out[2 * i + 1] = __uint_as_float(c[i] & 0xffff0000u);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; i++) out[i] = __uint_as_float(c.w[i]);
+    for (int i = 0; i < 4; i++) out[i] = __uint_as_float(c[i]);
   }
 }
 
@@ -249,18 +281,45 @@ __device__ __forceinline__ Chunk float_to_chunk(const float* v) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       bf16x2 p = {(bf16)v[2 * i], (bf16)v[2 * i + 1]};
-      c.w[i] = __builtin_bit_cast(uint32_t, p);
+      c[i] = __builtin_bit_cast(uint32_t, p);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; i++) c.w[i] = __float_as_uint(v[i]);
+    for (int i = 0; i < 4; i++) c[i] = __float_as_uint(v[i]);
   }
   return c;
+}
+
+// Store one 16-byte chunk (elements col .. col + 16/sizeof(T) - 1 of row `row`) into a RowTile.
+template <typename T, int D>
+__device__ __forceinline__ void rowtile_store(T* tile, int rows, int row, int col, const Chunk& ck) {
+  using RT = RowTile<T, D>;
+  if constexpr (RT::kTransposed) {
+    float x[4];
+    chunk_to_float<T>(ck, x);
+#pragma unroll
+    for (int j = 0; j < 4; j++) tile[(col + j) * RT::tstride(rows) + row] = (T)x[j];
+  } else {
+    *reinterpret_cast<Chunk*>(tile + row * RT::kRowStride + col) = ck;
+  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8) with DPP lane moves.
+template <int DPP>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_move<0xB1>(v);   // quad_perm(1,0,3,2): lane ^ 1
+  if constexpr (N >= 4) v += dpp_move<0x4E>(v);   // quad_perm(2,3,0,1): lane ^ 2
+  if constexpr (N >= 8) v += dpp_move<0x141>(v);  // row_half_mirror: the other quad of 8 lanes
   return v;
 }
 
@@ -273,13 +332,25 @@ __device__ __forceinline__ int perm_row(int r, int half) { return 8 * (r >> 2) +
 //
 // Workgroup = NW waves; wave w owns latents [lat0, lat0 + LPW) as NLB blocks of 16. The workgroup
 // streams its token chunk through LDS in stages of kStage tokens (double-buffered): a row-major key
-// tile (A operand of the score MFMA) and a transposed value tile (B operand of the P.V MFMA). For
-// each latent row it accumulates the shift m, the sum l of exp2(logit - m) and the P.V product.
+// tile (A operand of the score MFMA) and a value RowTile (B operand of the P.V MFMA). Global loads
+// run two stages ahead of the compute through two register sets. For each latent row the kernel
+// accumulates the shift m, the sum l of exp2(logit - m) and the P.V product.
+//
+// A chunk is first streamed with shift 0 (no running maximum). That is exact whenever no
+// exponential overflowed and every term that matters stayed a normal float, which the kernel checks
+// afterwards on every row: l in [2^-80, 2^100] and a finite accumulator. If any row of the workgroup
+// fails, the whole chunk is streamed again with exact running maxima (online softmax).
+//
+// Grid: x enumerates (chunk, latent group) so that the latent groups of one chunk land on the same
+// XCD (workgroups are dealt to the 8 XCDs round-robin by x) and share its L2; y = b * H + h.
 template <typename T, int D, int LPW, int NW, bool SYNTH>
 __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   using O = Ops<T, D>;
   using Slice = typename O::Slice;
   using Oct = typename O::Oct;
+  using VT = RowTile<T, D>;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   constexpr int NLB = LPW / 16;
   constexpr int NDB = D / 16;
   constexpr int NT = NW * 64;
@@ -288,23 +359,37 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   constexpr int NCH = kStage * CPR;     // chunks per stage per tensor
   constexpr int PER = (NCH + NT - 1) / NT;
   constexpr int RS = D + CH;            // key tile row stride (elements)
-  constexpr int VS = kStage + CH;       // transposed value tile row stride (elements)
+  constexpr int VE = VT::elems(kStage); // value tile elements per buffer
+  constexpr int VSTR = VT::stride(kStage);
 
   extern __shared__ __align__(16) unsigned char smem[];
-  T* ks = reinterpret_cast<T*>(smem);                       // [2][kStage][RS]
-  T* vt = ks + 2 * kStage * RS;                              // [2][D][VS]
-  float* kmax_s = reinterpret_cast<float*>(vt + 2 * D * VS); // [2][NW]
+  T* ks = reinterpret_cast<T*>(smem);                   // [2][kStage][RS]
+  T* vt = ks + 2 * kStage * RS;                          // [2][VE]
+  int* fail_s = reinterpret_cast<int*>(vt + 2 * VE);     // one flag
+
+  // (chunk, latent group) of this workgroup.
+  int chunk_id, lg;
+  if (a.nlg == 1) {
+    chunk_id = blockIdx.x;
+    lg = 0;
+  } else {
+    const int slot = blockIdx.x >> 3;
+    lg = slot % a.nlg;
+    chunk_id = (slot / a.nlg) * 8 + (blockIdx.x & 7);
+  }
+  if (chunk_id >= a.nchunk) return;  // padding workgroups of the XCD mapping (whole workgroup)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int bh = blockIdx.y;
-  const int chunk_id = blockIdx.x % a.nchunk;
-  const int lg = blockIdx.x / a.nchunk;
   const int64_t n_begin = (int64_t)chunk_id * a.chunk;
   const int64_t n_end = (n_begin + a.chunk < a.N) ? n_begin + a.chunk : a.N;
+  const int nstage = (int)((n_end - n_begin + kStage - 1) / kStage);
   const int lat0 = (lg * NW + wave) * LPW;
   const bool active = lat0 < a.Mp;
+  if (tid == 0) *fail_s = 0;
+  __syncthreads();
 
   const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
   const T* vbase = reinterpret_cast<const T*>(a.V) + (int64_t)bh * a.N * D;
@@ -315,41 +400,25 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 
   // Query operands (B of the score MFMA): lane (c, g) holds slice g of latent lat0 + 16 lb + c.
   Slice qb[NLB], qlo[NLB];
-  float qss = 0.f;
 #pragma unroll
   for (int lb = 0; lb < NLB; lb++) {
     const int row = lat0 + 16 * lb + c;
     qb[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QP * D, g) : O::zero_slice();
     if constexpr (QP == 2) qlo[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QP * D + D, g) : O::zero_slice();
-    float ss = O::sumsq(qb[lb]);
-    ss += shfl_xor(ss, 16);
-    ss += shfl_xor(ss, 32);
-    qss = fmaxf(qss, ss);
   }
-  // Norm of the hi part; the lo part adds at most 2^-8 relative (covered by the 1.01 margin).
-  const float qnorm = sqrtf(wave_max(qss)) * 1.01f;
-  // Synthesis keys are c * N0(S): their norm is at most c * sqrt(D) (plus bf16 rounding).
   const float c_scale = kLog2e * rsqrtf((float)D);
-  const bool syn_fast = qnorm * c_scale * sqrtf((float)D) * 1.01f <= kFastBound;
 
   f32x4 zacc[NLB][NDB];
   float lsum[NLB], mrow[NLB];
-#pragma unroll
-  for (int lb = 0; lb < NLB; lb++) {
-    lsum[lb] = 0.f;
-    mrow[lb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; db++) zacc[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bool slow = false;      // running-maximum mode (wave-uniform)
-  bool seen_fast = false; // a zero-shift stage has been accumulated
 
-  Chunk kreg[PER], vreg[PER];
-  auto load_stage = [&](int64_t s0) {
+  // Two register sets of loaded chunks; set P holds stages of parity P.
+  Chunk kr[2][PER], vr[2][PER];
+  auto load_set = [&](auto P, int stage) {
+    const int64_t s0 = n_begin + (int64_t)stage * kStage;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
       const int q = tid + i * NT;
-      Chunk ck{}, cv{};
+      Chunk ck = {0u, 0u, 0u, 0u}, cv = {0u, 0u, 0u, 0u};
       if (q < NCH) {
         const int t = q / CPR, part = q % CPR;
         const int64_t n = s0 + t;
@@ -358,28 +427,27 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
           if constexpr (!SYNTH) cv = *reinterpret_cast<const Chunk*>(vbase + n * D + part * CH);
         }
       }
-      kreg[i] = ck;
-      vreg[i] = cv;
+      kr[decltype(P)::value][i] = ck;
+      vr[decltype(P)::value][i] = cv;
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_set = [&](auto P, int buf) {
     T* kdst = ks + buf * kStage * RS;
-    T* vdst = vt + buf * D * VS;
-    float kmx = 0.f;
+    T* vdst = vt + buf * VE;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
       const int q = tid + i * NT;
-      float x[CH];
-      chunk_to_float<T>(kreg[i], x);
-      float ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < CH; j++) ss += x[j] * x[j];
-#pragma unroll
-      for (int m = 1; m < CPR; m <<= 1) ss += shfl_xor(ss, m);
       if (q < NCH) {
         const int t = q / CPR, part = q % CPR;
         if constexpr (SYNTH) {
-          // N0 of the synthesis key row (Section 3.2, Eq. 5): keys c*N0(s), values N0(s).
+          // N0 of the synthesis key row (Section 3.2, Eq. 5): keys c*N0(s), values N0(s). The
+          // row's CPR chunks sit in consecutive lanes, reduced with DPP.
+          float x[CH];
+          chunk_to_float<T>(kr[decltype(P)::value][i], x);
+          float ss = 0.f;
+#pragma unroll
+          for (int j = 0; j < CH; j++) ss += x[j] * x[j];
+          ss = group_sum<CPR>(ss);
           const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kRmsEps);
           float kx[CH];
 #pragma unroll
@@ -388,136 +456,167 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
             kx[j] = x[j] * c_scale;
           }
           *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = float_to_chunk<T>(kx);
-#pragma unroll
-          for (int j = 0; j < CH; j++) vdst[(part * CH + j) * VS + t] = (T)x[j];
+          rowtile_store<T, D>(vdst, kStage, t, part * CH, float_to_chunk<T>(x));
         } else {
-          kmx = fmaxf(kmx, ss);
-          *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kreg[i];
-          float v[CH];
-          chunk_to_float<T>(vreg[i], v);
-#pragma unroll
-          for (int j = 0; j < CH; j++) vdst[(part * CH + j) * VS + t] = (T)v[j];
+          *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kr[decltype(P)::value][i];
+          rowtile_store<T, D>(vdst, kStage, t, part * CH, vr[decltype(P)::value][i]);
         }
       }
-    }
-    if constexpr (!SYNTH) {
-      kmx = wave_max(kmx);
-      if (lane == 0) kmax_s[buf * NW + wave] = kmx;
     }
   };
 
-  const int nstage = (int)((n_end - n_begin + kStage - 1) / kStage);
-  load_stage(n_begin);
-  store_stage(0);
-  __syncthreads();
-
-  for (int s = 0; s < nstage; s++) {
-    const int buf = s & 1;
-    const int64_t s0 = n_begin + (int64_t)s * kStage;
-    if (s + 1 < nstage) load_stage(s0 + kStage);
-
-    if (active) {
-      bool fast;
-      if constexpr (SYNTH) {
-        fast = syn_fast;
-      } else {
-        float km = 0.f;
+  // One stage of compute on buffer `buf` (tokens s0 .. s0 + nvalid - 1).
+  auto compute = [&](auto EXACT, int buf, int nvalid) {
+    constexpr bool exact = decltype(EXACT)::value;
+    const T* kt = ks + buf * kStage * RS;
+    const T* vtt = vt + buf * VE;
+    const int nsub = (nvalid + 31) / 32;
+    for (int st = 0; st < nsub; st++) {
+      const Slice ka0 = O::load_slice(kt + (32 * st + perm_row(c, 0)) * RS, g);
+      const Slice ka1 = O::load_slice(kt + (32 * st + perm_row(c, 1)) * RS, g);
+      f32x4 s0v[NLB], s1v[NLB];
 #pragma unroll
-        for (int w = 0; w < NW; w++) km = fmaxf(km, kmax_s[buf * NW + w]);
-        fast = qnorm * sqrtf(km) <= kFastBound;
-      }
-      if (!slow && !fast) {
-        slow = true;
-        if (!seen_fast) {
-#pragma unroll
-          for (int lb = 0; lb < NLB; lb++) mrow[lb] = -INFINITY;
+      for (int lb = 0; lb < NLB; lb++) {
+        s0v[lb] = O::qk(ka0, qb[lb], f32x4{0.f, 0.f, 0.f, 0.f});
+        s1v[lb] = O::qk(ka1, qb[lb], f32x4{0.f, 0.f, 0.f, 0.f});
+        if constexpr (QP == 2) {
+          s0v[lb] = O::qk(ka0, qlo[lb], s0v[lb]);
+          s1v[lb] = O::qk(ka1, qlo[lb], s1v[lb]);
         }
       }
-      if (!slow) seen_fast = true;
-
-      const T* kt = ks + buf * kStage * RS;
-      const T* vtt = vt + buf * D * VS;
-      const int nvalid = (int)((n_end - s0 < kStage) ? (n_end - s0) : kStage);
-      const int nsub = (nvalid + 31) / 32;
-      for (int st = 0; st < nsub; st++) {
-        const Slice ka0 = O::load_slice(kt + (32 * st + perm_row(c, 0)) * RS, g);
-        const Slice ka1 = O::load_slice(kt + (32 * st + perm_row(c, 1)) * RS, g);
-        f32x4 s0v[NLB], s1v[NLB];
+      __builtin_amdgcn_sched_barrier(kAllButMfma);
+      keep_live(ka0);
+      keep_live(ka1);
+      // Tokens past the end of the chunk do not enter the softmax.
+      if (32 * st + 32 > nvalid) {
 #pragma unroll
-        for (int lb = 0; lb < NLB; lb++) {
-          s0v[lb] = O::qk(ka0, qb[lb], f32x4{0.f, 0.f, 0.f, 0.f});
-          s1v[lb] = O::qk(ka1, qb[lb], f32x4{0.f, 0.f, 0.f, 0.f});
-          if constexpr (QP == 2) {
-            s0v[lb] = O::qk(ka0, qlo[lb], s0v[lb]);
-            s1v[lb] = O::qk(ka1, qlo[lb], s1v[lb]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(kAllButMfma);
-        keep_live(ka0);
-        keep_live(ka1);
-        // Tokens past the end of the chunk do not enter the softmax.
-        if (32 * st + 32 > nvalid) {
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const bool ok0 = 32 * st + 8 * g + i < nvalid;
-            const bool ok1 = 32 * st + 8 * g + 4 + i < nvalid;
-#pragma unroll
-            for (int lb = 0; lb < NLB; lb++) {
-              if (!ok0) s0v[lb][i] = -INFINITY;
-              if (!ok1) s1v[lb][i] = -INFINITY;
-            }
-          }
-        }
-        if (slow) {
+        for (int i = 0; i < 4; i++) {
+          const bool ok0 = 32 * st + 8 * g + i < nvalid;
+          const bool ok1 = 32 * st + 8 * g + 4 + i < nvalid;
 #pragma unroll
           for (int lb = 0; lb < NLB; lb++) {
-            float tm = fmaxf(fmaxf(fmaxf(s0v[lb][0], s0v[lb][1]), fmaxf(s0v[lb][2], s0v[lb][3])),
-                             fmaxf(fmaxf(s1v[lb][0], s1v[lb][1]), fmaxf(s1v[lb][2], s1v[lb][3])));
-            tm = fmaxf(tm, shfl_xor(tm, 16));
-            tm = fmaxf(tm, shfl_xor(tm, 32));
-            const float mold = mrow[lb];
-            const float mnew = fmaxf(mold, tm);
-            const float alpha = (mnew == mold) ? 1.0f : exp2_fast(mold - mnew);
-            const float shift = (mnew == -INFINITY) ? 0.0f : mnew;
-            mrow[lb] = mnew;
-            lsum[lb] *= alpha;
-            // Accumulator row 4g+i of this block belongs to the latent held by lane column 4g+i.
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const float ai = shfl(alpha, 4 * g + i);
-#pragma unroll
-              for (int db = 0; db < NDB; db++) zacc[lb][db][i] *= ai;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              s0v[lb][i] = exp2_fast(s0v[lb][i] - shift);
-              s1v[lb][i] = exp2_fast(s1v[lb][i] - shift);
-            }
+            if (!ok0) s0v[lb][i] = -INFINITY;
+            if (!ok1) s1v[lb][i] = -INFINITY;
           }
-        } else {
-#pragma unroll
-          for (int lb = 0; lb < NLB; lb++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              s0v[lb][i] = exp2_fast(s0v[lb][i]);
-              s1v[lb][i] = exp2_fast(s1v[lb][i]);
-            }
-        }
-        Oct vb[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; db++) vb[db] = O::load_oct(vtt + (16 * db + c) * VS + 32 * st + 8 * g);
-#pragma unroll
-        for (int lb = 0; lb < NLB; lb++) {
-          const Oct pa = O::pack(s0v[lb], s1v[lb]);
-          lsum[lb] = O::osum(pa, lsum[lb]);
-#pragma unroll
-          for (int db = 0; db < NDB; db++) zacc[lb][db] = O::pv(pa, vb[db], zacc[lb][db]);
         }
       }
+      if constexpr (exact) {
+#pragma unroll
+        for (int lb = 0; lb < NLB; lb++) {
+          float tm = fmaxf(fmaxf(fmaxf(s0v[lb][0], s0v[lb][1]), fmaxf(s0v[lb][2], s0v[lb][3])),
+                           fmaxf(fmaxf(s1v[lb][0], s1v[lb][1]), fmaxf(s1v[lb][2], s1v[lb][3])));
+          tm = fmaxf(tm, shfl_xor(tm, 16));
+          tm = fmaxf(tm, shfl_xor(tm, 32));
+          const float mold = mrow[lb];
+          const float mnew = fmaxf(mold, tm);
+          const float alpha = (mnew == mold) ? 1.0f : exp2_fast(mold - mnew);
+          const float shift = (mnew == -INFINITY) ? 0.0f : mnew;
+          mrow[lb] = mnew;
+          lsum[lb] *= alpha;
+          // Accumulator row 4g+i of this block belongs to the latent held by lane column 4g+i.
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float ai = shfl(alpha, 4 * g + i);
+#pragma unroll
+            for (int db = 0; db < NDB; db++) zacc[lb][db][i] *= ai;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            s0v[lb][i] = exp2_fast(s0v[lb][i] - shift);
+            s1v[lb][i] = exp2_fast(s1v[lb][i] - shift);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int lb = 0; lb < NLB; lb++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            s0v[lb][i] = exp2_fast(s0v[lb][i]);
+            s1v[lb][i] = exp2_fast(s1v[lb][i]);
+          }
+      }
+      Oct vb[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; db++) vb[db] = O::load_oct_rows(vtt, VSTR, 32 * st, 16 * db, c, g);
+#pragma unroll
+      for (int lb = 0; lb < NLB; lb++) {
+        const Oct pa = O::pack(s0v[lb], s1v[lb]);
+        lsum[lb] = O::osum(pa, lsum[lb]);
+#pragma unroll
+        for (int db = 0; db < NDB; db++) zacc[lb][db] = O::pv(pa, vb[db], zacc[lb][db]);
+      }
     }
-    if (s + 1 < nstage) store_stage(buf ^ 1);
+  };
+
+  // Stage s: store stage s+1 (register set P = (s+1) % 2) into its buffer, refill set P with stage
+  // s+3, compute stage s, barrier.
+  auto step = [&](auto P, auto EXACT, int s) {
+    if (s + 1 < nstage) store_set(P, (s + 1) & 1);
+    if (s + 3 < nstage) load_set(P, s + 3);
+    if (active) {
+      const int64_t left = n_end - (n_begin + (int64_t)s * kStage);
+      compute(EXACT, s & 1, left < kStage ? (int)left : kStage);
+    }
     __syncthreads();
+  };
+
+  auto run_chunk = [&](auto EXACT) {
+#pragma unroll
+    for (int lb = 0; lb < NLB; lb++) {
+      lsum[lb] = 0.f;
+      mrow[lb] = decltype(EXACT)::value ? -INFINITY : 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; db++) zacc[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    load_set(I0{}, 0);
+    if (nstage > 1) load_set(I1{}, 1);
+    store_set(I0{}, 0);
+    if (nstage > 2) load_set(I0{}, 2);
+    __syncthreads();
+    for (int s = 0; s < nstage; s += 2) {
+      step(I1{}, EXACT, s);
+      if (s + 1 < nstage) step(I0{}, EXACT, s + 1);
+    }
+  };
+
+  // Synthesis logits are bounded a priori by ||Qseed_m|| log2(e) (the keys have unit RMS): seeds
+  // far outside the zero-shift range go straight to the exact pass.
+  bool exact = a.force_exact != 0;
+  if constexpr (SYNTH) {
+    float qss = 0.f;
+#pragma unroll
+    for (int lb = 0; lb < NLB; lb++) {
+      float ss = O::sumsq(qb[lb]);
+      ss += shfl_xor(ss, 16);
+      ss += shfl_xor(ss, 32);
+      qss = fmaxf(qss, ss);
+    }
+    if (!__all(sqrtf(qss) * kLog2e * 1.01f <= kFastBound) && lane == 0) atomicOr(fail_s, 1);
+    __syncthreads();
+    exact = exact || *fail_s != 0;
   }
+  if (!exact) {
+    run_chunk(std::false_type{});
+    // Check every row of the zero-shift pass.
+    bool ok = true;
+    if (active) {
+#pragma unroll
+      for (int lb = 0; lb < NLB; lb++) {
+        float l = lsum[lb];
+        l += shfl_xor(l, 16);
+        l += shfl_xor(l, 32);
+        ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
+#pragma unroll
+        for (int db = 0; db < NDB; db++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) ok = ok && fabsf(zacc[lb][db][i]) <= 3.0e38f;
+      }
+    }
+    if (!__all(ok) && lane == 0) atomicOr(fail_s, 1);
+    __syncthreads();
+    exact = *fail_s != 0;
+  }
+  if (exact) run_chunk(std::true_type{});
 
   if (!active) return;
   // Partials of this chunk: l and m per latent, the P.V accumulator per latent and channel.
@@ -530,7 +629,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     const int row = lat0 + 16 * lb + c;
     if (g == 0 && row < a.Mp) {
       a.part_l[pbase + row] = l;
-      a.part_m[pbase + row] = slow ? mrow[lb] : 0.0f;
+      a.part_m[pbase + row] = mrow[lb];
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -594,28 +693,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Decode: every token's scores against all M routing queries, softmax over M, times Z
-// (Eq. 8, second call). The workgroup keeps c*Q (row-major, A operand of the score MFMA) and Z
-// (transposed, A operand of the P.V MFMA) in LDS; each wave takes groups of 64 tokens whose K
-// rows it reads straight from HBM as B operands.
-template <typename T, int D, int NW>
+// (Eq. 8, second call). The workgroup keeps c*Q (row-major, A operand of the score MFMA, hi then lo
+// per row) and Z (a RowTile: the A operand of the P.V MFMA runs along latents) in LDS; each wave
+// takes groups of 16 * TB tokens whose K rows it reads straight from HBM as B operands.
+template <typename T, int D, int NW, int TB>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   using O = Ops<T, D>;
   using Slice = typename O::Slice;
   using Oct = typename O::Oct;
+  using ZT = RowTile<T, D>;
   constexpr int NDB = D / 16;
   constexpr int NT = NW * 64;
   constexpr int CH = 16 / sizeof(T);
   constexpr int CPR = D / CH;
   constexpr int QP = kQParts<T>;
   constexpr int RQ = QP * D + CH;  // a row holds the hi part then (bf16) the lo part
-  constexpr int TB = 4;  // 16-token blocks per wave group
+  constexpr int TG = 16 * TB;      // tokens per wave group
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;  // multiple of 32
-  const int RZ = Mp + CH;
-  T* qs = reinterpret_cast<T*>(smem);     // [Mp][RQ]
-  T* zt = qs + Mp * RQ;                    // [D][RZ]
-  float* qn_s = reinterpret_cast<float*>(zt + D * RZ);
+  T* qs = reinterpret_cast<T*>(smem);  // [Mp][RQ]
+  T* zs = qs + Mp * RQ;                 // RowTile of Mp rows
+  const int ZSTR = ZT::stride(Mp);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -624,37 +723,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const T* qsrc = reinterpret_cast<const T*>(a.Q) + (int64_t)bh * Mp * QP * D;
   const T* zsrc = reinterpret_cast<const T*>(a.Z) + (int64_t)bh * Mp * D;
 
-  float qmx = 0.f;
   for (int q0 = 0; q0 < Mp * CPR; q0 += NT) {
     const int q = q0 + tid;
-    float ss = 0.f;
     if (q < Mp * CPR) {
       const int row = q / CPR, part = q % CPR;
-      const Chunk cq = *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + part * CH);
-      *reinterpret_cast<Chunk*>(qs + row * RQ + part * CH) = cq;
+      *reinterpret_cast<Chunk*>(qs + row * RQ + part * CH) =
+          *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + part * CH);
       if constexpr (QP == 2)
         *reinterpret_cast<Chunk*>(qs + row * RQ + D + part * CH) =
             *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + D + part * CH);
-      float x[CH];
-      chunk_to_float<T>(cq, x);
-#pragma unroll
-      for (int j = 0; j < CH; j++) ss += x[j] * x[j];
-      const Chunk cz = *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * CH);
-      chunk_to_float<T>(cz, x);
-#pragma unroll
-      for (int j = 0; j < CH; j++) zt[(part * CH + j) * RZ + row] = (T)x[j];
+      rowtile_store<T, D>(zs, Mp, row, part * CH, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * CH));
     }
-#pragma unroll
-    for (int m = 1; m < CPR; m <<= 1) ss += shfl_xor(ss, m);
-    qmx = fmaxf(qmx, ss);
   }
-  qmx = wave_max(qmx);
-  if (lane == 0) qn_s[wave] = qmx;
   __syncthreads();
-  float qm = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; w++) qm = fmaxf(qm, qn_s[w]);
-  const float qnorm = sqrtf(qm) * 1.01f;  // hi part; lo adds at most 2^-8 relative
 
   const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
   const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
@@ -663,19 +744,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int nlb = Mp / 32;
   const bool ragged = (a.M & 31) != 0;
 
-  for (int64_t base = t_begin + (int64_t)wave * 64; base < t_end; base += (int64_t)NW * 64) {
+  for (int64_t base = t_begin + (int64_t)wave * TG; base < t_end; base += (int64_t)NW * TG) {
     Slice kb[TB];
-    float kss = 0.f;
 #pragma unroll
     for (int t = 0; t < TB; t++) {
       const int64_t tok = base + 16 * t + c;
       kb[t] = (tok < a.N) ? O::load_slice(kbase + tok * D, g) : O::zero_slice();
-      float ss = O::sumsq(kb[t]);
-      ss += shfl_xor(ss, 16);
-      ss += shfl_xor(ss, 32);
-      kss = fmaxf(kss, ss);
     }
-    const bool fast = qnorm * sqrtf(wave_max(kss)) <= kFastBound;
 
     // Scores of latent block lb for every token block t: lane (c, g) gets token 16t + c and
     // latents 32 lb + 8g .. 32 lb + 8g + 7 (s0[t]: first four, s1[t]: last four).
@@ -714,10 +789,65 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    float shift[TB];
+    f32x4 yacc[TB][NDB];
+    float lsum[TB];
+    auto clear = [&]() {
 #pragma unroll
-    for (int t = 0; t < TB; t++) shift[t] = 0.f;
-    if (!fast) {
+      for (int t = 0; t < TB; t++) {
+        lsum[t] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; db++) yacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    // Probabilities, their sums and the P.V product over all latent blocks, with the exponentials
+    // shifted by `shift` (exact path) or unshifted (zero-shift path).
+    float shift[TB];
+    auto accumulate = [&](auto exact) {
+      for (int lb = 0; lb < nlb; lb++) {
+        Oct za[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; db++) za[db] = O::load_oct_rows(zs, ZSTR, 32 * lb, 16 * db, c, g);
+        f32x4 s0[TB], s1[TB];
+        scores_all(lb, s0, s1);
+#pragma unroll
+        for (int t = 0; t < TB; t++) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            if constexpr (decltype(exact)::value) {
+              s0[t][i] = exp2_fast(s0[t][i] - shift[t]);
+              s1[t][i] = exp2_fast(s1[t][i] - shift[t]);
+            } else {
+              s0[t][i] = exp2_fast(s0[t][i]);
+              s1[t][i] = exp2_fast(s1[t][i]);
+            }
+          }
+          const Oct pb = O::pack(s0[t], s1[t]);
+          lsum[t] = O::osum(pb, lsum[t]);
+#pragma unroll
+          for (int db = 0; db < NDB; db++) yacc[t][db] = O::pv(za[db], pb, yacc[t][db]);
+        }
+        __builtin_amdgcn_sched_barrier(kAllButMfma);
+#pragma unroll
+        for (int db = 0; db < NDB; db++) keep_live(za[db]);
+      }
+    };
+
+    // Zero-shift pass, then the check of every token's softmax over M (see the file header).
+    clear();
+    bool ok = a.force_exact == 0;
+    if (ok) accumulate(std::false_type{});
+#pragma unroll
+    for (int t = 0; t < TB; t++) {
+      float l = lsum[t];
+      l += shfl_xor(l, 16);
+      l += shfl_xor(l, 32);
+      ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
+#pragma unroll
+      for (int db = 0; db < NDB; db++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) ok = ok && fabsf(yacc[t][db][i]) <= 3.0e38f;
+    }
+    if (!__all(ok)) {
       // Two-pass maximum over the M latents for each token.
 #pragma unroll
       for (int t = 0; t < TB; t++) shift[t] = -INFINITY;
@@ -734,35 +864,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         shift[t] = fmaxf(shift[t], shfl_xor(shift[t], 16));
         shift[t] = fmaxf(shift[t], shfl_xor(shift[t], 32));
       }
+      clear();
+      accumulate(std::true_type{});
     }
 
-    f32x4 yacc[TB][NDB];
-    float lsum[TB];
-#pragma unroll
-    for (int t = 0; t < TB; t++) {
-      lsum[t] = 0.f;
-#pragma unroll
-      for (int db = 0; db < NDB; db++) yacc[t][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int lb = 0; lb < nlb; lb++) {
-      Oct za[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; db++) za[db] = O::load_oct(zt + (16 * db + c) * RZ + 32 * lb + 8 * g);
-      f32x4 s0[TB], s1[TB];
-      scores_all(lb, s0, s1);
-#pragma unroll
-      for (int t = 0; t < TB; t++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          s0[t][i] = exp2_fast(s0[t][i] - shift[t]);
-          s1[t][i] = exp2_fast(s1[t][i] - shift[t]);
-        }
-        const Oct pb = O::pack(s0[t], s1[t]);
-        lsum[t] = O::osum(pb, lsum[t]);
-#pragma unroll
-        for (int db = 0; db < NDB; db++) yacc[t][db] = O::pv(za[db], pb, yacc[t][db]);
-      }
-    }
 #pragma unroll
     for (int t = 0; t < TB; t++) {
       float l = lsum[t];
@@ -803,10 +908,15 @@ static hipError_t allow_lds(F* fn, size_t lds) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
+template <typename T, int D, int NW>
+static size_t partial_lds_t() {
+  constexpr int CH = 16 / sizeof(T);
+  return (size_t)(2 * kStage * (D + CH) + 2 * RowTile<T, D>::elems(kStage)) * sizeof(T) + 16;
+}
+
 template <typename T, int D, int LPW, int NW, bool SYNTH>
 static hipError_t launch_partial_t(const PartialArgs& a, int grid_x, int grid_y, hipStream_t st) {
-  constexpr int CH = 16 / sizeof(T);
-  const size_t lds = (size_t)(2 * kStage * (D + CH) + 2 * D * (kStage + CH)) * sizeof(T) + 2 * NW * sizeof(float);
+  const size_t lds = partial_lds_t<T, D, NW>();
   hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
@@ -818,8 +928,7 @@ static hipError_t launch_partial_d(const PartialArgs& a, int plan, int gx, int g
   switch (plan) {
     case 0: return launch_partial_t<T, D, 16, 4, SYNTH>(a, gx, gy, st);
     case 1: return launch_partial_t<T, D, 32, 4, SYNTH>(a, gx, gy, st);
-    case 2: return launch_partial_t<T, D, 64, 4, SYNTH>(a, gx, gy, st);
-    default: return launch_partial_t<T, D, 64, 8, SYNTH>(a, gx, gy, st);
+    default: return launch_partial_t<T, D, 32, 8, SYNTH>(a, gx, gy, st);
   }
 }
 
@@ -850,26 +959,50 @@ hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH,
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_t(const DecodeArgs& a, int gx, int gy, hipStream_t st) {
-  constexpr int NW = kDecodeWaves;
+static size_t decode_lds_t(int Mp, int NW) {
   constexpr int CH = 16 / sizeof(T);
-  const size_t lds = (size_t)(a.Mp * (kQParts<T> * D + CH) + D * (a.Mp + CH)) * sizeof(T) + NW * sizeof(float);
-  hipError_t e = allow_lds(decode_kernel<T, D, NW>, lds);
+  return (size_t)(Mp * (kQParts<T> * D + CH) + RowTile<T, D>::elems(Mp)) * sizeof(T) + NW * sizeof(float);
+}
+
+template <typename T, int D, int NW, int TB>
+static hipError_t launch_decode_t(const DecodeArgs& a, int gx, int gy, hipStream_t st) {
+  const size_t lds = decode_lds_t<T, D>(a.Mp, NW);
+  hipError_t e = allow_lds(decode_kernel<T, D, NW, TB>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<T, D, NW>), dim3(gx, gy), dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, NW, TB>), dim3(gx, gy), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int gx, int gy, hipStream_t st) {
-  if (dtype == 1) return D == 32 ? launch_decode_t<bf16, 32>(a, gx, gy, st) : launch_decode_t<bf16, 16>(a, gx, gy, st);
-  return D == 32 ? launch_decode_t<float, 32>(a, gx, gy, st) : launch_decode_t<float, 16>(a, gx, gy, st);
+// Waves per workgroup and 16-token blocks per wave group: (8, 4), (12, 4) or (16, 2).
+// fp32 runs use (8, 4) or (16, 2): four fp32 token blocks do not fit the register budget of 12 waves.
+template <typename T, int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, int nw, int gx, int gy, hipStream_t st) {
+  if (nw == 16) return launch_decode_t<T, D, 16, 2>(a, gx, gy, st);
+  if constexpr (sizeof(T) == 2) {
+    if (nw == 12) return launch_decode_t<T, D, 12, 4>(a, gx, gy, st);
+  }
+  if (nw != 8) return hipErrorInvalidValue;
+  return launch_decode_t<T, D, 8, 4>(a, gx, gy, st);
 }
 
-size_t decode_lds_bytes(int dtype, int D, int Mp) {
-  const int es = dtype == 1 ? 2 : 4;
-  const int CH = 16 / es;
-  const int qp = dtype == 1 ? 2 : 1;
-  return (size_t)(Mp * (qp * D + CH) + D * (Mp + CH)) * es + kDecodeWaves * sizeof(float);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int gx, int gy, hipStream_t st) {
+  if (dtype == 1) return D == 32 ? launch_decode_d<bf16, 32>(a, nw, gx, gy, st) : launch_decode_d<bf16, 16>(a, nw, gx, gy, st);
+  return D == 32 ? launch_decode_d<float, 32>(a, nw, gx, gy, st) : launch_decode_d<float, 16>(a, nw, gx, gy, st);
+}
+
+size_t decode_lds_bytes(int dtype, int D, int Mp, int nw) {
+  if (dtype == 1) return D == 32 ? decode_lds_t<bf16, 32>(Mp, nw) : decode_lds_t<bf16, 16>(Mp, nw);
+  return D == 32 ? decode_lds_t<float, 32>(Mp, nw) : decode_lds_t<float, 16>(Mp, nw);
+}
+
+size_t partial_lds_bytes(int dtype, int D, int plan) {
+  const int nw = plan >= 2 ? 8 : 4;
+  if (dtype == 1) {
+    if (D == 32) return nw == 8 ? partial_lds_t<bf16, 32, 8>() : partial_lds_t<bf16, 32, 4>();
+    return nw == 8 ? partial_lds_t<bf16, 16, 8>() : partial_lds_t<bf16, 16, 4>();
+  }
+  if (D == 32) return nw == 8 ? partial_lds_t<float, 32, 8>() : partial_lds_t<float, 32, 4>();
+  return nw == 8 ? partial_lds_t<float, 16, 8>() : partial_lds_t<float, 16, 4>();
 }
 
 }  // namespace flarepp

@@ -23,7 +23,10 @@ def _gpu():
     fl.lib()  # fails loudly when the library is missing
 
 
-def _check(w, heads=None, block=None, stages=True, label=""):
+def _check(w, heads=None, block=None, stages=True, label="", bf16_storage=False):
+    """bf16_storage: for bf16 outputs whose spread reaches several times their RMS, the per-element
+    bar adds the representation error of the two bf16 tensors on the path to Y (Y itself, and the
+    latents Z that decode reads), 2^-8 |Y_ref| together; the latent stages keep the plain bar."""
     say(f"[parity] {label or w.name}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
     Y, Qd, Q, Z = run_gpu(w, debug=True)
     assert np.isfinite(Y).all()
@@ -31,7 +34,12 @@ def _check(w, heads=None, block=None, stages=True, label=""):
     pairs = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
     for b, h in pairs:
         ref = oracle_head(w, b, h, block=block)
-        errs = {"Y": slice_err(Y[b, h], ref["Y"], w.dtype)}
+        if bf16_storage:
+            rms = np.sqrt(np.mean(ref["Y"] ** 2))
+            excess = np.abs(Y[b, h] - ref["Y"]) - 2.0 ** -8 * np.abs(ref["Y"])
+            errs = {"Y": max(float(excess.max()), 0.0) / rms}
+        else:
+            errs = {"Y": slice_err(Y[b, h], ref["Y"], w.dtype)}
         if stages:
             errs.update(Qd=slice_err(Qd[b, h], ref["Qd"], w.dtype), Q=slice_err(Q[b, h], ref["Q"], w.dtype),
                         Z=slice_err(Z[b, h], ref["Z"], w.dtype))
@@ -95,34 +103,60 @@ def test_latent_counts_gaussian_inputs(M):
     _check(make_workload(3, B=1, H=2, N=700, M=M, seed=3 * M), label=f"gauss M={M}")
 
 
-@pytest.mark.parametrize("dtype,kscale,qscale", [("fp32", 4.0, 4.0), ("bf16", 2.0, 3.0)])
-def test_wide_logits_take_the_exact_path(dtype, kscale, qscale):
-    # Scaled keys and seeds push the logit bounds past the zero-shift window, so the calls run with
-    # exact running maxima. The bf16 scales stay moderate: bf16 synthesis keys carry a relative
-    # rounding of 2^-9, which turns into a logit error proportional to the logit itself.
-    w = make_workload(3, B=1, H=2, N=3000, M=64, dtype=dtype, seed=11)
+@pytest.fixture
+def force_exact():
+    import rank_latent_routing_amd as fl
+    prev = fl.flarepp_debug_force_exact(True)
+    yield
+    fl.flarepp_debug_force_exact(prev)
+
+
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(B=1, H=3, N=5000)), (3, dict(B=1)),
+                                    (4, dict(B=1, H=2, N=20000)), (5, dict(H=1, N=70000)),
+                                    (2, dict(B=1, H=2, N=700, M=17, D=32, dtype="fp32"))])
+def test_exact_path_everywhere(force_exact, cfg, kw):
+    # The running-maximum softmaxes of all three calls, on well-conditioned inputs.
+    _check(make_workload(cfg, **kw), label=f"exact cfg{cfg} {kw}")
+
+
+def _decode_rows_out_of_range(w, b=0, h=0):
+    """Fraction of tokens whose zero-shift decode row sum, sum_m 2^(log2(e) q_m.k/sqrt(D)), falls
+    outside [2^-80, 2^100]: the tokens the library must recompute with running maxima."""
+    import oracle
+    K, S = w.f64("K")[b, h], w.f64("S")[b, h]
+    Q = oracle.gate(w.f64("Qf")[h], oracle.synthesis(w.f64("Qseed")[h], S), float(w.g[h]))
+    L = (K @ Q.T) * (np.log2(np.e) / np.sqrt(K.shape[1]))
+    m = L.max(axis=1)
+    lsum = m + np.log2(np.exp2(L - m[:, None]).sum(axis=1))
+    return float(((lsum > 100.0) | (lsum < -80.0)).mean())
+
+
+def test_wide_logits_take_the_exact_path():
+    # Keys scaled x24: routing logits reach about 200 (log2 units), beyond the range the zero-shift
+    # pass accepts, so encode chunks and decode tokens fall back to running maxima. The routing
+    # logits stay accurate in bf16 runs (exact bf16 keys, hi/lo queries, fp32 accumulation).
+    w = make_workload(3, B=1, H=2, N=3000, M=64, seed=11)
     from workloads.gen import _store
-    w.K = _store(w.f64("K") * kscale, dtype)
-    w.Qseed = _store(w.f64("Qseed") * qscale, dtype)
-    c = np.log2(np.e) / np.sqrt(w.D)
-    syn_bound = np.linalg.norm(w.f64("Qseed"), axis=-1).max() * np.log2(np.e)
-    say(f"[parity] wide logits {dtype}: synthesis logit bound {syn_bound:.1f} (zero-shift window 30)")
-    assert syn_bound > 30.0
-    _check(w, label=f"wide logits {dtype}")
+    w.K = _store(w.f64("K") * 24.0, "bf16")
+    assert _decode_rows_out_of_range(w, 0, 0) > 0.05
+    _check(w, label="wide logits")
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_zero_shift_to_exact_switch_inside_a_chunk(dtype):
-    # Large keys only in a late token range and in a middle range: earlier stages of a chunk are
-    # accumulated with shift 0 and the later ones switch to the running maximum; decode token groups
-    # mix both paths.
+@pytest.mark.parametrize("dtype,big", [("fp32", 36.0), ("bf16", 40.0)])
+def test_zero_shift_and_exact_chunks_mixed(dtype, big):
+    # Large keys in two token ranges: the chunks and decode token groups that hold them fall back
+    # to the exact path, all others keep the zero-shift result.
     w = make_workload(4, B=1, H=2, N=20000, dtype=dtype)
     from workloads.gen import _store
     K = w.f64("K")
-    K[:, :, 17000:17500] *= 6.0
-    K[:, :, 8000:8100] *= 5.0
+    K[:, :, 17000:17500] *= big
+    K[:, :, 8000:8100] *= big
     w.K = _store(K, dtype)
-    _check(w, label=f"switch {dtype}")
+    frac = _decode_rows_out_of_range(w, 0, 0)
+    assert 0.0 < frac < 0.03
+    # The decode rows of the large keys are one-hot picks of single latents, about 6 RMS(Y) in size:
+    # in bf16 their own storage costs up to 1.2% of RMS, beyond what the plain bar leaves.
+    _check(w, label=f"mixed {dtype}", bf16_storage=(dtype == "bf16"))
 
 
 def test_gate_one_and_zero_everywhere():
