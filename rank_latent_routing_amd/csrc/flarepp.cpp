@@ -82,7 +82,8 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   const int nw_env = env_int("FLAREPP_DECODE_WAVES", 0);
   if (nw_env == 8 || nw_env == 12 || nw_env == 16) p.dec_nw = nw_env;
   if (dtype == FLAREPP_FP32 && p.dec_nw == 12) p.dec_nw = 16;  // no 12-wave fp32 variant
-  const int64_t group = flarepp::decode_group_tokens(p.dec_nw);
+  if (dtype == FLAREPP_BF16 && D == 32 && p.dec_nw == 16) p.dec_nw = 12;  // no 16-wave variant
+  const int64_t group = flarepp::decode_group_tokens(dtype, D, p.dec_nw);
   const int64_t dec_target = env_int("FLAREPP_DECODE_WORKGROUPS", p.dec_nw == 8 ? 512 : 256);
   int64_t gx = ceil_div(dec_target, p.BH);
   const int64_t max_gx = ceil_div(N, group * p.dec_nw);
@@ -97,7 +98,7 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.off_acc = off; off = align256(off + nrow * D * sizeof(float));
   p.off_l = off;   off = align256(off + nrow * sizeof(float));
   p.off_m = off;   off = align256(off + nrow * sizeof(float));
-  const size_t qparts = dtype == FLAREPP_BF16 ? 2 : 1;  // bf16 routing queries as a hi/lo pair
+  const size_t qparts = dtype == FLAREPP_BF16 ? 3 : 1;  // bf16 routing queries: hi, lo and fp16
   p.off_q = off;   off = align256(off + (size_t)p.BH * p.Mp32 * qparts * D * es);
   p.off_z = off;   off = align256(off + (size_t)p.BH * p.Mp32 * D * es);
   p.total = off;

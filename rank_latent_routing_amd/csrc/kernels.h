@@ -10,17 +10,21 @@ namespace flarepp {
 // Tokens per LDS stage of the split-N partial kernels.
 constexpr int kStage = 128;
 // Waves per decode workgroup: 8, or 12 when the latent tensors in LDS allow one workgroup per CU
-// (16 is also built: 2 token blocks per wave group instead of 4). A wave group is 16 * TB tokens.
+// (16 is also built). Tokens per wave group: bf16 with D = 32 always 64 (two blocks of 32);
+// otherwise 16 * TB with TB = 4 (8 or 12 waves) or 2 (16 waves).
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeWavesWide = 12;
-inline int decode_group_tokens(int nw) { return nw == 16 ? 32 : 64; }
+inline int decode_group_tokens(int dtype, int D, int nw) {
+  if (dtype == 1 && D == 32) return 64;
+  return nw == 16 ? 32 : 64;
+}
 
 // One split-N softmax pass (synthesis or encode) over [BH, N, D] keys/values.
 struct PartialArgs {
   const void* K;   // keys [BH][N][D] (synthesis: the un-normalized synthesis keys S)
   const void* V;   // values [BH][N][D] (unused by synthesis: values are the normalized keys)
-  const void* Q;   // query rows: synthesis Qseed [H][Mq][D]; encode c*Q [BH][Mq][P][D]
-                   // (P = 2 parts hi, lo for bf16; 1 for fp32)
+  const void* Q;   // query rows: synthesis Qseed [H][Mq][D]; encode c*Q [BH][Mq][R*D]
+                   // (R = 3 parts hi, lo, fp16 for bf16; 1 for fp32)
   int H;           // heads (synthesis queries are indexed by bh % H)
   int Mq;          // rows per query block (rows >= Mq read as zero)
   int Mp;          // latent rows in the partial buffers (M rounded up to 16)
@@ -46,14 +50,14 @@ struct MergeArgs {
   int H;
   const void* Qf;  // gate only: [H][M][D] dtype
   const float* g;  // gate only: [H]
-  void* out;       // gate: c*Q [BH][Mout][P][D] (P parts as above); merge: Z [BH][Mout][D]
+  void* out;       // gate: c*Q [BH][Mout][R*D] (R parts as above); merge: Z [BH][Mout][D]
   float* dbg_qd;   // optional fp32 [BH][M][D] (gate only): Qd
   float* dbg_out;  // optional fp32 [BH][M][D]: Q (gate) or Z (merge)
 };
 
 struct DecodeArgs {
   const void* K;   // [BH][N][D]
-  const void* Q;   // c*Q [BH][Mp][P][D]
+  const void* Q;   // c*Q rows [BH][Mp][R*D] (R = 3 parts hi, lo, fp16 for bf16; 1 for fp32)
   const void* Z;   // Z [BH][Mp][D]
   void* out;       // [BH][N][D]
   int64_t N;

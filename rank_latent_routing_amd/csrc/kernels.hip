@@ -52,6 +52,9 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -88,6 +91,27 @@ __device__ __forceinline__ f32x4 mfma_16k(bf16x4 a, bf16x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_4k(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// 32x32x16 bf16 (gfx950): lane l supplies row (l % 32) of A and column (l % 32) of B with
+// k = 8 (l / 32) .. 8 (l / 32) + 7, and receives column (l % 32), rows 8 (v / 4) + 4 (l / 32) + v % 4
+// (v = 0..15) of the 32x32 result.
+__device__ __forceinline__ f32x16 mfma_32x32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void keep_live(const f32x16& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep_live(const f16x8& x) { asm volatile("" ::"v"(x)); }
+// bf16 -> fp16, rounding to nearest even (exact inside the fp16 range; overflow gives inf, which
+// the range check of the zero-shift pass catches).
+__device__ __forceinline__ f16x8 to_f16x8(bf16x8 x) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; e++) r[e] = (f16)(float)x[e];
+  return r;
+}
+// Row (or column) of the 32x32 result held in slot v by a lane of half h = l / 32.
+__host__ __device__ constexpr int row32(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
 // Transposed LDS read of 4 bf16 (see the file header for the lane mapping). `p` points into LDS.
 __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
@@ -139,6 +163,31 @@ struct OpsBf16Common {
     return o;
   }
 };
+
+// B operand of a 32x32x16 P.V MFMA from a row-major bf16 LDS tile whose rows run along k: lane l
+// (dims 16 cb + i, cb = (l / 16) % 2, i = l % 16, half h = l / 32) receives rows
+// r0 + row32(e, h) (e = 0..7) of column col0 + 16 cb + i, read with two transposed loads.
+__device__ __forceinline__ bf16x8 load_rows32(const bf16* tile, int stride, int r0, int col0, int lane) {
+  const int i = lane & 15, cb = (lane >> 4) & 1, h = lane >> 5;
+  const bf16* p = tile + (r0 + 4 * h + (i >> 2)) * stride + col0 + 16 * cb + 4 * (i & 3);
+  const bf16x4 lo = lds_read_tr4(p);
+  const bf16x4 hi = lds_read_tr4(p + 8 * stride);
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    o[e] = lo[e];
+    o[4 + e] = hi[e];
+  }
+  return o;
+}
+// Eight consecutive slots (8 t .. 8 t + 7) of a 32x32 result as the bf16 A operand of the next
+// 32x32x16 MFMA (k = rows 16 t .. 16 t + 15 of the result).
+__device__ __forceinline__ bf16x8 pack32(const f32x16& x, int t) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; e++) r[e] = (bf16)x[8 * t + e];
+  return r;
+}
 
 template <>
 struct Ops<bf16, 32> : OpsBf16Common {
@@ -240,9 +289,14 @@ struct Ops<float, D> {
 template <typename T>
 __device__ __forceinline__ float to_f(T x) { return (float)x; }
 
-// Parts per routing-query row in the workspace: bf16 keeps a hi/lo pair, fp32 one exact value.
+// Parts per routing query in the score MFMAs of the exact passes: bf16 keeps a hi/lo pair, fp32
+// one exact value.
 template <typename T>
 constexpr int kQParts = sizeof(T) == 2 ? 2 : 1;
+// Elements per routing-query row in the workspace: bf16 rows hold hi, lo and the fp16 query (the
+// score operand of the zero-shift passes, stored as raw fp16 bits); fp32 rows hold the query.
+template <typename T>
+constexpr int kQRow = sizeof(T) == 2 ? 3 : 1;
 
 // LDS layout of a tile whose rows (tokens or latents) run along the k-range of a P.V operand:
 // bf16 keeps the rows (read with transposed loads), fp32 stores the transpose. The bf16 row stride
@@ -395,16 +449,47 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   const T* vbase = reinterpret_cast<const T*>(a.V) + (int64_t)bh * a.N * D;
   // Synthesis queries are the seeds (one exact part); encode queries are the workspace hi/lo pair.
   constexpr int QP = SYNTH ? 1 : kQParts<T>;
-  const T* qbase = reinterpret_cast<const T*>(a.Q) +
-                   (SYNTH ? (int64_t)(bh % a.H) * a.Mq * D : (int64_t)bh * a.Mq * QP * D);
+  constexpr int QRS = SYNTH ? D : kQRow<T> * D;  // query row stride (elements)
+  const T* qbase = reinterpret_cast<const T*>(a.Q) + (int64_t)(SYNTH ? bh % a.H : bh) * a.Mq * QRS;
 
   // Query operands (B of the score MFMA): lane (c, g) holds slice g of latent lat0 + 16 lb + c.
   Slice qb[NLB], qlo[NLB];
+  auto load_queries = [&]() {
 #pragma unroll
-  for (int lb = 0; lb < NLB; lb++) {
-    const int row = lat0 + 16 * lb + c;
-    qb[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QP * D, g) : O::zero_slice();
-    if constexpr (QP == 2) qlo[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QP * D + D, g) : O::zero_slice();
+    for (int lb = 0; lb < NLB; lb++) {
+      const int row = lat0 + 16 * lb + c;
+      qb[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QRS, g) : O::zero_slice();
+      if constexpr (QP == 2) qlo[lb] = (row < a.Mq) ? O::load_slice(qbase + (int64_t)row * QRS + D, g) : O::zero_slice();
+    }
+  };
+  // bf16 runs with D = 32 and whole 32-latent blocks per wave take the zero-shift pass with
+  // 32x32x16 MFMAs on fp16 score operands (keys and queries in fp16, one MFMA per 16 dims) and bf16
+  // probabilities and values; the exact pass keeps 16x16x32 bf16 MFMAs with hi/lo queries.
+  constexpr bool kWide = sizeof(T) == 2 && D == 32 && LPW % 32 == 0;
+  constexpr int NB = kWide ? LPW / 32 : 1;
+  const int h32 = lane >> 5;
+  // Wide query operands: lane l holds dims 16 kh + 8 h .. + 7 of latent lat0 + 32 nb + l % 32
+  // (encode: the fp16 part of the workspace row; synthesis: the bf16 seeds converted).
+  f16x8 qw[NB][2];
+  if constexpr (kWide) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const int row = lat0 + 32 * nb + (lane & 31);
+#pragma unroll
+      for (int kh = 0; kh < 2; kh++) {
+        if (row >= a.Mq) {
+          qw[nb][kh] = f16x8{};
+        } else if constexpr (SYNTH) {
+          qw[nb][kh] = to_f16x8(*reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(qbase) +
+                                                                 (int64_t)row * QRS + 16 * kh + 8 * h32));
+        } else {
+          qw[nb][kh] = *reinterpret_cast<const f16x8*>(reinterpret_cast<const bf16*>(qbase) + (int64_t)row * QRS +
+                                                       2 * D + 16 * kh + 8 * h32);
+        }
+      }
+    }
+  } else {
+    load_queries();
   }
   const float c_scale = kLog2e * rsqrtf((float)D);
 
@@ -431,7 +516,10 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       vr[decltype(P)::value][i] = cv;
     }
   };
-  auto store_set = [&](auto P, int buf) {
+  // Store a register set into LDS buffer `buf`. F16 (bf16 runs of the wide zero-shift pass): the
+  // key tile holds fp16 keys.
+  auto store_set = [&](auto P, int buf, auto F16) {
+    constexpr bool f16keys = decltype(F16)::value && sizeof(T) == 2;
     T* kdst = ks + buf * kStage * RS;
     T* vdst = vt + buf * VE;
 #pragma unroll
@@ -455,10 +543,21 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
             x[j] *= inv;
             kx[j] = x[j] * c_scale;
           }
-          *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = float_to_chunk<T>(kx);
+          if constexpr (f16keys) {
+            f16x8 hk;
+#pragma unroll
+            for (int j = 0; j < 8; j++) hk[j] = (f16)kx[j];
+            *reinterpret_cast<f16x8*>(kdst + t * RS + part * CH) = hk;
+          } else {
+            *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = float_to_chunk<T>(kx);
+          }
           rowtile_store<T, D>(vdst, kStage, t, part * CH, float_to_chunk<T>(x));
         } else {
-          *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kr[decltype(P)::value][i];
+          if constexpr (f16keys)
+            *reinterpret_cast<f16x8*>(kdst + t * RS + part * CH) =
+                to_f16x8(__builtin_bit_cast(bf16x8, kr[decltype(P)::value][i]));
+          else
+            *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kr[decltype(P)::value][i];
           rowtile_store<T, D>(vdst, kStage, t, part * CH, vr[decltype(P)::value][i]);
         }
       }
@@ -548,10 +647,86 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     }
   };
 
+  // Zero-shift stage compute with 32x32x16 MFMAs (kWide): per 32-token sub-tile, the fp16 key rows
+  // (A operand, token 32 st + l % 32) against each 32-latent block's fp16 queries, then the bf16
+  // probabilities of result slots 8t .. 8t+7 (tokens row32(8t + e, h)) times the value rows of the
+  // same tokens.
+  f32x16 zw[NB];
+  float lw[NB];
+  auto compute_wide = [&](int buf, int nvalid) {
+    if constexpr (kWide) {
+      const bf16* kt = reinterpret_cast<const bf16*>(ks) + buf * kStage * RS;
+      const bf16* vtt = reinterpret_cast<const bf16*>(vt) + buf * VE;
+      const int nsub = (nvalid + 31) / 32;
+      for (int st = 0; st < nsub; st++) {
+        const bf16* krow = kt + (32 * st + (lane & 31)) * RS + 8 * h32;
+        const f16x8 ka0 = *reinterpret_cast<const f16x8*>(krow);
+        const f16x8 ka1 = *reinterpret_cast<const f16x8*>(krow + 16);
+        f32x16 sw[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          sw[nb] = mfma_32x32_f16(ka0, qw[nb][0], f32x16{});
+          sw[nb] = mfma_32x32_f16(ka1, qw[nb][1], sw[nb]);
+        }
+        __builtin_amdgcn_sched_barrier(kAllButMfma);
+        keep_live(ka0);
+        keep_live(ka1);
+        if (32 * st + 32 > nvalid) {
+#pragma unroll
+          for (int v = 0; v < 16; v++)
+            if (32 * st + row32(v, h32) >= nvalid)
+#pragma unroll
+              for (int nb = 0; nb < NB; nb++) sw[nb][v] = -INFINITY;
+        }
+        const bf16x8 vb0 = load_rows32(vtt, VSTR, 32 * st, 0, lane);
+        const bf16x8 vb1 = load_rows32(vtt, VSTR, 32 * st + 16, 0, lane);
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+#pragma unroll
+          for (int v = 0; v < 16; v++) sw[nb][v] = exp2_fast(sw[nb][v]);
+          const bf16x8 p0 = pack32(sw[nb], 0), p1 = pack32(sw[nb], 1);
+          lw[nb] = O::osum(p1, O::osum(p0, lw[nb]));
+          zw[nb] = mfma_32x32(p0, vb0, zw[nb]);
+          zw[nb] = mfma_32x32(p1, vb1, zw[nb]);
+          __builtin_amdgcn_sched_barrier(kAllButMfma);
+          keep_live(p0);
+          keep_live(p1);
+        }
+        keep_live(vb0);
+        keep_live(vb1);
+      }
+    }
+  };
+  auto run_chunk_wide = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      lw[nb] = 0.f;
+      zw[nb] = f32x16{};
+    }
+    load_set(I0{}, 0);
+    if (nstage > 1) load_set(I1{}, 1);
+    store_set(I0{}, 0, std::true_type{});
+    if (nstage > 2) load_set(I0{}, 2);
+    __syncthreads();
+    auto wstep = [&](auto P, int s) {
+      if (s + 1 < nstage) store_set(P, (s + 1) & 1, std::true_type{});
+      if (s + 3 < nstage) load_set(P, s + 3);
+      if (active) {
+        const int64_t left = n_end - (n_begin + (int64_t)s * kStage);
+        compute_wide(s & 1, left < kStage ? (int)left : kStage);
+      }
+      __syncthreads();
+    };
+    for (int s = 0; s < nstage; s += 2) {
+      wstep(I1{}, s);
+      if (s + 1 < nstage) wstep(I0{}, s + 1);
+    }
+  };
+
   // Stage s: store stage s+1 (register set P = (s+1) % 2) into its buffer, refill set P with stage
   // s+3, compute stage s, barrier.
   auto step = [&](auto P, auto EXACT, int s) {
-    if (s + 1 < nstage) store_set(P, (s + 1) & 1);
+    if (s + 1 < nstage) store_set(P, (s + 1) & 1, std::false_type{});
     if (s + 3 < nstage) load_set(P, s + 3);
     if (active) {
       const int64_t left = n_end - (n_begin + (int64_t)s * kStage);
@@ -570,7 +745,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     }
     load_set(I0{}, 0);
     if (nstage > 1) load_set(I1{}, 1);
-    store_set(I0{}, 0);
+    store_set(I0{}, 0, std::false_type{});
     if (nstage > 2) load_set(I0{}, 2);
     __syncthreads();
     for (int s = 0; s < nstage; s += 2) {
@@ -584,16 +759,67 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   bool exact = a.force_exact != 0;
   if constexpr (SYNTH) {
     float qss = 0.f;
+    if constexpr (kWide) {
 #pragma unroll
-    for (int lb = 0; lb < NLB; lb++) {
-      float ss = O::sumsq(qb[lb]);
-      ss += shfl_xor(ss, 16);
-      ss += shfl_xor(ss, 32);
-      qss = fmaxf(qss, ss);
+      for (int nb = 0; nb < NB; nb++) {
+        float ss = 0.f;
+#pragma unroll
+        for (int kh = 0; kh < 2; kh++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) ss += (float)qw[nb][kh][e] * (float)qw[nb][kh][e];
+        ss += shfl_xor(ss, 32);
+        qss = fmaxf(qss, ss);
+      }
+    } else {
+#pragma unroll
+      for (int lb = 0; lb < NLB; lb++) {
+        float ss = O::sumsq(qb[lb]);
+        ss += shfl_xor(ss, 16);
+        ss += shfl_xor(ss, 32);
+        qss = fmaxf(qss, ss);
+      }
     }
     if (!__all(sqrtf(qss) * kLog2e * 1.01f <= kFastBound) && lane == 0) atomicOr(fail_s, 1);
     __syncthreads();
     exact = exact || *fail_s != 0;
+  }
+  const int64_t pbase = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp;
+  if constexpr (kWide) {
+    if (!exact) {
+      run_chunk_wide();
+      bool ok = true;
+      if (active) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          const float l = lw[nb] + shfl_xor(lw[nb], 32);
+          ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
+#pragma unroll
+          for (int v = 0; v < 16; v++) ok = ok && fabsf(zw[nb][v]) <= 3.0e38f;
+        }
+      }
+      if (!__all(ok) && lane == 0) atomicOr(fail_s, 1);
+      __syncthreads();
+      if (*fail_s == 0) {
+        if (!active) return;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          const float l = lw[nb] + shfl_xor(lw[nb], 32);
+          const int row = lat0 + 32 * nb + (lane & 31);
+          if (h32 == 0 && row < a.Mp) {
+            a.part_l[pbase + row] = l;
+            a.part_m[pbase + row] = 0.f;
+          }
+#pragma unroll
+          for (int v = 0; v < 16; v++) {
+            const int r = lat0 + 32 * nb + row32(v, h32);
+            if (r < a.Mp) a.part_acc[(pbase + r) * D + (lane & 31)] = zw[nb][v];
+          }
+        }
+        return;
+      }
+      exact = true;
+    }
+    load_queries();
   }
   if (!exact) {
     run_chunk(std::false_type{});
@@ -620,7 +846,6 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 
   if (!active) return;
   // Partials of this chunk: l and m per latent, the P.V accumulator per latent and channel.
-  const int64_t pbase = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp;
 #pragma unroll
   for (int lb = 0; lb < NLB; lb++) {
     float l = lsum[lb];
@@ -680,11 +905,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     if (a.dbg_out && row < a.M) a.dbg_out[((int64_t)bh * a.M + row) * D + d] = res;
     // c*Q as hi (and, for bf16, lo = the rounding residual of hi).
     const float cq = res * (kLog2e * rsqrtf((float)D));
-    constexpr int QP = kQParts<T>;
-    T* qo = reinterpret_cast<T*>(a.out) + ((int64_t)bh * a.Mout + row) * QP * D + d;
+    T* qo = reinterpret_cast<T*>(a.out) + ((int64_t)bh * a.Mout + row) * kQRow<T> * D + d;
     const T hi = (T)cq;
     qo[0] = hi;
-    if constexpr (QP == 2) qo[D] = (T)(cq - to_f(hi));
+    if constexpr (sizeof(T) == 2) {
+      qo[D] = (T)(cq - to_f(hi));
+      reinterpret_cast<f16*>(qo + 2 * D)[0] = (f16)cq;
+    }
   } else {
     if (a.dbg_out && row < a.M) a.dbg_out[((int64_t)bh * a.M + row) * D + d] = res;
     reinterpret_cast<T*>(a.out)[((int64_t)bh * a.Mout + row) * D + d] = (T)res;
@@ -720,7 +947,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int bh = blockIdx.y;
-  const T* qsrc = reinterpret_cast<const T*>(a.Q) + (int64_t)bh * Mp * QP * D;
+  const T* qsrc = reinterpret_cast<const T*>(a.Q) + (int64_t)bh * Mp * kQRow<T> * D;
   const T* zsrc = reinterpret_cast<const T*>(a.Z) + (int64_t)bh * Mp * D;
 
   for (int q0 = 0; q0 < Mp * CPR; q0 += NT) {
@@ -728,10 +955,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     if (q < Mp * CPR) {
       const int row = q / CPR, part = q % CPR;
       *reinterpret_cast<Chunk*>(qs + row * RQ + part * CH) =
-          *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + part * CH);
+          *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<T> * D + part * CH);
       if constexpr (QP == 2)
         *reinterpret_cast<Chunk*>(qs + row * RQ + D + part * CH) =
-            *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * QP * D + D + part * CH);
+            *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<T> * D + D + part * CH);
       rowtile_store<T, D>(zs, Mp, row, part * CH, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * CH));
     }
   }
@@ -896,6 +1123,201 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Decode for bf16 runs with D = 32 (Eq. 8, second call). The workgroup keeps the fp16 routing
+// queries c*Q (A operand of the score MFMA, row-major) and Z (a RowTile: B operand of the P.V MFMA,
+// read along latents) in LDS. Each wave takes groups of 32 * TB tokens; per latent block of 32 the
+// scores of every token block come from 32x32x16 fp16 MFMAs (the keys converted to fp16 in
+// registers), land with one token per lane column and 16 latents per lane, and feed the bf16 P.V
+// MFMA directly. Zero-shift pass, per-token range check, and for a group that fails an exact pass:
+// two passes over the latents with running maxima, scores from bf16 keys and the hi/lo queries
+// read from the workspace.
+template <int NW, int TB>
+__global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
+  constexpr int D = 32;
+  constexpr int QHS = D + 8;  // fp16 query row stride in LDS (80 bytes: conflict-free row reads)
+  using ZT = RowTile<bf16, D>;
+  constexpr int NT = NW * 64;
+  constexpr int TG = 32 * TB;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;  // multiple of 32
+  f16* qh = reinterpret_cast<f16*>(smem);            // [Mp][QHS]
+  bf16* zs = reinterpret_cast<bf16*>(qh + Mp * QHS);  // RowTile of Mp rows
+  const int ZSTR = ZT::stride(Mp);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.y;
+  const bf16* qsrc = reinterpret_cast<const bf16*>(a.Q) + (int64_t)bh * Mp * kQRow<bf16> * D;
+  const bf16* zsrc = reinterpret_cast<const bf16*>(a.Z) + (int64_t)bh * Mp * D;
+
+  for (int q = tid; q < Mp * 4; q += NT) {
+    const int row = q >> 2, part = q & 3;
+    *reinterpret_cast<Chunk*>(qh + row * QHS + part * 8) =
+        *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<bf16> * D + 2 * D + part * 8);
+    rowtile_store<bf16, D>(zs, Mp, row, part * 8, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * 8));
+  }
+  __syncthreads();
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.K) + (int64_t)bh * a.N * D;
+  bf16* obase = reinterpret_cast<bf16*>(a.out) + (int64_t)bh * a.N * D;
+  const int nlb = Mp / 32;
+  const bool ragged = (a.M & 31) != 0;
+
+  for (int64_t base = t_begin + (int64_t)wave * TG; base < t_end; base += (int64_t)NW * TG) {
+    // Key operands (B of the score MFMA): lane l holds dims 16 kh + 8 h .. + 7 of token
+    // base + 32 tb + l % 32.
+    auto load_keys = [&](int tb, int kh) __attribute__((always_inline)) {
+      const int64_t tok = base + 32 * tb + col;
+      return tok < a.N ? *reinterpret_cast<const bf16x8*>(kbase + tok * D + 16 * kh + 8 * h) : bf16x8{};
+    };
+    f16x8 kf[TB][2];
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+      for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(load_keys(tb, kh));
+
+    f32x16 yacc[TB];
+    float lsum[TB], shift[TB];
+    auto clear = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) {
+        lsum[tb] = 0.f;
+        yacc[tb] = f32x16{};
+      }
+    };
+    // Latents past M do not enter the softmax.
+    auto mask = [&](int lb, f32x16 (&sc)[TB]) __attribute__((always_inline)) {
+      if (ragged && lb == nlb - 1) {
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          if (32 * lb + row32(v, h) >= a.M)
+#pragma unroll
+            for (int tb = 0; tb < TB; tb++) sc[tb][v] = -INFINITY;
+      }
+    };
+    auto scores_fast = [&](int lb, f32x16 (&sc)[TB]) __attribute__((always_inline)) {
+      const f16* qrow = qh + (32 * lb + col) * QHS + 8 * h;
+      const f16x8 qa0 = *reinterpret_cast<const f16x8*>(qrow);
+      const f16x8 qa1 = *reinterpret_cast<const f16x8*>(qrow + 16);
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) {
+        sc[tb] = mfma_32x32_f16(qa0, kf[tb][0], f32x16{});
+        sc[tb] = mfma_32x32_f16(qa1, kf[tb][1], sc[tb]);
+      }
+      __builtin_amdgcn_sched_barrier(kAllButMfma);
+      keep_live(qa0);
+      keep_live(qa1);
+      mask(lb, sc);
+    };
+    // Exact-pass scores: bf16 keys against the hi and lo query parts (four chained MFMAs).
+    bf16x8 kb[TB][2];
+    auto scores_exact = [&](int lb, f32x16 (&sc)[TB]) __attribute__((always_inline)) {
+      const bf16* qrow = qsrc + (int64_t)(32 * lb + col) * kQRow<bf16> * D + 8 * h;
+      const bf16x8 hi0 = *reinterpret_cast<const bf16x8*>(qrow);
+      const bf16x8 hi1 = *reinterpret_cast<const bf16x8*>(qrow + 16);
+      const bf16x8 lo0 = *reinterpret_cast<const bf16x8*>(qrow + D);
+      const bf16x8 lo1 = *reinterpret_cast<const bf16x8*>(qrow + D + 16);
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) {
+        sc[tb] = mfma_32x32(hi0, kb[tb][0], f32x16{});
+        sc[tb] = mfma_32x32(hi1, kb[tb][1], sc[tb]);
+        sc[tb] = mfma_32x32(lo0, kb[tb][0], sc[tb]);
+        sc[tb] = mfma_32x32(lo1, kb[tb][1], sc[tb]);
+      }
+      __builtin_amdgcn_sched_barrier(kAllButMfma);
+      keep_live(hi0);
+      keep_live(hi1);
+      keep_live(lo0);
+      keep_live(lo1);
+      mask(lb, sc);
+    };
+    // Probabilities (shifted by the token's maximum in the exact pass), their sums and P.V.
+    auto accumulate = [&](auto EXACT) __attribute__((always_inline)) {
+      for (int lb = 0; lb < nlb; lb++) {
+        const bf16x8 zb0 = load_rows32(zs, ZSTR, 32 * lb, 0, lane);
+        const bf16x8 zb1 = load_rows32(zs, ZSTR, 32 * lb + 16, 0, lane);
+        f32x16 sc[TB];
+        if constexpr (decltype(EXACT)::value)
+          scores_exact(lb, sc);
+        else
+          scores_fast(lb, sc);
+#pragma unroll
+        for (int tb = 0; tb < TB; tb++) {
+#pragma unroll
+          for (int v = 0; v < 16; v++) {
+            if constexpr (decltype(EXACT)::value)
+              sc[tb][v] = exp2_fast(sc[tb][v] - shift[tb]);
+            else
+              sc[tb][v] = exp2_fast(sc[tb][v]);
+          }
+          const bf16x8 p0 = pack32(sc[tb], 0), p1 = pack32(sc[tb], 1);
+          lsum[tb] = Ops<bf16, 32>::osum(p1, Ops<bf16, 32>::osum(p0, lsum[tb]));
+          yacc[tb] = mfma_32x32(p0, zb0, yacc[tb]);
+          yacc[tb] = mfma_32x32(p1, zb1, yacc[tb]);
+          __builtin_amdgcn_sched_barrier(kAllButMfma);
+          keep_live(p0);
+          keep_live(p1);
+        }
+        keep_live(zb0);
+        keep_live(zb1);
+      }
+    };
+
+    clear();
+    bool ok = a.force_exact == 0;
+    if (ok) accumulate(std::false_type{});
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++) {
+      const float l = lsum[tb] + shfl_xor(lsum[tb], 32);
+      ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
+#pragma unroll
+      for (int v = 0; v < 16; v++) ok = ok && fabsf(yacc[tb][v]) <= 3.0e38f;
+    }
+    if (!__all(ok)) {
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+        for (int kh = 0; kh < 2; kh++) kb[tb][kh] = load_keys(tb, kh);
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) shift[tb] = -INFINITY;
+      for (int lb = 0; lb < nlb; lb++) {
+        f32x16 sc[TB];
+        scores_exact(lb, sc);
+#pragma unroll
+        for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+          for (int v = 0; v < 16; v++) shift[tb] = fmaxf(shift[tb], sc[tb][v]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) {
+        shift[tb] = fmaxf(shift[tb], shfl_xor(shift[tb], 32));
+        if (shift[tb] == -INFINITY) shift[tb] = 0.f;
+      }
+      clear();
+      accumulate(std::true_type{});
+    }
+
+    // Y = yacc / l. Result slot v of lane l holds token row32(v, h) of its block and dim l % 32;
+    // the token's sum sits in lanes row32(v, h) and row32(v, h) + 32.
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++) {
+      const float inv = 1.0f / (lsum[tb] + shfl_xor(lsum[tb], 32));
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int r = row32(v, h);
+        const float iv = shfl(inv, r);
+        const int64_t tok = base + 32 * tb + r;
+        if (tok < t_end) obase[tok * D + col] = (bf16)(yacc[tb][v] * iv);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
@@ -985,13 +1407,35 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int nw, int gx, int gy, h
   return launch_decode_t<T, D, 8, 4>(a, gx, gy, st);
 }
 
+static size_t decode_wide_lds(int Mp) {
+  return (size_t)Mp * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16);
+}
+
+template <int NW, int TB>
+static hipError_t launch_decode_wide_t(const DecodeArgs& a, int gx, int gy, hipStream_t st) {
+  const size_t lds = decode_wide_lds(a.Mp);
+  hipError_t e = allow_lds(decode_wide_kernel<NW, TB>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_wide_kernel<NW, TB>), dim3(gx, gy), dim3(NW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int gx, int gy, hipStream_t st) {
-  if (dtype == 1) return D == 32 ? launch_decode_d<bf16, 32>(a, nw, gx, gy, st) : launch_decode_d<bf16, 16>(a, nw, gx, gy, st);
+  if (dtype == 1 && D == 32) {
+    // Two 32-token blocks per wave group need about 160 registers: at most 12 waves per CU.
+    switch (nw) {
+      case 8: return launch_decode_wide_t<8, 2>(a, gx, gy, st);
+      case 12:
+      case 16: return launch_decode_wide_t<12, 2>(a, gx, gy, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (dtype == 1) return launch_decode_d<bf16, 16>(a, nw, gx, gy, st);
   return D == 32 ? launch_decode_d<float, 32>(a, nw, gx, gy, st) : launch_decode_d<float, 16>(a, nw, gx, gy, st);
 }
 
 size_t decode_lds_bytes(int dtype, int D, int Mp, int nw) {
-  if (dtype == 1) return D == 32 ? decode_lds_t<bf16, 32>(Mp, nw) : decode_lds_t<bf16, 16>(Mp, nw);
+  if (dtype == 1) return D == 32 ? decode_wide_lds(Mp) : decode_lds_t<bf16, 16>(Mp, nw);
   return D == 32 ? decode_lds_t<float, 32>(Mp, nw) : decode_lds_t<float, 16>(Mp, nw);
 }
 
