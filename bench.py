@@ -7,6 +7,7 @@ the achieved TFLOP/s (12 N M D flops per head), per-kernel event timings, the ro
 the dominant kernel and the float64 CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+                      [--cpu-sample-heads H] [--copy-calibration]
 """
 import argparse
 import json
@@ -25,6 +26,32 @@ PEAK_HBM_GBS = 8000.0
 PEAK_EXP_PER_S = 256 * 2.4e9 * 32
 
 KERNELS = ["synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"]
+KERNEL_SRC = os.path.join(ROOT, "rank_latent_routing_amd", "csrc", "kernels.hip")
+PROFILE = os.path.join(ROOT, "profiles", "flarepp_mixer_1M_tokens.md")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by the factors a 256 MiB device copy measured in the same
+    runs. None when the summary is missing or was taken on a different kernel source."""
+    try:
+        lines = open(PROFILE).read().splitlines()
+    except OSError:
+        return None
+    rec = None
+    for ln in lines:
+        if ln.startswith("traffic-json: "):
+            rec = json.loads(ln[len("traffic-json: "):])
+    if not rec or rec.get("kernels_hip_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("per_launch_bytes", {}).get(kernel)
+    return None if k is None else float(k)
 
 
 def _parse():
@@ -34,7 +61,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=524288)
+    ap.add_argument("--cpu-sample-heads", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (a reference "
                          "dispatch for scaling the HBM byte counters of a profile)")
@@ -48,9 +75,24 @@ def kernel_flops(name, w):
     return per if name in ("synthesis_partial", "encode_partial", "decode") else 0.0
 
 
-def cpu_baseline(w, ntok):
-    """The float64 oracle on one head of the same workload, first `ntok` tokens."""
-    import numpy as np
+def kernel_bytes(name, w):
+    """Algorithmic HBM bytes of one launch: the token tensors it must read or write once (K, V, S,
+    out at the input width) and, for decode, the latent tensors c*Q and Z it reads; the fp32 chunk
+    partials of the split-N kernels (under 4% of their bytes here) are not counted."""
+    es = 2 if w.dtype == "bf16" else 4
+    tok = float(w.N) * w.D * w.B * w.H * es
+    lat = float(w.M) * w.D * w.B * w.H
+    if name == "synthesis_partial":
+        return tok
+    if name == "encode_partial":
+        return 2 * tok
+    if name == "decode":
+        return 2 * tok + lat * (es * 3 + es)
+    return 0.0
+
+
+def cpu_baseline(w, heads):
+    """The float64 oracle on the first `heads` heads (b = 0) of the same workload, all N tokens."""
     import oracle
     from workloads import to_float64
     try:
@@ -58,16 +100,15 @@ def cpu_baseline(w, ntok):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    n = min(ntok, w.N)
-    args = [to_float64(w.K[0, 0, :n], w.dtype), to_float64(w.V[0, 0, :n], w.dtype),
-            to_float64(w.S[0, 0, :n], w.dtype), to_float64(w.Qseed[0], w.dtype), to_float64(w.Qf[0], w.dtype),
-            float(w.g[0])]
+    heads = max(1, min(heads, w.H))
     t0 = time.perf_counter()
-    oracle.mix_head(*args, block=65536)
+    for h in range(heads):
+        oracle.mix_head(to_float64(w.K[0, h], w.dtype), to_float64(w.V[0, h], w.dtype), to_float64(w.S[0, h], w.dtype),
+                        to_float64(w.Qseed[h], w.dtype), to_float64(w.Qf[h], w.dtype), float(w.g[h]), block=65536)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"one head (b=0, h=0), first {n} of {w.N} tokens, M={w.M}, D={w.D}, float64 numpy; "
-                      f"{dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded"}
+    return {"value": heads * w.N / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (b, h) slices (b=0, h<{heads}), all {w.N} tokens, M={w.M}, D={w.D}, "
+                      f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded"}
 
 
 def main():
@@ -141,9 +182,12 @@ def main():
     dom = max(KERNELS, key=lambda k: kern[k]["ms_avg"])
     dom_ms = kern[dom]["ms_avg"]
     achieved = kernel_flops(dom, w) / (dom_ms * 1e-3) * 1e-12
+    traffic = profiled_traffic(dom) if args.config == 5 else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel_ms": round(dom_ms, 4), "flops_per_launch": kernel_flops(dom, w),
+                "algorithmic_bytes_per_launch": kernel_bytes(dom, w),
+                "hbm_gbs": round(kernel_bytes(dom, w) / (dom_ms * 1e-3) * 1e-9, 1),
                 "exp_frac": round((w.N * w.M * w.B * w.H) / (dom_ms * 1e-3) / PEAK_EXP_PER_S, 4)}
 
     res = {
@@ -169,7 +213,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
     print(json.dumps(res), flush=True)
 
 
