@@ -44,7 +44,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Plan {
   int BH = 0;
   int Mp16 = 0, Mp32 = 0;
-  int part_plan = 0;  // kernel variant: 0 (16 latents/wave, 4 waves), 1 (32, 4), 2 (32, 8)
+  int part_plan = 0;  // kernel variant, see flarepp::partial_plan_shape
   int nlg = 1;        // latent groups (workgroups per chunk)
   int64_t chunk = 0;
   int nchunk = 0;
@@ -61,18 +61,22 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.Mp16 = (M + 15) / 16 * 16;
   p.Mp32 = (M + 31) / 32 * 32;
   // Partial-kernel variant: latents per wave x waves per workgroup, and latent groups per chunk.
-  int lpw, nw;
-  if (p.Mp16 <= 64) { p.part_plan = 0; lpw = 16; nw = 4; }
-  else if (p.Mp16 <= 128) { p.part_plan = 1; lpw = 32; nw = 4; }
-  else { p.part_plan = 2; lpw = 32; nw = 8; }
-  p.nlg = (int)ceil_div(p.Mp16, (int64_t)lpw * nw);
-  // About two rounds of resident workgroups over 256 CUs (8-wave groups: 2 per CU; 4-wave: 4).
-  const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", nw == 8 ? 1024 : 2048);
+  if (p.Mp16 <= 64) p.part_plan = 0;
+  else if (p.Mp16 <= 128) p.part_plan = 1;
+  else if (p.Mp16 <= 256 || dtype == FLAREPP_FP32) p.part_plan = 2;
+  else p.part_plan = 3;  // bf16, M > 256: one 16-wave workgroup per chunk, 256-token stages
+  const int plan_env = env_int("FLAREPP_PARTIAL_PLAN", -1);
+  if (plan_env >= 0 && plan_env <= 3 && !(plan_env == 3 && dtype == FLAREPP_FP32)) p.part_plan = plan_env;
+  const flarepp::PartialShape ps = flarepp::partial_plan_shape(p.part_plan);
+  p.nlg = (int)ceil_div(p.Mp16, (int64_t)ps.lpw * ps.nw);
+  // About two rounds of resident workgroups over 256 CUs (16-wave groups: 1 per CU; 8-wave: 2;
+  // 4-wave: 4).
+  const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", ps.nw == 16 ? 512 : ps.nw == 8 ? 1024 : 2048);
   int64_t nchunk = ceil_div(target, (int64_t)p.BH * p.nlg);
   nchunk = nchunk < 1 ? 1 : nchunk;
-  const int64_t max_chunks = ceil_div(N, kStage);
+  const int64_t max_chunks = ceil_div(N, (int64_t)ps.stage);
   if (nchunk > max_chunks) nchunk = max_chunks;
-  p.chunk = ceil_div(ceil_div(N, nchunk), kStage) * kStage;
+  p.chunk = ceil_div(ceil_div(N, nchunk), (int64_t)ps.stage) * ps.stage;
   p.nchunk = (int)ceil_div(N, p.chunk);
   // With several latent groups, grid x holds 8 chunks per XCD slot row (see partial_kernel).
   p.part_gx = p.nlg == 1 ? p.nchunk : (int)(ceil_div(p.nchunk, 8) * 8 * p.nlg);

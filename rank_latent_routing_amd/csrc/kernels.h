@@ -7,8 +7,20 @@
 
 namespace flarepp {
 
-// Tokens per LDS stage of the split-N partial kernels.
+// Tokens per LDS stage of the split-N partial kernels (plans 0-2; plan 3 uses 2 * kStage).
 constexpr int kStage = 128;
+// Partial-kernel plans: {latents per wave, waves per workgroup, tokens per stage}.
+struct PartialShape {
+  int lpw, nw, stage;
+};
+inline PartialShape partial_plan_shape(int plan) {
+  switch (plan) {
+    case 0: return {16, 4, kStage};
+    case 1: return {32, 4, kStage};
+    case 2: return {32, 8, kStage};
+    default: return {32, 16, 2 * kStage};
+  }
+}
 // Waves per decode workgroup: 8, or 12 when the latent tensors in LDS allow one workgroup per CU
 // (16 is also built). Tokens per wave group: bf16 with D = 32 always 64 (two blocks of 32);
 // otherwise 16 * TB with TB = 4 (8 or 12 waves) or 2 (16 waves).
@@ -29,7 +41,7 @@ struct PartialArgs {
   int Mq;          // rows per query block (rows >= Mq read as zero)
   int Mp;          // latent rows in the partial buffers (M rounded up to 16)
   int64_t N;       // tokens
-  int64_t chunk;   // tokens per chunk, a multiple of kStage
+  int64_t chunk;   // tokens per chunk, a multiple of the plan's stage
   int nchunk;      // chunks per (b, h)
   int nlg;         // latent groups per chunk (workgroups sharing one chunk's tokens)
   int force_exact; // skip the zero-shift pass (test hook)

@@ -397,8 +397,9 @@ __device__ __forceinline__ int perm_row(int r, int half) { return 8 * (r >> 2) +
 //
 // Grid: x enumerates (chunk, latent group) so that the latent groups of one chunk land on the same
 // XCD (workgroups are dealt to the 8 XCDs round-robin by x) and share its L2; y = b * H + h.
-template <typename T, int D, int LPW, int NW, bool SYNTH>
+template <typename T, int D, int LPW, int NW, bool SYNTH, int STG>
 __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
+  constexpr int kStage = STG;  // tokens per LDS stage
   using O = Ops<T, D>;
   using Slice = typename O::Slice;
   using Oct = typename O::Oct;
@@ -697,6 +698,82 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       }
     }
   };
+  // Full stages of the wide zero-shift pass, software-pipelined over the 32-token sub-tiles. Step j
+  // issues, in this order (each piece fenced so the scheduler keeps it):
+  //   S1(j+1) | exp 0-3 (j) | S2(j+1) | exp 4-7 | pack/sum slots 0-7 | PV1(j) | exp 8-15 |
+  //   pack/sum slots 8-15 | PV2(j)
+  // where S1, S2 are the two fp16 score MFMAs of the next sub-tile and PV1, PV2 the bf16 P.V MFMAs
+  // of this one, so every MFMA runs under vector work of the same wave. LDS operands are read one
+  // step ahead. Sub-tiles go in pairs so no register copies are needed between steps.
+  auto compute_wide_full = [&](int buf) {
+    if constexpr (kWide && NB == 1) {
+      constexpr int NS = kStage / 32;
+      static_assert(NS % 2 == 0, "pairs of sub-tiles");
+      const bf16* kt = reinterpret_cast<const bf16*>(ks) + buf * kStage * RS + (lane & 31) * RS + 8 * h32;
+      const bf16* vtt = reinterpret_cast<const bf16*>(vt) + buf * VE;
+      auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+      struct KOp { f16x8 a, b; };
+      struct VOp { bf16x8 a, b; };
+      auto load_k = [&](int st) __attribute__((always_inline)) {
+        return KOp{*reinterpret_cast<const f16x8*>(kt + 32 * st * RS), *reinterpret_cast<const f16x8*>(kt + 32 * st * RS + 16)};
+      };
+      auto load_v = [&](int st) __attribute__((always_inline)) {
+        return VOp{load_rows32(vtt, VSTR, 32 * st, 0, lane), load_rows32(vtt, VSTR, 32 * st + 16, 0, lane)};
+      };
+      auto exps = [&](f32x16& x, int v0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) x[v0 + v] = exp2_fast(x[v0 + v]);
+      };
+      // Step: scores of the next sub-tile into `nx` (from `kn`), probabilities and P.V of `cu`.
+      auto step = [&](f32x16& cu, const VOp& vc, f32x16& nx, const KOp& kn, bool has_next) __attribute__((always_inline)) {
+        if (has_next) nx = mfma_32x32_f16(kn.a, qw[0][0], f32x16{});
+        fence();
+        exps(cu, 0);
+        fence();
+        if (has_next) nx = mfma_32x32_f16(kn.b, qw[0][1], nx);
+        fence();
+        keep_live(kn.a);
+        keep_live(kn.b);
+        exps(cu, 4);
+        const bf16x8 p0 = pack32(cu, 0);
+        lw[0] = O::osum(p0, lw[0]);
+        fence();
+        zw[0] = mfma_32x32(p0, vc.a, zw[0]);
+        fence();
+        keep_live(p0);
+        keep_live(vc.a);
+        exps(cu, 8);
+        exps(cu, 12);
+        const bf16x8 p1 = pack32(cu, 1);
+        lw[0] = O::osum(p1, lw[0]);
+        fence();
+        zw[0] = mfma_32x32(p1, vc.b, zw[0]);
+        fence();
+        keep_live(p1);
+        keep_live(vc.b);
+      };
+      // Prologue: scores of sub-tile 0 and the keys of sub-tile 1. Step st reads the values of
+      // sub-tile st at its start and the keys of sub-tile st+2 for the next step.
+      f32x16 sc[2];
+      KOp kb[2];
+      {
+        const KOp k0 = load_k(0);
+        sc[0] = mfma_32x32_f16(k0.a, qw[0][0], f32x16{});
+        sc[0] = mfma_32x32_f16(k0.b, qw[0][1], sc[0]);
+        fence();
+        keep_live(k0.a);
+        keep_live(k0.b);
+      }
+      kb[1] = load_k(1);
+#pragma unroll
+      for (int st = 0; st < NS; st++) {
+        const VOp vc = load_v(st);
+        if (st + 2 < NS) kb[st & 1] = load_k(st + 2);
+        step(sc[st & 1], vc, sc[(st + 1) & 1], kb[(st + 1) & 1], st + 1 < NS);
+      }
+    }
+  };
+
   auto run_chunk_wide = [&]() {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) {
@@ -713,7 +790,10 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       if (s + 3 < nstage) load_set(P, s + 3);
       if (active) {
         const int64_t left = n_end - (n_begin + (int64_t)s * kStage);
-        compute_wide(s & 1, left < kStage ? (int)left : kStage);
+        if (NB == 1 && left >= kStage)
+          compute_wide_full(s & 1);
+        else
+          compute_wide(s & 1, left < kStage ? (int)left : kStage);
       }
       __syncthreads();
     };
@@ -1330,27 +1410,34 @@ static hipError_t allow_lds(F* fn, size_t lds) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int STG>
 static size_t partial_lds_t() {
   constexpr int CH = 16 / sizeof(T);
-  return (size_t)(2 * kStage * (D + CH) + 2 * RowTile<T, D>::elems(kStage)) * sizeof(T) + 16;
+  return (size_t)(2 * STG * (D + CH) + 2 * RowTile<T, D>::elems(STG)) * sizeof(T) + 16;
 }
 
-template <typename T, int D, int LPW, int NW, bool SYNTH>
+template <typename T, int D, int LPW, int NW, bool SYNTH, int STG>
 static hipError_t launch_partial_t(const PartialArgs& a, int grid_x, int grid_y, hipStream_t st) {
-  const size_t lds = partial_lds_t<T, D, NW>();
-  hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH>, lds);
+  const size_t lds = partial_lds_t<T, D, STG>();
+  hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH, STG>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH, STG>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
+// Partial-kernel variants (latents per wave, waves per workgroup, tokens per stage); see
+// partial_plan_shape. The 16-wave variant is built for bf16 only (fp32 operands need more than the
+// 128 registers per lane that 16 waves leave).
 template <typename T, int D, bool SYNTH>
 static hipError_t launch_partial_d(const PartialArgs& a, int plan, int gx, int gy, hipStream_t st) {
   switch (plan) {
-    case 0: return launch_partial_t<T, D, 16, 4, SYNTH>(a, gx, gy, st);
-    case 1: return launch_partial_t<T, D, 32, 4, SYNTH>(a, gx, gy, st);
-    default: return launch_partial_t<T, D, 32, 8, SYNTH>(a, gx, gy, st);
+    case 0: return launch_partial_t<T, D, 16, 4, SYNTH, 128>(a, gx, gy, st);
+    case 1: return launch_partial_t<T, D, 32, 4, SYNTH, 128>(a, gx, gy, st);
+    case 2: return launch_partial_t<T, D, 32, 8, SYNTH, 128>(a, gx, gy, st);
+    case 3:
+      if constexpr (sizeof(T) == 2) return launch_partial_t<T, D, 32, 16, SYNTH, 256>(a, gx, gy, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -1440,13 +1527,13 @@ size_t decode_lds_bytes(int dtype, int D, int Mp, int nw) {
 }
 
 size_t partial_lds_bytes(int dtype, int D, int plan) {
-  const int nw = plan >= 2 ? 8 : 4;
+  const bool big = plan == 3;
   if (dtype == 1) {
-    if (D == 32) return nw == 8 ? partial_lds_t<bf16, 32, 8>() : partial_lds_t<bf16, 32, 4>();
-    return nw == 8 ? partial_lds_t<bf16, 16, 8>() : partial_lds_t<bf16, 16, 4>();
+    if (D == 32) return big ? partial_lds_t<bf16, 32, 256>() : partial_lds_t<bf16, 32, 128>();
+    return big ? partial_lds_t<bf16, 16, 256>() : partial_lds_t<bf16, 16, 128>();
   }
-  if (D == 32) return nw == 8 ? partial_lds_t<float, 32, 8>() : partial_lds_t<float, 32, 4>();
-  return nw == 8 ? partial_lds_t<float, 16, 8>() : partial_lds_t<float, 16, 4>();
+  if (D == 32) return big ? partial_lds_t<float, 32, 256>() : partial_lds_t<float, 32, 128>();
+  return big ? partial_lds_t<float, 16, 256>() : partial_lds_t<float, 16, 128>();
 }
 
 }  // namespace flarepp
