@@ -86,7 +86,7 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   const int nw_env = env_int("FLAREPP_DECODE_WAVES", 0);
   if (nw_env == 8 || nw_env == 12 || nw_env == 16) p.dec_nw = nw_env;
   if (dtype == FLAREPP_FP32 && p.dec_nw == 12) p.dec_nw = 16;  // no 12-wave fp32 variant
-  if (dtype == FLAREPP_BF16 && D == 32 && p.dec_nw == 16) p.dec_nw = 12;  // no 16-wave variant
+  if (dtype == FLAREPP_BF16 && D == 32 && nw_env == 0) p.dec_nw = 12;  // pipelined variant
   const int64_t group = flarepp::decode_group_tokens(dtype, D, p.dec_nw);
   const int64_t dec_target = env_int("FLAREPP_DECODE_WORKGROUPS", p.dec_nw == 8 ? 512 : 256);
   int64_t gx = ceil_div(dec_target, p.BH);

@@ -22,12 +22,13 @@ inline PartialShape partial_plan_shape(int plan) {
   }
 }
 // Waves per decode workgroup: 8, or 12 when the latent tensors in LDS allow one workgroup per CU
-// (16 is also built). Tokens per wave group: bf16 with D = 32 always 64 (two blocks of 32);
-// otherwise 16 * TB with TB = 4 (8 or 12 waves) or 2 (16 waves).
+// (16 is also built for the other cases). Tokens per wave group: bf16 with D = 32, 32 * TB with
+// TB = 2 (8 waves) or 1 (12 waves, the default); otherwise 16 * TB with TB = 4 (8, 12 waves) or 2
+// (16 waves).
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeWavesWide = 12;
 inline int decode_group_tokens(int dtype, int D, int nw) {
-  if (dtype == 1 && D == 32) return 64;
+  if (dtype == 1 && D == 32) return nw == 8 ? 64 : 32;  // 12 waves: one 32-token block per group
   return nw == 16 ? 32 : 64;
 }
 

@@ -1208,8 +1208,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 // queries c*Q (A operand of the score MFMA, row-major) and Z (a RowTile: B operand of the P.V MFMA,
 // read along latents) in LDS. Each wave takes groups of 32 * TB tokens; per latent block of 32 the
 // scores of every token block come from 32x32x16 fp16 MFMAs (the keys converted to fp16 in
-// registers), land with one token per lane column and 16 latents per lane, and feed the bf16 P.V
-// MFMA directly. Zero-shift pass, per-token range check, and for a group that fails an exact pass:
+// registers) and land with one token per lane column and 16 latents per lane: exactly the B operand
+// of the bf16 MFMA Z^T P, which yields Y^T with one token per lane column. Zero-shift pass, per-token range check, and for a group that fails an exact pass:
 // two passes over the latents with running maxima, scores from bf16 keys and the hi/lo queries
 // read from the workspace.
 template <int NW, int TB>
@@ -1222,8 +1222,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;  // multiple of 32
-  f16* qh = reinterpret_cast<f16*>(smem);            // [Mp][QHS]
-  bf16* zs = reinterpret_cast<bf16*>(qh + Mp * QHS);  // RowTile of Mp rows
+  f16* qh = reinterpret_cast<f16*>(smem);                  // [Mp + 32][QHS]: a zero block at the end
+  bf16* zs = reinterpret_cast<bf16*>(qh + (Mp + 32) * QHS);  // RowTile of Mp rows
   const int ZSTR = ZT::stride(Mp);
 
   const int tid = threadIdx.x;
@@ -1239,6 +1239,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
         *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<bf16> * D + 2 * D + part * 8);
     rowtile_store<bf16, D>(zs, Mp, row, part * 8, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * 8));
   }
+  for (int q = tid; q < 32 * 4; q += NT) *reinterpret_cast<Chunk*>(qh + (Mp + (q >> 2)) * QHS + (q & 3) * 8) = Chunk{0u, 0u, 0u, 0u};
   __syncthreads();
 
   const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
@@ -1248,18 +1249,32 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
   const int nlb = Mp / 32;
   const bool ragged = (a.M & 31) != 0;
 
-  for (int64_t base = t_begin + (int64_t)wave * TG; base < t_end; base += (int64_t)NW * TG) {
-    // Key operands (B of the score MFMA): lane l holds dims 16 kh + 8 h .. + 7 of token
-    // base + 32 tb + l % 32.
-    auto load_keys = [&](int tb, int kh) __attribute__((always_inline)) {
-      const int64_t tok = base + 32 * tb + col;
-      return tok < a.N ? *reinterpret_cast<const bf16x8*>(kbase + tok * D + 16 * kh + 8 * h) : bf16x8{};
-    };
+  // Key operands (B of the score MFMA): lane l holds dims 16 kh + 8 h .. + 7 of token
+  // base + 32 tb + l % 32. The next wave group's keys are loaded while this one is computed.
+  auto load_keys_at = [&](int64_t base, int tb, int kh) __attribute__((always_inline)) {
+    const int64_t tok = base + 32 * tb + col;
+    return tok < t_end ? *reinterpret_cast<const bf16x8*>(kbase + tok * D + 16 * kh + 8 * h) : bf16x8{};
+  };
+  const int64_t gstride = (int64_t)NW * TG;
+  bf16x8 knext[TB][2];
+#pragma unroll
+  for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+    for (int kh = 0; kh < 2; kh++) knext[tb][kh] = load_keys_at(t_begin + (int64_t)wave * TG, tb, kh);
+
+  for (int64_t base = t_begin + (int64_t)wave * TG; base < t_end; base += gstride) {
+    auto load_keys = [&](int tb, int kh) __attribute__((always_inline)) { return load_keys_at(base, tb, kh); };
     f16x8 kf[TB][2];
 #pragma unroll
     for (int tb = 0; tb < TB; tb++)
 #pragma unroll
-      for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(load_keys(tb, kh));
+      for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(knext[tb][kh]);
+    if (base + gstride < t_end) {
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+        for (int kh = 0; kh < 2; kh++) knext[tb][kh] = load_keys_at(base + gstride, tb, kh);
+    }
 
     f32x16 yacc[TB];
     float lsum[TB], shift[TB];
@@ -1337,8 +1352,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
           }
           const bf16x8 p0 = pack32(sc[tb], 0), p1 = pack32(sc[tb], 1);
           lsum[tb] = Ops<bf16, 32>::osum(p1, Ops<bf16, 32>::osum(p0, lsum[tb]));
-          yacc[tb] = mfma_32x32(p0, zb0, yacc[tb]);
-          yacc[tb] = mfma_32x32(p1, zb1, yacc[tb]);
+          yacc[tb] = mfma_32x32(zb0, p0, yacc[tb]);
+          yacc[tb] = mfma_32x32(zb1, p1, yacc[tb]);
           __builtin_amdgcn_sched_barrier(kAllButMfma);
           keep_live(p0);
           keep_live(p1);
@@ -1348,9 +1363,94 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
       }
     };
 
+    // Zero-shift pass for one 32-token block, software-pipelined over the latent blocks as in the
+    // partial kernels: step lb issues the score MFMAs of block lb+1 (the zero block past Mp after
+    // the last) between fenced groups of block lb's exponentials and pack/sum work, then its P.V.
+    auto accumulate_fast_pipelined = [&]() __attribute__((always_inline)) {
+      if constexpr (TB == 1) {
+        auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+        struct QOp { f16x8 a, b; };
+        auto load_q = [&](int lb) __attribute__((always_inline)) {
+          const f16* qrow = qh + (32 * lb + col) * QHS + 8 * h;
+          return QOp{*reinterpret_cast<const f16x8*>(qrow), *reinterpret_cast<const f16x8*>(qrow + 16)};
+        };
+        auto exps = [&](f32x16& x, int v0) __attribute__((always_inline)) {
+#pragma unroll
+          for (int v = 0; v < 4; v++) x[v0 + v] = exp2_fast(x[v0 + v]);
+        };
+        // qn holds the query operands of block lb+1 on entry and of block lb+2 on exit. LAST: the
+        // final latent block, whose rows past M are masked when M is not a multiple of 32 (kept
+        // out of the loop so the mask costs nothing per block).
+        auto step = [&](auto LAST, int lb, f32x16& cu, f32x16& nx, QOp& qn) __attribute__((always_inline)) {
+          const bf16x8 zb0 = load_rows32(zs, ZSTR, 32 * lb, 0, lane);
+          const bf16x8 zb1 = load_rows32(zs, ZSTR, 32 * lb + 16, 0, lane);
+          if constexpr (decltype(LAST)::value) {
+            if (ragged) {
+#pragma unroll
+              for (int v = 0; v < 16; v++)
+                if (32 * lb + row32(v, h) >= a.M) cu[v] = -INFINITY;
+            }
+          }
+          nx = mfma_32x32_f16(qn.a, kf[0][0], f32x16{});
+          fence();
+          exps(cu, 0);
+          fence();
+          nx = mfma_32x32_f16(qn.b, kf[0][1], nx);
+          fence();
+          keep_live(qn.a);
+          keep_live(qn.b);
+          qn = load_q(lb + 2 <= nlb ? lb + 2 : nlb);
+          exps(cu, 4);
+          const bf16x8 p0 = pack32(cu, 0);
+          lsum[0] = Ops<bf16, 32>::osum(p0, lsum[0]);
+          fence();
+          yacc[0] = mfma_32x32(zb0, p0, yacc[0]);
+          fence();
+          keep_live(p0);
+          keep_live(zb0);
+          exps(cu, 8);
+          exps(cu, 12);
+          const bf16x8 p1 = pack32(cu, 1);
+          lsum[0] = Ops<bf16, 32>::osum(p1, lsum[0]);
+          fence();
+          yacc[0] = mfma_32x32(zb1, p1, yacc[0]);
+          fence();
+          keep_live(p1);
+          keep_live(zb1);
+        };
+        f32x16 sa, sb;
+        {
+          const QOp q0 = load_q(0);
+          sa = mfma_32x32_f16(q0.a, kf[0][0], f32x16{});
+          sa = mfma_32x32_f16(q0.b, kf[0][1], sa);
+          fence();
+          keep_live(q0.a);
+          keep_live(q0.b);
+        }
+        QOp qn = load_q(1);
+        int lb = 0;
+        for (; lb + 2 < nlb; lb += 2) {
+          step(std::false_type{}, lb, sa, sb, qn);
+          step(std::false_type{}, lb + 1, sb, sa, qn);
+        }
+        if (lb + 2 == nlb) {
+          step(std::false_type{}, lb, sa, sb, qn);
+          step(std::true_type{}, lb + 1, sb, sa, qn);
+        } else {
+          step(std::true_type{}, lb, sa, sb, qn);
+        }
+      }
+    };
+
     clear();
     bool ok = a.force_exact == 0;
-    if (ok) accumulate(std::false_type{});
+    if (ok) {
+      if constexpr (TB == 1)
+        accumulate_fast_pipelined();
+      else
+        accumulate(std::false_type{});
+    }
+
 #pragma unroll
     for (int tb = 0; tb < TB; tb++) {
       const float l = lsum[tb] + shfl_xor(lsum[tb], 32);
@@ -1382,17 +1482,21 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
       accumulate(std::true_type{});
     }
 
-    // Y = yacc / l. Result slot v of lane l holds token row32(v, h) of its block and dim l % 32;
-    // the token's sum sits in lanes row32(v, h) and row32(v, h) + 32.
+    // Y = yacc / l. The P.V product is computed transposed (Z^T P), so result slot v of lane l
+    // holds dim row32(v, h) of token l % 32 of its block: four runs of four consecutive dims, each
+    // stored as one 8-byte write, and the token's sum is the lane's own (plus its partner l ^ 32).
 #pragma unroll
     for (int tb = 0; tb < TB; tb++) {
       const float inv = 1.0f / (lsum[tb] + shfl_xor(lsum[tb], 32));
+      const int64_t tok = base + 32 * tb + col;
+      if (tok < t_end) {
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int r = row32(v, h);
-        const float iv = shfl(inv, r);
-        const int64_t tok = base + 32 * tb + r;
-        if (tok < t_end) obase[tok * D + col] = (bf16)(yacc[tb][v] * iv);
+        for (int gq = 0; gq < 4; gq++) {
+          bf16x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; i++) o[i] = (bf16)(yacc[tb][4 * gq + i] * inv);
+          *reinterpret_cast<bf16x4*>(obase + tok * D + row32(4 * gq, h)) = o;
+        }
       }
     }
   }
@@ -1495,7 +1599,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int nw, int gx, int gy, h
 }
 
 static size_t decode_wide_lds(int Mp) {
-  return (size_t)Mp * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16);
+  return (size_t)(Mp + 32) * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16);
 }
 
 template <int NW, int TB>
@@ -1509,11 +1613,12 @@ static hipError_t launch_decode_wide_t(const DecodeArgs& a, int gx, int gy, hipS
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int gx, int gy, hipStream_t st) {
   if (dtype == 1 && D == 32) {
-    // Two 32-token blocks per wave group need about 160 registers: at most 12 waves per CU.
+    // 12 waves: one 32-token block per wave group with the pipelined zero-shift pass (about 140
+    // registers); 8 waves: two blocks per group, not pipelined (about 180 registers).
     switch (nw) {
       case 8: return launch_decode_wide_t<8, 2>(a, gx, gy, st);
-      case 12:
-      case 16: return launch_decode_wide_t<12, 2>(a, gx, gy, st);
+      case 12: return launch_decode_wide_t<12, 1>(a, gx, gy, st);
+      case 16: return launch_decode_wide_t<16, 1>(a, gx, gy, st);
       default: return hipErrorInvalidValue;
     }
   }
