@@ -74,7 +74,9 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", ps.nw == 16 ? 512 : ps.nw == 8 ? 1024 : 2048);
   int64_t nchunk = ceil_div(target, (int64_t)p.BH * p.nlg);
   nchunk = nchunk < 1 ? 1 : nchunk;
-  const int64_t max_chunks = ceil_div(N, (int64_t)ps.stage);
+  // At most 2048 chunks: the merge keeps a row block's chunk weights in LDS (16 rows x 2048 x 4 B).
+  int64_t max_chunks = ceil_div(N, (int64_t)ps.stage);
+  if (max_chunks > 2048) max_chunks = 2048;
   if (nchunk > max_chunks) nchunk = max_chunks;
   p.chunk = ceil_div(ceil_div(N, nchunk), (int64_t)ps.stage) * ps.stage;
   p.nchunk = (int)ceil_div(N, p.chunk);
@@ -86,7 +88,7 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   const int nw_env = env_int("FLAREPP_DECODE_WAVES", 0);
   if (nw_env == 8 || nw_env == 12 || nw_env == 16) p.dec_nw = nw_env;
   if (dtype == FLAREPP_FP32 && p.dec_nw == 12) p.dec_nw = 16;  // no 12-wave fp32 variant
-  if (dtype == FLAREPP_BF16 && D == 32 && nw_env == 0) p.dec_nw = 12;  // pipelined variant
+  if (dtype == FLAREPP_BF16 && D == 32 && nw_env == 0) p.dec_nw = 16;  // pipelined 16-wave variant
   const int64_t group = flarepp::decode_group_tokens(dtype, D, p.dec_nw);
   const int64_t dec_target = env_int("FLAREPP_DECODE_WORKGROUPS", p.dec_nw == 8 ? 512 : 256);
   int64_t gx = ceil_div(dec_target, p.BH);

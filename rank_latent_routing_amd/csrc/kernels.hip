@@ -954,25 +954,51 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 // (latent, channel); rows in [M, Mout) are written as zeros.
 template <typename T, int D, bool GATE>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  // Block: 256 / D latent rows x D channels. The chunk maxima and the normalizer of a row are
+  // reduced across its D lanes (chunks strided over the lanes); the chunk weights 2^(m_c - m) go
+  // through LDS to the accumulator pass, which streams the chunks with several loads in flight.
+  constexpr int RPB = 256 / D;
+  extern __shared__ float wsh[];  // [RPB][nchunk]
   const int bh = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int row = idx / D, d = idx % D;
-  if (row >= a.Mout) return;  // whole D-groups exit together
+  const int lr = threadIdx.x / D, d = threadIdx.x % D;
+  const int row = blockIdx.x * RPB + lr;
+  float* w = wsh + lr * a.nchunk;
   float res = 0.f, qd = 0.f;
-  if (row < a.M) {
-    const int64_t base = (int64_t)bh * a.nchunk * a.Mp;
-    float m = -INFINITY;
-    for (int ch = 0; ch < a.nchunk; ch++) m = fmaxf(m, a.part_m[base + (int64_t)ch * a.Mp + row]);
-    float den = 0.f, num = 0.f;
-    for (int ch = 0; ch < a.nchunk; ch++) {
+  const int64_t base = (int64_t)bh * a.nchunk * a.Mp;
+  const bool valid = row < a.M;
+  float m = -INFINITY, den = 0.f;
+  if (valid) {
+    for (int ch = d; ch < a.nchunk; ch += D) m = fmaxf(m, a.part_m[base + (int64_t)ch * a.Mp + row]);
+  }
+#pragma unroll
+  for (int o = 1; o < D; o <<= 1) m = fmaxf(m, shfl_xor(m, o));
+  if (valid) {
+    for (int ch = d; ch < a.nchunk; ch += D) {
       const int64_t o = base + (int64_t)ch * a.Mp + row;
-      const float w = exp2_fast(a.part_m[o] - m);
-      den += w * a.part_l[o];
-      num += w * a.part_acc[o * D + d];
+      const float wc = exp2_fast(a.part_m[o] - m);
+      w[ch] = wc;
+      den += wc * a.part_l[o];
     }
-    qd = num / den;
+  }
+#pragma unroll
+  for (int o = 1; o < D; o <<= 1) den += shfl_xor(den, o);
+  __syncthreads();
+  if (valid) {
+    const float* acc = a.part_acc + (base + row) * D + d;
+    const int64_t cstride = (int64_t)a.Mp * D;
+    float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f;
+    int ch = 0;
+    for (; ch + 4 <= a.nchunk; ch += 4) {
+      num0 += w[ch] * acc[(int64_t)ch * cstride];
+      num1 += w[ch + 1] * acc[(int64_t)(ch + 1) * cstride];
+      num2 += w[ch + 2] * acc[(int64_t)(ch + 2) * cstride];
+      num3 += w[ch + 3] * acc[(int64_t)(ch + 3) * cstride];
+    }
+    for (; ch < a.nchunk; ch++) num0 += w[ch] * acc[(int64_t)ch * cstride];
+    qd = ((num0 + num1) + (num2 + num3)) / den;
     res = qd;
   }
+  if (row >= a.Mout) return;  // rows past M up to Mout are written as zeros below
   if constexpr (GATE) {
     const int h = bh % a.H;
     const float f = (row < a.M) ? to_f(reinterpret_cast<const T*>(a.Qf)[((int64_t)h * a.M + row) * D + d]) : 0.f;
@@ -1558,7 +1584,10 @@ hipError_t launch_partial(const PartialArgs& a, int dtype, int D, bool synth, in
 template <typename T, int D, bool GATE>
 static hipError_t launch_merge_t(const MergeArgs& a, int BH, hipStream_t st) {
   const int gx = (a.Mout * D + 255) / 256;
-  hipLaunchKernelGGL((merge_kernel<T, D, GATE>), dim3(gx, BH), dim3(256), 0, st, a);
+  const size_t lds = (size_t)(256 / D) * a.nchunk * sizeof(float);
+  hipError_t e = allow_lds(merge_kernel<T, D, GATE>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<T, D, GATE>), dim3(gx, BH), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
