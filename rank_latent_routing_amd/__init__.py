@@ -10,7 +10,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libflarepp.so")
+# FLAREPP_LIB may name another build of the same library (for side-by-side timing).
+LIB_PATH = os.environ.get("FLAREPP_LIB") or os.path.join(PKG_DIR, "libflarepp.so")
 
 FLAREPP_OK = 0
 FLAREPP_INVALID_ARGUMENT = 1

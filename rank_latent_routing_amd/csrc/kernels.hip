@@ -113,6 +113,18 @@ __device__ __forceinline__ f16x8 to_f16x8(bf16x8 x) {
 // Row (or column) of the 32x32 result held in slot v by a lane of half h = l / 32.
 __host__ __device__ constexpr int row32(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
+// Sums of packed probabilities on the matrix unit. A bf16x8 operand of the 32x32x16 layout (lane l:
+// index l % 32, eight k values) read as a 16x16x32 operand puts index i and i + 16 in the same
+// 16-row, in the even and odd k-slices. Against this 0/1 selector (all ones in k-slices of the
+// matching parity, columns 0-7 for even slices and 8-15 for odd ones) the 16x16x32 MFMA returns
+// the sum over the k values of index i in row (or column) i % 16 of columns (rows) 0-7 when
+// i < 16, and of columns (rows) 8-15 when i >= 16.
+__device__ __forceinline__ bf16x8 sum_selector(int lane) {
+  const bool one = (((lane >> 4) & 1) == 0) == ((lane & 15) < 8);
+  const bf16 v = one ? (bf16)1.0f : (bf16)0.0f;
+  return bf16x8{v, v, v, v, v, v, v, v};
+}
+
 // Transposed LDS read of 4 bf16 (see the file header for the lane mapping). `p` points into LDS.
 __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   lds_s16x4* q = (lds_s16x4*)(__attribute__((address_space(3))) char*)(p);
@@ -654,6 +666,9 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   // same tokens.
   f32x16 zw[NB];
   float lw[NB];
+  // Row sums of the pipelined stages, accumulated on the matrix unit (see sum_selector).
+  f32x4 ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 sel = sum_selector(lane);
   auto compute_wide = [&](int buf, int nvalid) {
     if constexpr (kWide) {
       const bf16* kt = reinterpret_cast<const bf16*>(ks) + buf * kStage * RS;
@@ -724,8 +739,10 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; v++) x[v0 + v] = exp2_fast(x[v0 + v]);
       };
-      // Step: scores of the next sub-tile into `nx` (from `kn`), probabilities and P.V of `cu`.
-      auto step = [&](f32x16& cu, const VOp& vc, f32x16& nx, const KOp& kn, bool has_next) __attribute__((always_inline)) {
+      // Step st: scores of sub-tile st+1 into `nx` (keys `kn`, replaced by those of st+2 once the
+      // score MFMAs are issued), probabilities and P.V of sub-tile st (`cu`).
+      auto step = [&](int st, f32x16& cu, const VOp& vc, f32x16& nx, KOp& kn) __attribute__((always_inline)) {
+        const bool has_next = st + 1 < NS;
         if (has_next) nx = mfma_32x32_f16(kn.a, qw[0][0], f32x16{});
         fence();
         exps(cu, 0);
@@ -734,28 +751,28 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
         fence();
         keep_live(kn.a);
         keep_live(kn.b);
+        if (st + 2 < NS) kn = load_k(st + 2);
         exps(cu, 4);
         const bf16x8 p0 = pack32(cu, 0);
-        lw[0] = O::osum(p0, lw[0]);
         fence();
         zw[0] = mfma_32x32(p0, vc.a, zw[0]);
+        ls4 = mfma_32k(p0, sel, ls4);
         fence();
         keep_live(p0);
         keep_live(vc.a);
         exps(cu, 8);
         exps(cu, 12);
         const bf16x8 p1 = pack32(cu, 1);
-        lw[0] = O::osum(p1, lw[0]);
         fence();
         zw[0] = mfma_32x32(p1, vc.b, zw[0]);
+        ls4 = mfma_32k(p1, sel, ls4);
         fence();
         keep_live(p1);
         keep_live(vc.b);
       };
       // Prologue: scores of sub-tile 0 and the keys of sub-tile 1. Step st reads the values of
-      // sub-tile st at its start and the keys of sub-tile st+2 for the next step.
+      // sub-tile st at its start and the keys of sub-tile st+2 once its score MFMAs are issued.
       f32x16 sc[2];
-      KOp kb[2];
       {
         const KOp k0 = load_k(0);
         sc[0] = mfma_32x32_f16(k0.a, qw[0][0], f32x16{});
@@ -764,12 +781,11 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
         keep_live(k0.a);
         keep_live(k0.b);
       }
-      kb[1] = load_k(1);
+      KOp kn = load_k(1);
 #pragma unroll
       for (int st = 0; st < NS; st++) {
         const VOp vc = load_v(st);
-        if (st + 2 < NS) kb[st & 1] = load_k(st + 2);
-        step(sc[st & 1], vc, sc[(st + 1) & 1], kb[(st + 1) & 1], st + 1 < NS);
+        step(st, sc[st & 1], vc, sc[(st + 1) & 1], kn);
       }
     }
   };
@@ -780,6 +796,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       lw[nb] = 0.f;
       zw[nb] = f32x16{};
     }
+    ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
     load_set(I0{}, 0);
     if (nstage > 1) load_set(I1{}, 1);
     store_set(I0{}, 0, std::true_type{});
@@ -867,6 +884,16 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   if constexpr (kWide) {
     if (!exact) {
       run_chunk_wide();
+      if constexpr (NB == 1) {
+        // Latent j = l % 32 sums to row j % 16, columns 0-7 (j < 16) or 8-15 (j >= 16): lane
+        // 16 ((j % 16) / 4) + 8 (j / 16), slot j % 4. Counted once, on the half h = 0.
+        const int j = lane & 31;
+        const int src = 16 * ((j & 15) >> 2) + 8 * (j >> 4);
+        const float s0 = shfl(ls4[0], src), s1 = shfl(ls4[1], src), s2 = shfl(ls4[2], src), s3 = shfl(ls4[3], src);
+        const int slot = j & 3;
+        const float lj = slot == 0 ? s0 : slot == 1 ? s1 : slot == 2 ? s2 : s3;
+        if (h32 == 0) lw[0] += lj;
+      }
       bool ok = true;
       if (active) {
 #pragma unroll
@@ -1392,8 +1419,15 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
     // Zero-shift pass for one 32-token block, software-pipelined over the latent blocks as in the
     // partial kernels: step lb issues the score MFMAs of block lb+1 (the zero block past Mp after
     // the last) between fenced groups of block lb's exponentials and pack/sum work, then its P.V.
+    // Token sums on the matrix unit (see sum_selector) when the register budget allows (12
+    // waves); with 16 waves the four selector and four accumulator registers do not fit, and the
+    // sums stay on v_dot2.
+    constexpr bool kSumsOnMfma = NW <= 12;
+    f32x4 ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
     auto accumulate_fast_pipelined = [&]() __attribute__((always_inline)) {
       if constexpr (TB == 1) {
+        // Selector as the A operand: lane l supplies row l % 16 of k-slice l / 16.
+        const bf16x8 dsel = kSumsOnMfma ? sum_selector(lane) : bf16x8{};
         auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
         struct QOp { f16x8 a, b; };
         auto load_q = [&](int lb) __attribute__((always_inline)) {
@@ -1428,18 +1462,20 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
           qn = load_q(lb + 2 <= nlb ? lb + 2 : nlb);
           exps(cu, 4);
           const bf16x8 p0 = pack32(cu, 0);
-          lsum[0] = Ops<bf16, 32>::osum(p0, lsum[0]);
+          if constexpr (!kSumsOnMfma) lsum[0] = Ops<bf16, 32>::osum(p0, lsum[0]);
           fence();
           yacc[0] = mfma_32x32(zb0, p0, yacc[0]);
+          if constexpr (kSumsOnMfma) ls4 = mfma_32k(dsel, p0, ls4);
           fence();
           keep_live(p0);
           keep_live(zb0);
           exps(cu, 8);
           exps(cu, 12);
           const bf16x8 p1 = pack32(cu, 1);
-          lsum[0] = Ops<bf16, 32>::osum(p1, lsum[0]);
+          if constexpr (!kSumsOnMfma) lsum[0] = Ops<bf16, 32>::osum(p1, lsum[0]);
           fence();
           yacc[0] = mfma_32x32(zb1, p1, yacc[0]);
+          if constexpr (kSumsOnMfma) ls4 = mfma_32k(dsel, p1, ls4);
           fence();
           keep_live(p1);
           keep_live(zb1);
@@ -1453,6 +1489,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
           keep_live(q0.a);
           keep_live(q0.b);
         }
+        ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
         QOp qn = load_q(1);
         int lb = 0;
         for (; lb + 2 < nlb; lb += 2) {
@@ -1464,6 +1501,12 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
           step(std::true_type{}, lb + 1, sb, sa, qn);
         } else {
           step(std::true_type{}, lb, sa, sb, qn);
+        }
+        if constexpr (kSumsOnMfma) {
+          // Token t = l % 32 sums to column t % 16 of rows 0-7 (t < 16) or 8-15 (t >= 16): lane
+          // t (t < 16) or t + 16, slot 0. Counted once, on the half h = 0.
+          const float lt = shfl(ls4[0], col < 16 ? col : col + 16);
+          lsum[0] = h == 0 ? lt : 0.f;
         }
       }
     };
@@ -1642,8 +1685,8 @@ static hipError_t launch_decode_wide_t(const DecodeArgs& a, int gx, int gy, hipS
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int gx, int gy, hipStream_t st) {
   if (dtype == 1 && D == 32) {
-    // 12 waves: one 32-token block per wave group with the pipelined zero-shift pass (about 140
-    // registers); 8 waves: two blocks per group, not pipelined (about 180 registers).
+    // 12 or 16 waves: one 32-token block per wave group with the pipelined zero-shift pass; 8
+    // waves: two blocks per group, not pipelined.
     switch (nw) {
       case 8: return launch_decode_wide_t<8, 2>(a, gx, gy, st);
       case 12: return launch_decode_wide_t<12, 1>(a, gx, gy, st);
