@@ -101,6 +101,21 @@ int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Q
                       int dtype, void* out, float* Qd, float* Q, float* Z, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Plain FLARE (Section 3.1, Eq. 3), the fixed-query special case of the mixer: for each (b, h),
+ * out = softmax_M(K Q^T / sqrt(D)) softmax_N(Q K^T / sqrt(D)) V with the caller's latent queries
+ * Q [H, M, D] used as given (no normalization, no synthesis, no gate), shared over the batch.
+ * Layouts, support, semantics and errors as for flarepp_mix; Q must not overlap `out`. The library
+ * allocates its workspace stream-ordered (flarepp_flare) or takes the caller's
+ * (flarepp_flare_ws, at least flarepp_workspace_bytes(B, H, N, M, D, dtype) bytes, 256-byte
+ * aligned).
+ */
+int flarepp_flare(const void* K, const void* V, const void* Q, int B, int H, int64_t N, int M, int D,
+                  int dtype, void* out, hipStream_t stream);
+int flarepp_flare_ws(const void* K, const void* V, const void* Q, int B, int H, int64_t N, int M,
+                     int D, int dtype, void* out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
 /* Test hook: while enabled (non-zero), every call skips the zero-shift pass and computes all three
  * softmaxes with exact running maxima (the path the library otherwise takes only for rows whose
  * zero-shift result fails its range check). Results agree with the default path to rounding.

@@ -51,6 +51,11 @@ def lib() -> ctypes.CDLL:
     L.flarepp_mix_ws.restype = i32
     L.flarepp_mix_debug.argtypes = mix_args + [vp, vp, vp, vp, sz, vp]
     L.flarepp_mix_debug.restype = i32
+    flare_args = [vp, vp, vp, i32, i32, i64, i32, i32, i32, vp]
+    L.flarepp_flare.argtypes = flare_args + [vp]
+    L.flarepp_flare.restype = i32
+    L.flarepp_flare_ws.argtypes = flare_args + [vp, sz, vp]
+    L.flarepp_flare_ws.restype = i32
     L.flarepp_debug_force_exact.argtypes = [i32]
     L.flarepp_debug_force_exact.restype = i32
     L.flarepp_timing_enable.argtypes = [i32]
@@ -182,6 +187,39 @@ def flarepp_mix_debug(K, V, S, Qseed, Qf, g, out=None, workspace=None, stream=No
     return out, Qd, Q, Z
 
 
+def _flare_shapes(K, V, Q):
+    if K.dim() != 4 or V.shape != K.shape:
+        raise ValueError("K and V must be [B, H, N, D] of one shape")
+    B, H, N, D = K.shape
+    if Q.dim() != 3 or Q.shape[0] != H or Q.shape[2] != D:
+        raise ValueError("Q must be [H, M, D]")
+    for t in (K, V, Q):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if t.dtype != K.dtype:
+            raise ValueError("K, V, Q must share one dtype")
+    return B, H, N, Q.shape[1], D
+
+
+def flarepp_flare(K, V, Q, out=None, workspace=None, stream=None):
+    """Plain FLARE (Eq. 3): out = softmax_M(K Q^T/sqrt(D)) softmax_N(Q K^T/sqrt(D)) V with the
+    fixed latent queries Q [H, M, D] used as given. With `workspace` (a uint8 tensor of
+    flarepp_workspace_bytes bytes) the caller owns the workspace (flarepp_flare_ws)."""
+    import torch
+    B, H, N, M, D = _flare_shapes(K, V, Q)
+    dt = _dtype_code(K)
+    if out is None:
+        out = torch.empty_like(K)
+    if workspace is None:
+        st = lib().flarepp_flare(_ptr(K), _ptr(V), _ptr(Q), B, H, N, M, D, dt, _ptr(out), _stream_ptr(stream, K.device))
+        _check(st, "flarepp_flare")
+    else:
+        st = lib().flarepp_flare_ws(_ptr(K), _ptr(V), _ptr(Q), B, H, N, M, D, dt, _ptr(out), _ptr(workspace),
+                                    workspace.numel(), _stream_ptr(stream, K.device))
+        _check(st, "flarepp_flare_ws")
+    return out
+
+
 def flarepp_debug_force_exact(enable: bool = True) -> bool:
     """Test hook: force the exact (running-maximum) softmax path for all later calls in this
     process. Returns the previous setting."""
@@ -204,5 +242,6 @@ def flarepp_timing_read() -> dict:
 
 
 __all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
+           "flarepp_flare",
            "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
            "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

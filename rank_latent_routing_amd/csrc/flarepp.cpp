@@ -22,10 +22,10 @@ namespace {
 
 using flarepp::kStage;
 
-constexpr int kVersion = 100;  // 0.1.0
-constexpr int kNumKinds = 5;
+constexpr int kVersion = 200;  // 0.2.0
+constexpr int kNumKinds = 6;
 const char* const kKindNames[kNumKinds] = {"synthesis_partial", "merge_gate", "encode_partial",
-                                           "merge", "decode"};
+                                           "merge", "decode", "query_prep"};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -43,6 +43,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // flarepp_workspace_bytes and the launches, so both always agree.
 struct Plan {
   int BH = 0;
+  int H = 0;
   int Mp16 = 0, Mp32 = 0;
   int part_plan = 0;  // kernel variant, see flarepp::partial_plan_shape
   int nlg = 1;        // latent groups (workgroups per chunk)
@@ -58,6 +59,7 @@ struct Plan {
 Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   Plan p;
   p.BH = B * H;
+  p.H = H;
   p.Mp16 = (M + 15) / 16 * 16;
   p.Mp32 = (M + 31) / 32 * 32;
   // Partial-kernel variant: latents per wave x waves per workgroup, and latent groups per chunk.
@@ -194,6 +196,10 @@ int validate_pointers(const void* K, const void* V, const void* S, const void* Q
   return FLAREPP_OK;
 }
 
+// Encode partials, merge and decode on the routing-query rows already in the workspace.
+int enqueue_routing(const void* K, const void* V, int64_t N, int M, int D, int dtype, void* out, float* dZ,
+                    void* ws, const Plan& p, hipStream_t st);
+
 int enqueue(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
             int B, int H, int64_t N, int M, int D, int dtype, void* out, float* dQd, float* dQ, float* dZ,
             void* ws, const Plan& p, hipStream_t st) {
@@ -202,8 +208,8 @@ int enqueue(const void* K, const void* V, const void* S, const void* Qseed, cons
   float* pl = reinterpret_cast<float*>(w + p.off_l);
   float* pm = reinterpret_cast<float*>(w + p.off_m);
   void* qbuf = w + p.off_q;
-  void* zbuf = w + p.off_z;
   const int gx_part = p.part_gx;
+  (void)B;
 
   flarepp::PartialArgs pa{};
   pa.K = S; pa.V = S; pa.Q = Qseed; pa.H = H; pa.Mq = M; pa.Mp = p.Mp16; pa.N = N;
@@ -218,11 +224,28 @@ int enqueue(const void* K, const void* V, const void* S, const void* Qseed, cons
   if (run_kernel(1, st, [&] { return flarepp::launch_merge(ma, dtype, D, true, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
-  pa.K = K; pa.V = V; pa.Q = qbuf; pa.Mq = p.Mp32;
-  if (run_kernel(2, st, [&] { return flarepp::launch_partial(pa, dtype, D, false, p.part_plan, gx_part, p.BH, st); }) != hipSuccess)
+  return enqueue_routing(K, V, N, M, D, dtype, out, dZ, ws, p, st);
+}
+
+int enqueue_routing(const void* K, const void* V, int64_t N, int M, int D, int dtype, void* out, float* dZ,
+                    void* ws, const Plan& p, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(w + p.off_acc);
+  float* pl = reinterpret_cast<float*>(w + p.off_l);
+  float* pm = reinterpret_cast<float*>(w + p.off_m);
+  void* qbuf = w + p.off_q;
+  void* zbuf = w + p.off_z;
+
+  flarepp::PartialArgs pa{};
+  pa.K = K; pa.V = V; pa.Q = qbuf; pa.H = p.H; pa.Mq = p.Mp32; pa.Mp = p.Mp16; pa.N = N;
+  pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
+  pa.force_exact = g_force_exact.load(); pa.part_l = pl; pa.part_m = pm;
+  if (run_kernel(2, st, [&] { return flarepp::launch_partial(pa, dtype, D, false, p.part_plan, p.part_gx, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
-  ma.Qf = nullptr; ma.g = nullptr; ma.out = zbuf; ma.dbg_qd = nullptr; ma.dbg_out = dZ;
+  flarepp::MergeArgs ma{};
+  ma.part_acc = acc; ma.part_l = pl; ma.part_m = pm; ma.nchunk = p.nchunk; ma.Mp = p.Mp16; ma.M = M;
+  ma.Mout = p.Mp32; ma.H = p.H; ma.Qf = nullptr; ma.g = nullptr; ma.out = zbuf; ma.dbg_qd = nullptr; ma.dbg_out = dZ;
   if (run_kernel(3, st, [&] { return flarepp::launch_merge(ma, dtype, D, false, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
@@ -260,9 +283,55 @@ int mix_common(const void* K, const void* V, const void* S, const void* Qseed, c
   return rc;
 }
 
+int flare_common(const void* K, const void* V, const void* Q, int B, int H, int64_t N, int M, int D, int dtype,
+                 void* out, void* ws, size_t ws_bytes, bool own_ws, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  if (!K || !V || !Q || !out) return FLAREPP_INVALID_ARGUMENT;
+  const void* ptrs[] = {K, V, Q, out};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return FLAREPP_MISALIGNED;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t nbig = (size_t)B * H * N * D * es, nq = (size_t)H * M * D * es;
+  if (overlaps(out, nbig, K, nbig) || overlaps(out, nbig, V, nbig) || overlaps(out, nbig, Q, nq))
+    return FLAREPP_INVALID_ARGUMENT;
+  const Plan p = make_plan(B, H, N, M, D, dtype);
+  if (!own_ws) {
+    if (!ws || ws_bytes < p.total) return FLAREPP_INVALID_ARGUMENT;
+    if ((uintptr_t)ws & 255) return FLAREPP_MISALIGNED;
+  }
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  if (own_ws) {
+    if (hipMallocAsync(&ws, p.total, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLAREPP_OUT_OF_MEMORY;
+    }
+  }
+  flarepp::QueryPrepArgs qa{};
+  qa.Q = Q; qa.H = H; qa.M = M; qa.Mout = p.Mp32; qa.out = static_cast<char*>(ws) + p.off_q;
+  if (run_kernel(5, st, [&] { return flarepp::launch_query_prep(qa, dtype, D, p.BH, st); }) != hipSuccess)
+    rc = FLAREPP_LAUNCH_FAILED;
+  else
+    rc = enqueue_routing(K, V, N, M, D, dtype, out, nullptr, ws, p, st);
+  if (own_ws) (void)hipFreeAsync(ws, st);
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
+
+int flarepp_flare(const void* K, const void* V, const void* Q, int B, int H, int64_t N, int M, int D, int dtype,
+                  void* out, hipStream_t stream) {
+  return flare_common(K, V, Q, B, H, N, M, D, dtype, out, nullptr, 0, true, stream);
+}
+
+int flarepp_flare_ws(const void* K, const void* V, const void* Q, int B, int H, int64_t N, int M, int D,
+                     int dtype, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return flare_common(K, V, Q, B, H, N, M, D, dtype, out, workspace, workspace_bytes, false, stream);
+}
 
 int flarepp_mix(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
                 int B, int H, int64_t N, int M, int D, int dtype, void* out, hipStream_t stream) {

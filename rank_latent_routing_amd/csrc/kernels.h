@@ -80,6 +80,14 @@ struct DecodeArgs {
   int force_exact; // skip the zero-shift pass (test hook)
 };
 
+// Routing-query rows of the workspace from the caller's fixed queries (plain FLARE).
+struct QueryPrepArgs {
+  const void* Q;   // [H][M][D] dtype
+  int H, M, Mout;  // rows per (b, h) block in the output; rows in [M, Mout) are zero
+  void* out;       // c*Q rows [BH][Mout][R*D] as for the gate
+};
+
+hipError_t launch_query_prep(const QueryPrepArgs& a, int dtype, int D, int BH, hipStream_t stream);
 hipError_t launch_partial(const PartialArgs& a, int dtype, int D, bool synth, int plan, int grid_x,
                           int grid_y, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH, hipStream_t stream);

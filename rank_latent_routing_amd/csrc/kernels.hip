@@ -1052,6 +1052,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Plain FLARE (Section 3.1, Eq. 3): the routing-query rows of the workspace from the caller's
+// fixed queries, c*Q in the same parts as the gate writes (bf16: hi, lo, fp16). One thread per
+// (latent, channel) of every (b, h) block.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void query_prep_kernel(QueryPrepArgs a) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int row = idx / D, d = idx % D;
+  if (row >= a.Mout) return;
+  const int h = bh % a.H;
+  const float q = row < a.M ? to_f(reinterpret_cast<const T*>(a.Q)[((int64_t)h * a.M + row) * D + d]) : 0.f;
+  const float cq = q * (kLog2e * rsqrtf((float)D));
+  T* qo = reinterpret_cast<T*>(a.out) + ((int64_t)bh * a.Mout + row) * kQRow<T> * D + d;
+  const T hi = (T)cq;
+  qo[0] = hi;
+  if constexpr (sizeof(T) == 2) {
+    qo[D] = (T)(cq - to_f(hi));
+    reinterpret_cast<f16*>(qo + 2 * D)[0] = (f16)cq;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Decode: every token's scores against all M routing queries, softmax over M, times Z
 // (Eq. 8, second call). The workgroup keeps c*Q (row-major, A operand of the score MFMA, hi then lo
 // per row) and Z (a RowTile: the A operand of the P.V MFMA runs along latents) in LDS; each wave
@@ -1632,6 +1654,18 @@ static hipError_t launch_merge_t(const MergeArgs& a, int BH, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<T, D, GATE>), dim3(gx, BH), dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_query_prep_t(const QueryPrepArgs& a, int BH, hipStream_t st) {
+  const int gx = (a.Mout * D + 255) / 256;
+  hipLaunchKernelGGL((query_prep_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_query_prep(const QueryPrepArgs& a, int dtype, int D, int BH, hipStream_t st) {
+  if (dtype == 1) return D == 32 ? launch_query_prep_t<bf16, 32>(a, BH, st) : launch_query_prep_t<bf16, 16>(a, BH, st);
+  return D == 32 ? launch_query_prep_t<float, 32>(a, BH, st) : launch_query_prep_t<float, 16>(a, BH, st);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH, hipStream_t st) {

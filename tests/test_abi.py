@@ -34,9 +34,9 @@ def test_version_and_strings(L):
     assert fl.flarepp_version() >= 100
     for s in range(0, 8):
         assert isinstance(fl.flarepp_strerror(s), str) and fl.flarepp_strerror(s)
-    assert [fl.flarepp_kernel_name(i) for i in range(5)] == [
-        "synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"]
-    assert fl.flarepp_kernel_name(5) is None
+    assert [fl.flarepp_kernel_name(i) for i in range(6)] == [
+        "synthesis_partial", "merge_gate", "encode_partial", "merge", "decode", "query_prep"]
+    assert fl.flarepp_kernel_name(6) is None
 
 
 def _mix(L, K=0x1000, V=0x2000, S=0x3000, Qs=0x4000, Qf=0x5000, g=0x6000, B=1, H=1, N=64, M=8, D=16,
@@ -102,5 +102,25 @@ def test_workspace_too_small_is_rejected(L):
 def test_timing_read_without_records(L):
     fl.flarepp_timing_enable(False)
     t = fl.flarepp_timing_read()
-    assert set(t) == {"synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"}
+    assert set(t) == {"synthesis_partial", "merge_gate", "encode_partial", "merge", "decode", "query_prep"}
     assert all(v == (0.0, 0) for v in t.values())
+
+
+def _flare(L, K=0x1000, V=0x2000, Q=0x4000, B=1, H=1, N=64, M=8, D=16, dtype=1, out=0x7000000):
+    vp = ctypes.c_void_p
+    return L.flarepp_flare(vp(K), vp(V), vp(Q), B, H, N, M, D, dtype, vp(out), vp(0))
+
+
+def test_flare_validation(L):
+    assert _flare(L, D=24) == fl.FLAREPP_UNSUPPORTED
+    assert _flare(L, M=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _flare(L, M=513) == fl.FLAREPP_UNSUPPORTED
+    assert _flare(L, Q=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _flare(L, Q=0x4004) == fl.FLAREPP_MISALIGNED
+    assert _flare(L, out=0x1000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _flare(L, N=0) == fl.FLAREPP_OK
+    vp = ctypes.c_void_p
+    need = fl.flarepp_workspace_bytes(1, 1, 64, 8, 16, 1)
+    rc = L.flarepp_flare_ws(vp(0x1000), vp(0x2000), vp(0x4000), 1, 1, 64, 8, 16, 1, vp(0x7000000), vp(0x9000000),
+                            need - 1, vp(0))
+    assert rc == fl.FLAREPP_INVALID_ARGUMENT

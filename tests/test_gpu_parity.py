@@ -98,6 +98,14 @@ def test_latent_counts(dtype, D, M):
     _check(make_workload(2, B=1, H=2, N=700, M=M, D=D, dtype=dtype, seed=7 * M + D), label=f"M={M} D={D} {dtype}")
 
 
+@pytest.mark.parametrize("M", [257, 300, 480, 511])
+def test_large_ragged_latent_counts(M):
+    # bf16 D=32 with M > 256: one 16-wave workgroup per chunk (some waves without latents when
+    # M < 512), 256-token stages with a partial last stage, and decode latent blocks of both
+    # parities with a ragged last block.
+    _check(make_workload(4, B=1, H=2, N=3001, M=M, seed=11 * M), label=f"M={M}")
+
+
 @pytest.mark.parametrize("M", [17, 100])
 def test_latent_counts_gaussian_inputs(M):
     _check(make_workload(3, B=1, H=2, N=700, M=M, seed=3 * M), label=f"gauss M={M}")
@@ -234,3 +242,40 @@ def test_full_cfg5_constant_values_pass_through():
     err = np.abs(Y - ref).max() / np.sqrt(np.mean(ref ** 2))
     say(f"[full] cfg5 constant V err {err:.3g}")
     assert err <= tol("bf16")
+
+
+# ---- plain FLARE (Section 3.1, Eq. 3): fixed latent queries, no synthesis, no gate.
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (2, dict(B=2, H=3, N=5000)), (4, dict(B=1, H=2, N=20000)),
+                                    (5, dict(H=1, N=70000)), (4, dict(B=1, H=2, N=3001, M=300, seed=9))])
+def test_plain_flare(cfg, kw):
+    import oracle
+    import rank_latent_routing_amd as fl
+    w = make_workload(cfg, **kw)
+    say(f"[parity] flare cfg{cfg} {kw}")
+    dev = to_device(w)
+    Y = fl.flarepp_flare(dev["K"], dev["V"], dev["Qf"]).float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = oracle.flare(w.f64("Qf")[h], w.f64("K")[b, h], w.f64("V")[b, h])
+            worst = max(worst, slice_err(Y[b, h], ref, w.dtype))
+    say(f"[parity] flare cfg{cfg}: worst {worst} (bar {tol(w.dtype)})")
+    assert worst <= tol(w.dtype)
+
+
+def test_plain_flare_equals_mixer_with_gate_zero():
+    # g = 0 routes with N0(Qf) alone (Section 3.2), so the mixer equals FLARE on N0(Qf); the two
+    # entry points share the encode and decode kernels.
+    import rank_latent_routing_amd as fl
+    w = make_workload(4, B=1, H=2, N=20000, g=0.0)
+    dev = to_device(w)
+    Y = fl.flarepp_mix(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"])
+    qf = dev["Qf"].float()
+    qn = (qf / torch.sqrt((qf * qf).mean(dim=-1, keepdim=True) + 1e-6)).to(dev["Qf"].dtype).contiguous()
+    Y2 = fl.flarepp_flare(dev["K"], dev["V"], qn)
+    torch.cuda.synchronize()
+    # N0(Qf) is rounded to bf16 here but kept in fp32 inside the gate, so compare to the bar.
+    ref = Y.float().cpu().numpy().astype(np.float64)
+    got = Y2.float().cpu().numpy().astype(np.float64)
+    for h in range(w.H):
+        assert slice_err(got[0, h], ref[0, h], w.dtype) <= tol(w.dtype)
