@@ -1287,7 +1287,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 // of the bf16 MFMA Z^T P, which yields Y^T with one token per lane column. Zero-shift pass, per-token range check, and for a group that fails an exact pass:
 // two passes over the latents with running maxima, scores from bf16 keys and the hi/lo queries
 // read from the workspace.
-template <int NW, int TB>
+template <int NW, int TB, bool PREF = true>
 __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
   constexpr int D = 32;
   constexpr int QHS = D + 8;  // fp16 query row stride in LDS (80 bytes: conflict-free row reads)
@@ -1332,23 +1332,32 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
   };
   const int64_t gstride = (int64_t)NW * TG;
   bf16x8 knext[TB][2];
+  if constexpr (PREF) {
 #pragma unroll
-  for (int tb = 0; tb < TB; tb++)
+    for (int tb = 0; tb < TB; tb++)
 #pragma unroll
-    for (int kh = 0; kh < 2; kh++) knext[tb][kh] = load_keys_at(t_begin + (int64_t)wave * TG, tb, kh);
+      for (int kh = 0; kh < 2; kh++) knext[tb][kh] = load_keys_at(t_begin + (int64_t)wave * TG, tb, kh);
+  }
 
   for (int64_t base = t_begin + (int64_t)wave * TG; base < t_end; base += gstride) {
     auto load_keys = [&](int tb, int kh) __attribute__((always_inline)) { return load_keys_at(base, tb, kh); };
     f16x8 kf[TB][2];
-#pragma unroll
-    for (int tb = 0; tb < TB; tb++)
-#pragma unroll
-      for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(knext[tb][kh]);
-    if (base + gstride < t_end) {
+    if constexpr (PREF) {
 #pragma unroll
       for (int tb = 0; tb < TB; tb++)
 #pragma unroll
-        for (int kh = 0; kh < 2; kh++) knext[tb][kh] = load_keys_at(base + gstride, tb, kh);
+        for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(knext[tb][kh]);
+      if (base + gstride < t_end) {
+#pragma unroll
+        for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+          for (int kh = 0; kh < 2; kh++) knext[tb][kh] = load_keys_at(base + gstride, tb, kh);
+      }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+        for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(load_keys_at(base, tb, kh));
     }
 
     f32x16 yacc[TB];
@@ -1441,10 +1450,9 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
     // Zero-shift pass for one 32-token block, software-pipelined over the latent blocks as in the
     // partial kernels: step lb issues the score MFMAs of block lb+1 (the zero block past Mp after
     // the last) between fenced groups of block lb's exponentials and pack/sum work, then its P.V.
-    // Token sums on the matrix unit (see sum_selector) when the register budget allows (12
-    // waves); with 16 waves the four selector and four accumulator registers do not fit, and the
-    // sums stay on v_dot2.
-    constexpr bool kSumsOnMfma = NW <= 12;
+    // Token sums on the matrix unit (see sum_selector) when the register budget allows: with 12
+    // waves, or with 16 waves and no key prefetch; otherwise they stay on v_dot2.
+    constexpr bool kSumsOnMfma = NW <= 12 || !PREF;
     f32x4 ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
     auto accumulate_fast_pipelined = [&]() __attribute__((always_inline)) {
       if constexpr (TB == 1) {
@@ -1708,23 +1716,24 @@ static size_t decode_wide_lds(int Mp) {
   return (size_t)(Mp + 32) * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16);
 }
 
-template <int NW, int TB>
+template <int NW, int TB, bool PREF = true>
 static hipError_t launch_decode_wide_t(const DecodeArgs& a, int gx, int gy, hipStream_t st) {
   const size_t lds = decode_wide_lds(a.Mp);
-  hipError_t e = allow_lds(decode_wide_kernel<NW, TB>, lds);
+  hipError_t e = allow_lds(decode_wide_kernel<NW, TB, PREF>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_wide_kernel<NW, TB>), dim3(gx, gy), dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((decode_wide_kernel<NW, TB, PREF>), dim3(gx, gy), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int gx, int gy, hipStream_t st) {
   if (dtype == 1 && D == 32) {
-    // 12 or 16 waves: one 32-token block per wave group with the pipelined zero-shift pass; 8
-    // waves: two blocks per group, not pipelined.
+    // 12 or 16 waves: one 32-token block per wave group with the pipelined zero-shift pass (16
+    // waves: keys loaded at the group's start, leaving the registers for the token sums on the
+    // matrix unit); 8 waves: two blocks per group, not pipelined.
     switch (nw) {
       case 8: return launch_decode_wide_t<8, 2>(a, gx, gy, st);
       case 12: return launch_decode_wide_t<12, 1>(a, gx, gy, st);
-      case 16: return launch_decode_wide_t<16, 1>(a, gx, gy, st);
+      case 16: return launch_decode_wide_t<16, 1, false>(a, gx, gy, st);
       default: return hipErrorInvalidValue;
     }
   }
