@@ -129,6 +129,68 @@ def mix(K, V, S, Qseed, Qf, g, block: int | None = None) -> dict:
     return {key: np.stack(val) for key, val in out.items()}
 
 
+# ---- Backward pass ------------------------------------------------------------------------------
+
+def rms_normalize_backward(x: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """Cotangent of N0 (Section 3.2). With y = x r and r = (mean(x^2) + eps)^(-1/2) per row,
+    dx = r dy - r^3 x mean(x dy) (the derivative of r is -r^3 x / D)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + RMS_EPS)
+    return r * dy - r ** 3 * x * np.mean(x * dy, axis=-1, keepdims=True)
+
+
+def sdpa_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray):
+    """Cotangents of o = softmax(q k^T s) v, s = D^(-1/2), given dout (Appendix B.5, Eq. 46-49 on a
+    single shard, whose log-normalizer gets no cotangent): with P the normalized probabilities and
+    c_i = <dout_i, o_i>, dv = P^T dout, dS = P * (dout v^T - c), dq = s dS k, dk = s dS^T q.
+    Returns (dq, dk, dv)."""
+    s = 1.0 / math.sqrt(q.shape[-1])
+    P = softmax_rows(q @ k.T * s)
+    o = P @ v
+    dout = np.asarray(dout, dtype=np.float64)
+    dv = P.T @ dout
+    c = np.sum(dout * o, axis=-1, keepdims=True)
+    dS = P * (dout @ v.T - c)
+    return s * dS @ k, s * dS.T @ q, dv
+
+
+def mix_head_backward(K, V, S, Qseed, Qf, g, dY) -> dict:
+    """Cotangents of one (batch, head) slice of the mixer (Appendix A.1, Eq. 11) given dY [N, D]:
+    the decode call, then the encode call, the gate (Eq. 7) and the synthesis call, each SDPA by
+    ``sdpa_backward`` and each N0 by ``rms_normalize_backward``. The decode's keys are the routing
+    queries and its queries the token keys, so K and Q receive cotangents from both calls.
+    Returns dK, dV, dS [N, D], dQseed, dQf [M, D] and dg (a scalar)."""
+    Sn = rms_normalize(S)
+    Qd = sdpa(Qseed, Sn, Sn)
+    Q = gate(Qf, Qd, g)
+    Z = sdpa(Q, K, V)
+    dK_dec, dQ_dec, dZ = sdpa_backward(K, Q, Z, dY)
+    dQ_enc, dK_enc, dV = sdpa_backward(Q, K, V, dZ)
+    dQ = dQ_dec + dQ_enc
+    dQseed, dSn_keys, dSn_values = sdpa_backward(Qseed, Sn, Sn, float(g) * dQ)
+    return {"dK": dK_dec + dK_enc, "dV": dV, "dS": rms_normalize_backward(S, dSn_keys + dSn_values),
+            "dQseed": dQseed, "dQf": rms_normalize_backward(Qf, dQ), "dg": float(np.sum(dQ * Qd)),
+            "dQ": dQ, "dZ": dZ}
+
+
+def mix_backward(K, V, S, Qseed, Qf, g, dY) -> dict:
+    """``mix_head_backward`` over all batch elements and heads. The seeds, Qf and g are shared over
+    the batch, so their cotangents are summed over it. Returns dK, dV, dS [B, H, N, D], dQseed,
+    dQf [H, M, D] and dg [H]."""
+    B, H = K.shape[:2]
+    out = {"dK": np.zeros(K.shape), "dV": np.zeros(K.shape), "dS": np.zeros(K.shape),
+           "dQseed": np.zeros(Qseed.shape), "dQf": np.zeros(Qf.shape), "dg": np.zeros(H)}
+    for b in range(B):
+        for h in range(H):
+            r = mix_head_backward(K[b, h], V[b, h], S[b, h], Qseed[h], Qf[h], g[h], dY[b, h])
+            out["dK"][b, h], out["dV"][b, h], out["dS"][b, h] = r["dK"], r["dV"], r["dS"]
+            out["dQseed"][h] += r["dQseed"]
+            out["dQf"][h] += r["dQf"]
+            out["dg"][h] += r["dg"]
+    return out
+
+
 def routing_factors(Q: np.ndarray, K: np.ndarray):
     """The two routing factors of Section 3.1, Eq. 3-4, for queries Q [M, D] and keys K [N, D]:
     W_enc = softmax(S) [M, N] (over tokens) and W_dec = softmax(S^T) [N, M] (over latents), with
