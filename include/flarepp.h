@@ -116,6 +116,37 @@ int flarepp_flare_ws(const void* K, const void* V, const void* Q, int B, int H, 
                      int D, int dtype, void* out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/*
+ * Backward pass of flarepp_mix: given the same inputs and the cotangent dY of `out`
+ * ([B, H, N, D], dtype), writes the cotangents of every input (Appendix B.5, Eq. 46-49 applied to
+ * the decode, encode and synthesis calls of Section 3.2 Eq. 6 and Eq. 8 in reverse order, through
+ * the gate of Eq. 7 and the normalization N0 of Eq. 5):
+ *   dK, dV, dS  [B, H, N, D] dtype  (dK sums the encode and decode calls' contributions);
+ *   dQseed, dQf [H, M, D]    dtype  (summed over the batch, as the seeds and Qf are shared);
+ *   dg          [H]          fp32   (the cotangent of the gate value g, summed over the batch).
+ * The forward pass is recomputed inside the call (nothing has to be kept from flarepp_mix).
+ * Accumulation is fp32. In bf16 runs every operand the library computes (probabilities, score
+ * cotangents, the routing queries, Z, dZ and the other latent cotangents) enters the matrix unit
+ * as a pair of bf16 values hi + lo, so that the cotangents carry about 16 significant bits until
+ * they are stored in bf16. Support as for flarepp_mix. Every output is written fully and must not
+ * overlap any other argument buffer; inputs are read-only. With B*H*N == 0 the shared parameters'
+ * cotangents are set to zero. Deterministic (no atomics), asynchronous on `stream`.
+ * flarepp_mix_backward allocates its workspace stream-ordered; flarepp_mix_backward_ws takes the
+ * caller's: at least flarepp_backward_workspace_bytes(B, H, N, M, D, dtype) bytes (0 for invalid
+ * sizes), 256-byte aligned. It holds per-token statistics and, for bf16, the decode call's part of
+ * dK in fp32, so it grows with B*H*N*D.
+ */
+size_t flarepp_backward_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype);
+int flarepp_mix_backward(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                         const float* g, const void* dY, int B, int H, int64_t N, int M, int D,
+                         int dtype, void* dK, void* dV, void* dS, void* dQseed, void* dQf, float* dg,
+                         hipStream_t stream);
+int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const void* Qseed,
+                            const void* Qf, const float* g, const void* dY, int B, int H, int64_t N,
+                            int M, int D, int dtype, void* dK, void* dV, void* dS, void* dQseed,
+                            void* dQf, float* dg, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Test hook: while enabled (non-zero), every call skips the zero-shift pass and computes all three
  * softmaxes with exact running maxima (the path the library otherwise takes only for rows whose
  * zero-shift result fails its range check). Results agree with the default path to rounding.

@@ -56,6 +56,13 @@ def lib() -> ctypes.CDLL:
     L.flarepp_flare.restype = i32
     L.flarepp_flare_ws.argtypes = flare_args + [vp, sz, vp]
     L.flarepp_flare_ws.restype = i32
+    bwd_args = mix_args[:6] + [vp, i32, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.flarepp_mix_backward.argtypes = bwd_args + [vp]
+    L.flarepp_mix_backward.restype = i32
+    L.flarepp_mix_backward_ws.argtypes = bwd_args + [vp, sz, vp]
+    L.flarepp_mix_backward_ws.restype = i32
+    L.flarepp_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.flarepp_backward_workspace_bytes.restype = sz
     L.flarepp_debug_force_exact.argtypes = [i32]
     L.flarepp_debug_force_exact.restype = i32
     L.flarepp_timing_enable.argtypes = [i32]
@@ -220,6 +227,34 @@ def flarepp_flare(K, V, Q, out=None, workspace=None, stream=None):
     return out
 
 
+def flarepp_backward_workspace_bytes(B: int, H: int, N: int, M: int, D: int, dtype: int) -> int:
+    return int(lib().flarepp_backward_workspace_bytes(B, H, N, M, D, dtype))
+
+
+def flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=None, workspace=None, stream=None):
+    """Backward pass of flarepp_mix given the output cotangent dY [B, H, N, D] (the input dtype).
+    Returns {dK, dV, dS: [B, H, N, D], dQseed, dQf: [H, M, D] in the input dtype, dg: [H] float32};
+    `grads` may supply those tensors. With `workspace` (a uint8 tensor of
+    flarepp_backward_workspace_bytes bytes) the caller owns the workspace (flarepp_mix_backward_ws)."""
+    import torch
+    B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    if dY.shape != K.shape or dY.dtype != K.dtype or not dY.is_contiguous():
+        raise ValueError("dY must be a contiguous tensor of K's shape and dtype")
+    dt = _dtype_code(K)
+    if grads is None:
+        grads = {"dK": torch.empty_like(K), "dV": torch.empty_like(K), "dS": torch.empty_like(K),
+                 "dQseed": torch.empty_like(Qseed), "dQf": torch.empty_like(Qf), "dg": torch.empty_like(g)}
+    outs = [_ptr(grads[k]) for k in ("dK", "dV", "dS", "dQseed", "dQf", "dg")]
+    args = [_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), _ptr(dY), B, H, N, M, D, dt] + outs
+    if workspace is None:
+        st = lib().flarepp_mix_backward(*args, _stream_ptr(stream, K.device))
+        _check(st, "flarepp_mix_backward")
+    else:
+        st = lib().flarepp_mix_backward_ws(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream, K.device))
+        _check(st, "flarepp_mix_backward_ws")
+    return grads
+
+
 def flarepp_debug_force_exact(enable: bool = True) -> bool:
     """Test hook: force the exact (running-maximum) softmax path for all later calls in this
     process. Returns the previous setting."""
@@ -232,7 +267,7 @@ def flarepp_timing_enable(enable: bool = True) -> None:
 
 def flarepp_timing_read() -> dict:
     """Per-kernel event timings accumulated since the last read: {name: (total_ms, launches)}."""
-    n = 16
+    n = 32
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_longlong * n)()
     k = lib().flarepp_timing_read(ms, cnt, n)
@@ -242,6 +277,6 @@ def flarepp_timing_read() -> dict:
 
 
 __all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
-           "flarepp_flare",
+           "flarepp_flare", "flarepp_mix_backward", "flarepp_backward_workspace_bytes",
            "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
            "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

@@ -1,0 +1,1252 @@
+// HIP kernels of the FLARE++ mixer backward pass for gfx950 (CDNA4).
+//
+// Method: "FLARE++: Low-rank attention with attention-synthesized routing" (arXiv 2608.11519 v2).
+// The mixer (Appendix A.1, Eq. 11) is three softmax routing calls (Section 3.2, Eq. 6 and Eq. 8)
+// joined by the gate (Eq. 7) and the normalization N0 (Eq. 5). Its cotangents follow the SDPA
+// backward of Appendix B.5 (Eq. 46-49) call by call, in reverse order: decode, encode, gate,
+// synthesis, N0. For one call o = softmax(q k^T / sqrt(D)) v with cotangent do and probabilities P:
+//   dP = do v^T,  c = rowsum(P * dP) = <do, o>,  dS = P * (dP - c),
+//   dq = dS k / sqrt(D),  dk = dS^T q / sqrt(D),  dv = P^T do.
+// The host first recomputes the synthesis and encode calls and keeps every softmax row's normalizer
+// L in the logits' log2 units (the logits carry c = log2(e)/sqrt(D)), so that each probability here
+// is one exponential of a known logit, P = 2^(l - L), with no running maximum.
+//
+// Kernels (32x32x16 MFMAs with bf16 operands and fp32 accumulation; fp32 runs issue eight 32x32x2
+// fp32 MFMAs per 32x32x16 step, with the same lane layout):
+//   center       Zc = Z - mean_m Z, the decode call's dP operand (the shift cancels in dP - c).
+//   decode       per token: the normalizer L_n and c_n = sum_m P dP of its softmax over latents (one
+//                online pass), then the decode call's part of dK (a second pass), in fp32.
+//   latent-side  one per call: the latent-indexed cotangents, which sum over tokens (decode: dZ and
+//                dQ; encode: dQ; synthesis: dQseed), split over token chunks like the forward
+//                partials. Each wave owns 32 latents; the chunk's token tiles pass through LDS.
+//   reduce       the chunk sums plus the latent-sized steps between the calls: <dZ, Z>, the gate
+//                and N0 of Qf, and the batch sums of the shared parameters.
+//   token-side   the token-indexed cotangents, which sum over latents: dK (adding the decode part)
+//                and dV from the encode call, dS from the synthesis call and N0. The latent tensors
+//                of one (batch, head) stay in LDS; each wave takes blocks of 32 tokens.
+//
+// Precision. The cotangents are sums in which rounding errors of the operands do not cancel while the
+// terms themselves largely do (each dS = P (dP - c) sums to zero along its softmax, and the values of
+// a call cluster). Every operand the kernels compute (P, dS, c*Q, Zc, dZ, G, c*N0(S)) therefore
+// enters the matrix unit as a bf16 pair hi + lo (hi = bf16(x), lo = bf16(x - hi), about 16
+// significant bits); a product of two pairs takes the three MFMAs hi.hi + hi.lo + lo.hi. The inputs
+// K, V, S, dY and the seeds are exact bf16. Each c is formed from the operands its dP products see
+// (the decode call's from its own P and dP, the encode call's as <dZ, Z> with dZ as carried, the
+// synthesis call's as <G, Qd> likewise), and the recomputed forward takes the exact hi/lo path, so
+// that its normalizers match the logits computed here.
+//
+// Layout of the 32x32x16 MFMA C[i][j] += sum_k A[i][k] B[k][j]: lane l supplies row l % 32 of A and
+// column l % 32 of B with k = 8 (l / 32) + e (e = 0..7) and receives column l % 32, rows
+// row32(v, l / 32) (v = 0..15). The 16 result slots of a tile, taken eight at a time (split), are
+// directly the B operand of a product that sums over the tile's rows; the matching A operand comes
+// from LDS with transposed reads (krows), rows in the same row32 order.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <type_traits>
+
+#include "device.h"
+#include "kernels.h"
+
+namespace flarepp {
+namespace {
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// The register allocator may place an MFMA's destination on top of an A or B operand that dies at
+// that instruction, and the double-depth gfx950 MFMA forms then return wrong products. hold(acc, x)
+// keeps x live past the MFMA that produced acc: an empty asm that reads x and rewrites acc, so it can
+// only come after that MFMA, whatever order instruction selection and scheduling choose.
+template <typename O>
+__device__ __forceinline__ void hold(f32x16& acc, const O& x) {
+  asm volatile("" : "+v"(acc) : "v"(x));
+}
+
+// Rows of D elements in LDS whose 16-byte chunks are permuted by an XOR with (row / RPB) % CPR, where
+// RPB rows span the 64 banks: the row reads of 32 lanes (32 rows, one chunk each) and the transposed
+// reads (4 rows x 32 bytes per group of 16 lanes) then touch distinct banks.
+template <typename T, int D>
+struct Swz {
+  static constexpr int CH = 16 / sizeof(T);      // elements per chunk
+  static constexpr int CPR = D / CH;             // chunks per row
+  static constexpr int RPB = 256 / (16 * CPR);   // rows per 256 bytes
+  __device__ static int off(int row, int col) {
+    return row * D + (((col / CH) ^ ((row / RPB) % CPR)) * CH) + (col % CH);
+  }
+};
+
+// Position of latent (or token) m in a stats array laid out so that lane half h of a 32-block reads
+// the 16 values of its result slots, rows row32(v, h), as one contiguous run.
+__device__ __forceinline__ int stat_pos(int m) {
+  const int r = m & 31;
+  return (m & ~31) + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
+// Operands of one 32x32x16 step. Op holds the eight k values of a lane; Pair is an operand with its
+// rounding residual (bf16) or the operand alone (fp32).
+template <typename T>
+struct Frag;
+
+template <>
+struct Frag<bf16> {
+  using Op = bf16x8;
+  static constexpr bool kLo = true;
+  struct Pair {
+    Op h, l;
+  };
+  __device__ static Op zero() { return Op{}; }
+  __device__ static f32x16 mma(const Op& a, const Op& b, const f32x16& c) { return mfma_32x32(a, b, c); }
+  // Slots 8t .. 8t + 7 of a result tile as a pair.
+  __device__ static Pair split(const f32x16& x, int t) {
+    Pair p;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float v = x[8 * t + e];
+      const bf16 hv = (bf16)v;
+      p.h[e] = hv;
+      p.l[e] = (bf16)(v - (float)hv);
+    }
+    return p;
+  }
+  __device__ static Pair split8(const float* v) {
+    Pair p;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const bf16 hv = (bf16)v[e];
+      p.h[e] = hv;
+      p.l[e] = (bf16)(v[e] - (float)hv);
+    }
+    return p;
+  }
+  __device__ static void to_float(const Op& o, float* x) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = (float)o[e];
+  }
+  __device__ static Op gload(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  // Elements col .. col + 7 of row r of a swizzled tile.
+  template <int D>
+  __device__ static Op row(const bf16* tile, int r, int col) {
+    return *reinterpret_cast<const bf16x8*>(tile + Swz<bf16, D>::off(r, col));
+  }
+  // A operand along the tile's rows: lane l gets rows r0 + row32(e, l / 32) of column l % 32 (D = 16:
+  // column l % 16; the upper 16 result rows then repeat the lower ones and are not used).
+  template <int D>
+  __device__ static Op krows(const bf16* tile, int r0, int lane) {
+    using S = Swz<bf16, D>;
+    const int i = lane & 15, cb = ((lane >> 4) & 1) & (D / 16 - 1), hh = lane >> 5;
+    const int r = r0 + 4 * hh + (i >> 2), col = 16 * cb + 4 * (i & 3);
+    const bf16x4 lo = lds_read_tr4(tile + S::off(r, col));
+    const bf16x4 hi = lds_read_tr4(tile + S::off(r + 8, col));
+    Op o;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      o[e] = lo[e];
+      o[4 + e] = hi[e];
+    }
+    return o;
+  }
+};
+
+template <>
+struct Frag<float> {
+  using Op = f32x8;
+  static constexpr bool kLo = false;
+  struct Pair {
+    Op h;
+  };
+  __device__ static Op zero() { return Op{}; }
+  // Step e covers k = e (lanes 0-31) and k = 8 + e (lanes 32-63) of the 32x32x16 layout.
+  __device__ static f32x16 mma(const Op& a, const Op& b, const f32x16& c) {
+    f32x16 r = c;
+#pragma unroll
+    for (int e = 0; e < 8; e++) r = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], r, 0, 0, 0);
+    return r;
+  }
+  __device__ static Pair split(const f32x16& x, int t) {
+    Pair p;
+#pragma unroll
+    for (int e = 0; e < 8; e++) p.h[e] = x[8 * t + e];
+    return p;
+  }
+  __device__ static Pair split8(const float* v) {
+    Pair p;
+#pragma unroll
+    for (int e = 0; e < 8; e++) p.h[e] = v[e];
+    return p;
+  }
+  __device__ static void to_float(const Op& o, float* x) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = o[e];
+  }
+  __device__ static Op gload(const float* p) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return Op{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  template <int D>
+  __device__ static Op row(const float* tile, int r, int col) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + Swz<float, D>::off(r, col));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + Swz<float, D>::off(r, col + 4));
+    return Op{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  template <int D>
+  __device__ static Op krows(const float* tile, int r0, int lane) {
+    const int hh = lane >> 5, col = (lane & 31) & (D - 1);
+    Op o;
+#pragma unroll
+    for (int e = 0; e < 8; e++) o[e] = tile[Swz<float, D>::off(r0 + row32(e, hh), col)];
+    return o;
+  }
+};
+
+// Products of pairs and exact operands (the lo.lo term of two pairs is below fp32 resolution).
+template <typename F>
+__device__ __forceinline__ f32x16 mma_ep(const typename F::Op& a, const typename F::Pair& b, f32x16 c) {
+  if constexpr (F::kLo) c = F::mma(a, b.l, c);
+  return F::mma(a, b.h, c);
+}
+template <typename F>
+__device__ __forceinline__ f32x16 mma_pe(const typename F::Pair& a, const typename F::Op& b, f32x16 c) {
+  if constexpr (F::kLo) c = F::mma(a.l, b, c);
+  return F::mma(a.h, b, c);
+}
+template <typename F>
+__device__ __forceinline__ f32x16 mma_pp(const typename F::Pair& a, const typename F::Pair& b, f32x16 c) {
+  if constexpr (F::kLo) {
+    c = F::mma(a.l, b.h, c);
+    c = F::mma(a.h, b.l, c);
+  }
+  return F::mma(a.h, b.h, c);
+}
+template <typename F>
+__device__ __forceinline__ void hold(f32x16& acc, const typename F::Pair& x) {
+  hold(acc, x.h);
+  if constexpr (F::kLo) hold(acc, x.l);
+}
+// Pair reads of two swizzled tiles (hi, lo).
+template <typename F, int D, typename T>
+__device__ __forceinline__ typename F::Pair row_pair(const T* th, const T* tl, int r, int col) {
+  typename F::Pair p;
+  p.h = F::template row<D>(th, r, col);
+  if constexpr (F::kLo) p.l = F::template row<D>(tl, r, col);
+  return p;
+}
+template <typename F, int D, typename T>
+__device__ __forceinline__ typename F::Pair krows_pair(const T* th, const T* tl, int r0, int lane) {
+  typename F::Pair p;
+  p.h = F::template krows<D>(th, r0, lane);
+  if constexpr (F::kLo) p.l = F::template krows<D>(tl, r0, lane);
+  return p;
+}
+template <typename F, typename T>
+__device__ __forceinline__ typename F::Pair gload_pair(const T* h, const T* l, int64_t o) {
+  typename F::Pair p;
+  p.h = F::gload(h + o);
+  if constexpr (F::kLo) p.l = F::gload(l + o);
+  return p;
+}
+template <typename F>
+__device__ __forceinline__ typename F::Pair zero_pair() {
+  typename F::Pair p;
+  p.h = F::zero();
+  if constexpr (F::kLo) p.l = F::zero();
+  return p;
+}
+
+// x as a dtype pair: hi = T(x), lo = T(x - hi) (fp32: lo unused).
+template <typename T>
+__device__ __forceinline__ void store_pair(T* hi, T* lo, int64_t o, float x) {
+  const T h = (T)x;
+  hi[o] = h;
+  if constexpr (sizeof(T) == 2) lo[o] = (T)(x - to_f(h));
+}
+template <typename T>
+__device__ __forceinline__ float pair_value(const T* hi, const T* lo, int64_t o) {
+  if constexpr (sizeof(T) == 2) return to_f(hi[o]) + to_f(lo[o]);
+  return to_f(hi[o]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float x0, float x1, float x2, float x3) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{x0, x1, x2, x3};
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load4(const T* src, float* x) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(src);
+#pragma unroll
+    for (int i = 0; i < 4; i++) x[i] = (float)v[i];
+  } else {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+    for (int i = 0; i < 4; i++) x[i] = v[i];
+  }
+}
+
+// Stats of 32 latents (stat_pos order) for lane half hh: the 16 values of its result slots.
+__device__ __forceinline__ void load_stats16(const float* base, int hh, float* out) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(base + 16 * hh + 4 * q);
+#pragma unroll
+    for (int i = 0; i < 4; i++) out[4 * q + i] = v[i];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Latent-side kernel of one routing call (Appendix B.5, Eq. 46-49, the sums over tokens).
+//
+// Per 32-token x 32-latent tile of a wave, with the score tile C[token][latent] (lane = latent):
+//   l = X_n . Qr_m (log2 units), P = 2^(l - L), dP = W_n . Wr_m, dS = P (dP - c),
+//   acc1[d][m] += sum_n X[n][d] dS[n][m]        and, for decode, acc0[d][m] += sum_n W[n][d] P[n][m].
+// L and c are per token for decode (softmax over latents) and per latent for encode and synthesis
+// (softmax over tokens). Synthesis scores the normalized keys c*N0(S) (a pair) against the seeds and
+// takes dP = (c*N0(S)) . (G/c); the host scales acc1 by 1/sqrt(D) (decode, encode) or ln 2
+// (synthesis).
+//
+// Workgroup = NW waves, latent group of 32*NW latents; grid x enumerates (chunk, latent group) with
+// the groups of one chunk on the same XCD, y = b * H + h. The token tiles of a chunk pass through
+// LDS in stages of 64 tokens, double-buffered, the next stage's global loads issued before the
+// current stage's compute. Tokens past the chunk's end load as zeros and are masked out of P.
+template <typename T, int D, int CALL, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
+  using F = Frag<T>;
+  using Op = typename F::Op;
+  using Pair = typename F::Pair;
+  using Sw = Swz<T, D>;
+  constexpr int ST = kBwdStage;
+  constexpr int KB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int CH = 16 / sizeof(T), CPR = D / CH;
+  constexpr int NCH = ST * CPR;  // chunks per tensor per stage
+  constexpr bool DEC = CALL == kBwdDecode, SYN = CALL == kBwdSynthesis;
+  // Stage tiles: X and W (decode, encode), or the hi and lo parts of c*N0(S) (synthesis).
+  constexpr int NLOAD = SYN ? NCH : 2 * NCH;
+  constexpr int PER = (NLOAD + NT - 1) / NT;
+  constexpr int QRS = SYN ? D : kQRow<T> * D;  // elements per query row
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* xs = reinterpret_cast<T*>(smem);                          // [2][ST * D]
+  T* ws = xs + 2 * ST * D;                                     // [2][ST * D]: W, or the lo part of X
+  float* tst = reinterpret_cast<float*>(ws + 2 * ST * D);      // [2][2][ST] decode token stats
+
+  int chunk_id, lg;
+  if (a.nlg == 1) {
+    chunk_id = blockIdx.x;
+    lg = 0;
+  } else {
+    const int slot = blockIdx.x >> 3;
+    lg = slot % a.nlg;
+    chunk_id = (slot / a.nlg) * 8 + (blockIdx.x & 7);
+  }
+  if (chunk_id >= a.nchunk) return;  // padding workgroups of the XCD mapping (whole workgroup)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int bh = blockIdx.y;
+  const int64_t n_begin = (int64_t)chunk_id * a.chunk;
+  const int64_t n_end = (n_begin + a.chunk < a.N) ? n_begin + a.chunk : a.N;
+  const int nstage = (int)((n_end - n_begin + ST - 1) / ST);
+  const int lat0 = (lg * NW + wave) * 32;
+  const bool active = lat0 < a.Mp;
+  const int lrow = lat0 + (lane & 31);
+  const float c_scale = kLog2e * rsqrtf((float)D);
+
+  const T* xbase = reinterpret_cast<const T*>(a.X) + (int64_t)bh * a.N * D;
+  const T* wbase = SYN ? xbase : reinterpret_cast<const T*>(a.W) + (int64_t)bh * a.N * D;
+
+  // Latent operands (B of the score and dP products): lane l holds dims 16 kk + 8 (l / 32) .. + 7 of
+  // latent lrow. Synthesis: the seeds (exact); otherwise c*Q as a pair. Wr is always a pair.
+  Pair qb[KB], wb[KB];
+  float Ll = 0.f, Lc = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KB; kk++) {
+    qb[kk] = zero_pair<F>();
+    wb[kk] = zero_pair<F>();
+  }
+  if (active) {
+    const int64_t wo = ((int64_t)bh * a.Mp + lrow) * D;
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      if constexpr (SYN) {
+        if (lrow < a.M)
+          qb[kk].h = F::gload(reinterpret_cast<const T*>(a.Qr) + ((int64_t)(bh % a.H) * a.M + lrow) * D + 16 * kk + 8 * hh);
+      } else {
+        const T* q = reinterpret_cast<const T*>(a.Qr) + ((int64_t)bh * a.Mp + lrow) * QRS + 16 * kk + 8 * hh;
+        qb[kk].h = F::gload(q);
+        if constexpr (F::kLo) qb[kk].l = F::gload(q + D);
+      }
+      wb[kk] = gload_pair<F>(reinterpret_cast<const T*>(a.Wr), reinterpret_cast<const T*>(a.Wr_lo),
+                             wo + 16 * kk + 8 * hh);
+    }
+    if constexpr (!DEC) {
+      Ll = a.ll[(int64_t)bh * a.Mp + lrow];
+      Lc = a.lc[(int64_t)bh * a.Mp + lrow];
+    }
+  }
+
+  Chunk rg[PER];
+  float tsl = 0.f, tsc = 0.f;
+  auto load = [&](int stage) __attribute__((always_inline)) {
+    const int64_t s0 = n_begin + (int64_t)stage * ST;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int q = tid + i * NT;
+      Chunk v = {0u, 0u, 0u, 0u};
+      if (q < NLOAD) {
+        const bool isw = !SYN && q >= NCH;
+        const int qq = isw ? q - NCH : q;
+        const int64_t n = s0 + qq / CPR;
+        if (n < n_end) v = *reinterpret_cast<const Chunk*>((isw ? wbase : xbase) + n * D + (qq % CPR) * CH);
+      }
+      rg[i] = v;
+    }
+    if constexpr (DEC) {
+      if (tid < ST) {
+        const int64_t n = s0 + tid;
+        tsl = n < n_end ? a.tl[(int64_t)bh * a.N + n] : INFINITY;
+        tsc = n < n_end ? a.tc[(int64_t)bh * a.N + n] : 0.f;
+      }
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int q = tid + i * NT;
+      if constexpr (SYN) {
+        // c * N0 of the synthesis key row (Section 3.2, Eq. 5) as a pair: the row's CPR chunks sit
+        // in consecutive lanes.
+        float x[CH];
+        chunk_to_float<T>(rg[i], x);
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < CH; j++) ss += x[j] * x[j];
+        ss = group_sum<CPR>(ss);
+        const float sc = c_scale / sqrtf(ss * (1.0f / D) + kRmsEps);
+        float hi[CH], lo[CH];
+#pragma unroll
+        for (int j = 0; j < CH; j++) {
+          const float v = x[j] * sc;
+          hi[j] = to_f((T)v);
+          lo[j] = v - hi[j];
+        }
+        if (q < NLOAD) {
+          const int o = buf * ST * D + Sw::off(q / CPR, (q % CPR) * CH);
+          *reinterpret_cast<Chunk*>(xs + o) = float_to_chunk<T>(hi);
+          if constexpr (F::kLo) *reinterpret_cast<Chunk*>(ws + o) = float_to_chunk<T>(lo);
+        }
+      } else {
+        if (q < NLOAD) {
+          const bool isw = q >= NCH;
+          const int qq = isw ? q - NCH : q;
+          *reinterpret_cast<Chunk*>((isw ? ws : xs) + buf * ST * D + Sw::off(qq / CPR, (qq % CPR) * CH)) = rg[i];
+        }
+      }
+    }
+    if constexpr (DEC) {
+      if (tid < ST) {
+        const int p = stat_pos(tid);
+        tst[(2 * buf) * ST + p] = tsl;
+        tst[(2 * buf + 1) * ST + p] = tsc;
+      }
+    }
+  };
+
+  f32x16 acc0 = {}, acc1 = {};
+  auto compute = [&](int buf, int nvalid) __attribute__((always_inline)) {
+    const T* xt = xs + buf * ST * D;
+    const T* wt = ws + buf * ST * D;
+#pragma unroll
+    for (int sub = 0; sub < ST / 32; sub++) {
+      const int r0 = 32 * sub;
+      const int rr = r0 + (lane & 31);
+      f32x16 s = {}, dp = {};
+      if constexpr (SYN) {
+        Pair xa[KB];
+#pragma unroll
+        for (int kk = 0; kk < KB; kk++) {
+          xa[kk] = row_pair<F, D>(xt, wt, rr, 16 * kk + 8 * hh);
+          s = mma_pe<F>(xa[kk], qb[kk].h, s);
+          dp = mma_pp<F>(xa[kk], wb[kk], dp);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KB; kk++) {
+          hold<F>(s, xa[kk]);
+          hold<F>(dp, xa[kk]);
+        }
+      } else {
+        Op xa[KB], wa[KB];
+#pragma unroll
+        for (int kk = 0; kk < KB; kk++) {
+          xa[kk] = F::template row<D>(xt, rr, 16 * kk + 8 * hh);
+          wa[kk] = F::template row<D>(wt, rr, 16 * kk + 8 * hh);
+          s = mma_ep<F>(xa[kk], qb[kk], s);
+          dp = mma_ep<F>(wa[kk], wb[kk], dp);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KB; kk++) {
+          hold(s, xa[kk]);
+          hold(dp, wa[kk]);
+        }
+      }
+      float Lt[16], Ct[16];
+      if constexpr (DEC) {
+        load_stats16(tst + (2 * buf) * ST + r0, hh, Lt);
+        load_stats16(tst + (2 * buf + 1) * ST + r0, hh, Ct);
+      }
+      f32x16 P, dS;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        float p = exp2_fast(s[v] - (DEC ? Lt[v] : Ll));
+        if (nvalid < ST && r0 + row32(v, hh) >= nvalid) p = 0.f;
+        P[v] = p;
+        dS[v] = p * (dp[v] - (DEC ? Ct[v] : Lc));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const Pair dsp = F::split(dS, t);
+        if constexpr (SYN) {
+          const Pair xk = krows_pair<F, D>(xt, wt, r0 + 16 * t, lane);
+          acc1 = mma_pp<F>(xk, dsp, acc1);
+          hold<F>(acc1, xk);
+        } else {
+          const Op xk = F::template krows<D>(xt, r0 + 16 * t, lane);
+          acc1 = mma_ep<F>(xk, dsp, acc1);
+          hold(acc1, xk);
+        }
+        hold<F>(acc1, dsp);
+        if constexpr (DEC) {
+          const Op wk = F::template krows<D>(wt, r0 + 16 * t, lane);
+          const Pair pp = F::split(P, t);
+          acc0 = mma_ep<F>(wk, pp, acc0);
+          hold(acc0, wk);
+          hold<F>(acc0, pp);
+        }
+      }
+    }
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int stage = 0; stage < nstage; stage++) {
+    const int buf = stage & 1;
+    if (stage + 1 < nstage) load(stage + 1);
+    const int64_t left = n_end - (n_begin + (int64_t)stage * ST);
+    if (active) compute(buf, left < ST ? (int)left : ST);
+    if (stage + 1 < nstage) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // Result slot v of lane l: dim row32(v, l / 32) of latent lrow; four consecutive dims per store.
+  const int64_t prow = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp + lrow;
+#pragma unroll
+  for (int gq = 0; gq < 4; gq++) {
+    const int d0 = row32(4 * gq, hh);
+    if (d0 < D) {
+      *reinterpret_cast<f32x4*>(a.part1 + prow * D + d0) =
+          f32x4{acc1[4 * gq], acc1[4 * gq + 1], acc1[4 * gq + 2], acc1[4 * gq + 3]};
+      if constexpr (DEC)
+        *reinterpret_cast<f32x4*>(a.part0 + prow * D + d0) =
+            f32x4{acc0[4 * gq], acc0[4 * gq + 1], acc0[4 * gq + 2], acc0[4 * gq + 3]};
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Reductions. One thread per (latent, channel); blocks of 256 / D latent rows x D channels, so that
+// a row's D channels sit in consecutive lanes of one wave for the row sums.
+template <int D>
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < D; o <<= 1) v += shfl_xor(v, o);
+  return v;
+}
+
+// After the decode call: dZ = sum of the P^T dY partials (kept as a pair for the encode call), dQ_dec
+// = sum of the dS^T K partials over sqrt(D), and the encode call's c_m = <dZ_m, Z_m> with dZ as the
+// pair carries it.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_reduce_decode_kernel(BwdReduceArgs a) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int row = idx / D, d = idx % D;
+  if (row >= a.Mp) return;  // whole rows
+  const bool valid = row < a.M;
+  const int64_t cs = (int64_t)a.Mp * D;
+  const int64_t base = ((int64_t)bh * a.nchunk * a.Mp + row) * D + d;
+  float z = 0.f, q = 0.f;
+  if (valid) {
+    for (int c = 0; c < a.nchunk; c++) {
+      z += a.part0[base + c * cs];
+      q += a.part1[base + c * cs];
+    }
+    q *= rsqrtf((float)D);
+  }
+  const int64_t o = ((int64_t)bh * a.Mp + row) * D + d;
+  T* zh = reinterpret_cast<T*>(a.dZop);
+  T* zl = reinterpret_cast<T*>(a.dZop_lo);
+  store_pair<T>(zh, zl, o, z);
+  a.dZ32[o] = z;
+  a.dQdec[o] = q;
+  const float zr = pair_value<T>(zh, zl, o);
+  const float e = row_sum<D>(valid ? zr * a.Z32[((int64_t)bh * a.M + row) * D + d] : 0.f);
+  if (d == 0) a.ce[(int64_t)bh * a.Mp + row] = e;
+}
+
+// After the encode call: dQ = dQ_dec + dQ_enc; the gate Q = N0(Qf) + g Qd (Eq. 7) gives
+// dQf = N0'(Qf)^T dQ (per (b, h), summed over the batch later), the gate's <dQ, Qd> and the
+// synthesis call's cotangent G = g dQ (a pair G / c for the dP operand) with c_m = <G_m, Qd_m>
+// (G as the pair carries it).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_reduce_gate_kernel(BwdReduceArgs a) {
+  const int bh = blockIdx.y, h = bh % a.H;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int row = idx / D, d = idx % D;
+  if (row >= a.Mp) return;
+  const bool valid = row < a.M;
+  const int64_t cs = (int64_t)a.Mp * D;
+  const int64_t base = ((int64_t)bh * a.nchunk * a.Mp + row) * D + d;
+  const int64_t o = ((int64_t)bh * a.Mp + row) * D + d;
+  float q = 0.f;
+  if (valid) {
+    for (int c = 0; c < a.nchunk; c++) q += a.part1[base + c * cs];
+    q = a.dQdec[o] + q * rsqrtf((float)D);
+  }
+  const float f = valid ? to_f(reinterpret_cast<const T*>(a.Qf)[((int64_t)h * a.M + row) * D + d]) : 0.f;
+  const float ss = row_sum<D>(f * f);
+  const float tq = row_sum<D>(f * q);
+  const float r = 1.0f / sqrtf(ss * (1.0f / D) + kRmsEps);
+  a.dQf_bh[o] = valid ? r * q - r * r * r * f * tq * (1.0f / D) : 0.f;
+  const float qd = valid ? a.Qd32[((int64_t)bh * a.M + row) * D + d] : 0.f;
+  const float rd = row_sum<D>(q * qd);
+  const float gv = a.g[h];
+  const float c_scale = kLog2e * rsqrtf((float)D);
+  T* gh = reinterpret_cast<T*>(a.Gop);
+  T* gl = reinterpret_cast<T*>(a.Gop_lo);
+  store_pair<T>(gh, gl, o, valid ? gv * q / c_scale : 0.f);
+  const float cg = row_sum<D>(pair_value<T>(gh, gl, o) * qd) * c_scale;
+  if (d == 0) {
+    a.cs[(int64_t)bh * a.Mp + row] = valid ? cg : 0.f;
+    a.rowdot[(int64_t)bh * a.Mp + row] = valid ? rd : 0.f;
+  }
+}
+
+// After the synthesis call: the cotangents of the parameters shared over the batch. dQseed is the
+// sum over batch and chunks of the dS^T (c N0(S)) partials times ln 2 (= 1/(c sqrt(D))); dQf the batch
+// sum of the per-(b, h) values; dg = sum over the batch of <dQ, Qd>. Grid x covers the M x D
+// entries of one head (y); block 0 of each head also sums dg.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_reduce_synthesis_kernel(BwdReduceArgs a) {
+  const int h = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int row = idx / D, d = idx % D;
+  if (blockIdx.x == 0) {
+    __shared__ float part[4];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < a.B * a.M; i += 256) {
+      const int b = i / a.M, m = i % a.M;
+      s += a.rowdot[(int64_t)(b * a.H + h) * a.Mp + m];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s += shfl_xor(s, o);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) a.dg[h] = (part[0] + part[1]) + (part[2] + part[3]);
+  }
+  if (row >= a.M) return;
+  const int64_t cs = (int64_t)a.Mp * D;
+  float qs = 0.f, qf = 0.f;
+  for (int b = 0; b < a.B; b++) {
+    const int64_t bh = (int64_t)b * a.H + h;
+    const int64_t base = (bh * a.nchunk * a.Mp + row) * D + d;
+    for (int c = 0; c < a.nchunk; c++) qs += a.part1[base + c * cs];
+    qf += a.dQf_bh[(bh * a.Mp + row) * D + d];
+  }
+  const int64_t o = ((int64_t)h * a.M + row) * D + d;
+  reinterpret_cast<T*>(a.dQseed)[o] = (T)(qs * kLn2);
+  reinterpret_cast<T*>(a.dQf)[o] = (T)qf;
+}
+
+// ------------------------------------------------------------------------------------------
+// Zc = Z - mean_m Z per (b, h), as a pair: one block per (b, h), the column sums through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_center_kernel(BwdCenterArgs a) {
+  constexpr int RPB = 256 / D;  // rows per pass
+  __shared__ float part[256];
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x % D, r0 = threadIdx.x / D;
+  const float* z = a.Z32 + (int64_t)bh * a.M * D;
+  float s = 0.f;
+  for (int m = r0; m < a.M; m += RPB) s += z[(int64_t)m * D + d];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  float mean = 0.f;
+  for (int r = 0; r < RPB; r++) mean += part[r * D + d];
+  mean /= (float)a.M;
+  T* oh = reinterpret_cast<T*>(a.Zc) + (int64_t)bh * a.Mp * D;
+  T* ol = reinterpret_cast<T*>(a.Zc_lo) + (int64_t)bh * a.Mp * D;
+  for (int m = r0; m < a.Mp; m += RPB)
+    store_pair<T>(oh, ol, (int64_t)m * D + d, m < a.M ? z[(int64_t)m * D + d] - mean : 0.f);
+}
+
+// Latent tensors of one (batch, head) as swizzled LDS tiles: rows of `stride` elements from sh (and,
+// for a bf16 pair, the lo part from sl into tl); rows >= rows_valid are zero.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void fill_tile(T* th, T* tl, const T* sh, const T* sl, int Mp, int stride, int rows_valid) {
+  using Sw = Swz<T, D>;
+  constexpr int CH = 16 / sizeof(T), CPR = D / CH;
+  for (int q = threadIdx.x; q < Mp * CPR; q += NT) {
+    const int row = q / CPR, part = q % CPR;
+    const int o = Sw::off(row, part * CH);
+    const bool ok = row < rows_valid;
+    const int64_t so = (int64_t)row * stride + part * CH;
+    *reinterpret_cast<Chunk*>(th + o) = ok ? *reinterpret_cast<const Chunk*>(sh + so) : Chunk{0u, 0u, 0u, 0u};
+    if (tl != nullptr)
+      *reinterpret_cast<Chunk*>(tl + o) = ok ? *reinterpret_cast<const Chunk*>(sl + so) : Chunk{0u, 0u, 0u, 0u};
+  }
+}
+template <int NT>
+__device__ __forceinline__ void fill_stats(float* sl, float* sc, const float* l, const float* c, int Mp) {
+  for (int m = threadIdx.x; m < Mp; m += NT) {
+    const int p = stat_pos(m);
+    sl[p] = l[m];
+    sc[p] = c[m];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode call, per token (Section 3.2 Eq. 8, the softmax over latents; Appendix B.5 for the
+// cotangent). With l_nm = K_n . c Q_m and dP_nm = dY_n . Zc_m (c*Q and Zc as pairs):
+//   pass 1 (online, running maximum per lane half):  L_n = log2 sum_m 2^(l_nm),
+//                                                     c_n = sum_m 2^(l_nm - L_n) dP_nm;
+//   pass 2:  dK_dec,n = (1/sqrt(D)) sum_m P_nm (dP_nm - c_n) Q_m,  kept in fp32 for the encode kernel.
+// LDS holds c*Q and Zc (pairs).
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs a) {
+  using F = Frag<T>;
+  using Op = typename F::Op;
+  using Pair = typename F::Pair;
+  constexpr int KB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int NP = F::kLo ? 2 : 1;  // tiles per pair
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;
+  T* qh = reinterpret_cast<T*>(smem);  // [Mp][D] c*Q hi
+  T* ql = qh + Mp * D;                  // lo (bf16)
+  T* zh = qh + NP * Mp * D;             // [Mp][D] Zc hi
+  T* zl = zh + Mp * D;                  // lo (bf16)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int bh = blockIdx.y;
+  {
+    const T* qsrc = reinterpret_cast<const T*>(a.Qrows) + (int64_t)bh * Mp * kQRow<T> * D;
+    fill_tile<T, D, NT>(qh, F::kLo ? ql : nullptr, qsrc, qsrc + D, Mp, kQRow<T> * D, Mp);
+    fill_tile<T, D, NT>(zh, F::kLo ? zl : nullptr, reinterpret_cast<const T*>(a.Zc) + (int64_t)bh * Mp * D,
+                        reinterpret_cast<const T*>(a.Zc_lo) + (int64_t)bh * Mp * D, Mp, D, Mp);
+  }
+  __syncthreads();
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const int nlb = Mp / 32;
+  const bool ragged = (a.M & 31) != 0;
+  const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
+  const T* ybase = reinterpret_cast<const T*>(a.dY) + (int64_t)bh * a.N * D;
+
+  for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
+    const int64_t tok = base + (lane & 31);
+    const bool valid = tok < t_end;
+    Op kb[KB], yb[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      const int64_t o = tok * D + 16 * kk + 8 * hh;
+      kb[kk] = valid ? F::gload(kbase + o) : F::zero();
+      yb[kk] = valid ? F::gload(ybase + o) : F::zero();
+    }
+    // Logits and dP of latent block lb (C[latent][token], lane = token), masked past M.
+    auto scores = [&](int lb, f32x16& E, f32x16& dP) __attribute__((always_inline)) {
+      const int r = 32 * lb + (lane & 31);
+      Pair qa[KB], za[KB];
+      E = f32x16{};
+      dP = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        qa[kk] = row_pair<F, D>(qh, ql, r, 16 * kk + 8 * hh);
+        za[kk] = row_pair<F, D>(zh, zl, r, 16 * kk + 8 * hh);
+        E = mma_pe<F>(qa[kk], kb[kk], E);
+        dP = mma_pe<F>(za[kk], yb[kk], dP);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        hold<F>(E, qa[kk]);
+        hold(E, kb[kk]);
+        hold<F>(dP, za[kk]);
+        hold(dP, yb[kk]);
+      }
+      if (ragged && lb == nlb - 1) {
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          if (32 * lb + row32(v, hh) >= a.M) E[v] = -INFINITY;
+      }
+    };
+
+    float mrun = -INFINITY, l = 0.f, u = 0.f;
+    for (int lb = 0; lb < nlb; lb++) {
+      f32x16 E, dP;
+      scores(lb, E, dP);
+      float bm = E[0];
+#pragma unroll
+      for (int v = 1; v < 16; v++) bm = fmaxf(bm, E[v]);
+      const float mn = fmaxf(mrun, bm);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      const float sc = exp2_fast(mrun - ms);
+      l *= sc;
+      u *= sc;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const float p = exp2_fast(E[v] - ms);
+        l += p;
+        u += p * dP[v];
+      }
+      mrun = mn;
+    }
+    // The token's other 16 latents of every block are in lane l ^ 32.
+    const float mo = shfl_xor(mrun, 32), lo = shfl_xor(l, 32), uo = shfl_xor(u, 32);
+    const float mt = fmaxf(mrun, mo);
+    const float mts = mt == -INFINITY ? 0.f : mt;
+    const float wa = exp2_fast(mrun - mts), wb = exp2_fast(mo - mts);
+    const float lt = l * wa + lo * wb;
+    const float Ld = mts + log2f(lt);
+    const float cd = (u * wa + uo * wb) / lt;
+    if (valid && hh == 0) {
+      a.tl[(int64_t)bh * a.N + tok] = Ld;
+      a.tc[(int64_t)bh * a.N + tok] = cd;
+    }
+
+    f32x16 accK = {};
+    for (int lb = 0; lb < nlb; lb++) {
+      f32x16 E, dP;
+      scores(lb, E, dP);
+      f32x16 dS;
+#pragma unroll
+      for (int v = 0; v < 16; v++) dS[v] = exp2_fast(E[v] - Ld) * (dP[v] - cd);
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const Pair qk = krows_pair<F, D>(qh, ql, 32 * lb + 16 * t, lane);
+        const Pair sk = F::split(dS, t);
+        accK = mma_pp<F>(qk, sk, accK);
+        hold<F>(accK, qk);
+        hold<F>(accK, sk);
+      }
+    }
+    if (valid) {
+      // dK_dec = (1/sqrt(D)) dS Q = ln 2 * dS (c*Q); slot v holds dim row32(v, l / 32).
+      float* dk = a.dKdec + ((int64_t)bh * a.N + tok) * D;
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int d0 = row32(4 * gq, hh);
+        if (d0 < D)
+          *reinterpret_cast<f32x4*>(dk + d0) = f32x4{accK[4 * gq] * kLn2, accK[4 * gq + 1] * kLn2,
+                                                    accK[4 * gq + 2] * kLn2, accK[4 * gq + 3] * kLn2};
+      }
+    }
+  }
+}
+
+// Encode call, per token (Appendix B.5, the sums over latents): with P_mn = 2^(l_mn - L_m) and
+// dP_mn = dZ_m . V_n,
+//   dK_n = dK_dec,n + (1/sqrt(D)) sum_m P_mn (dP_mn - c_m) Q_m,   dV_n = sum_m P_mn dZ_m.
+// LDS holds c*Q and dZ (pairs) and the per-latent L and c. Score tiles are C[latent][token]
+// (lane = token); the products over latents are computed transposed, R[d][token], so that each lane
+// ends with 16 dims of its own token.
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs a) {
+  using F = Frag<T>;
+  using Op = typename F::Op;
+  using Pair = typename F::Pair;
+  constexpr int KB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int NP = F::kLo ? 2 : 1;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;
+  T* qh = reinterpret_cast<T*>(smem);  // [Mp][D] c*Q hi
+  T* ql = qh + Mp * D;                  // lo (bf16)
+  T* zh = qh + NP * Mp * D;             // [Mp][D] dZ hi
+  T* zl = zh + Mp * D;                  // lo (bf16)
+  float* sl = reinterpret_cast<float*>(zh + NP * Mp * D);  // [Mp] L_enc, stat_pos order
+  float* sc = sl + Mp;                                      // [Mp] c_enc
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int bh = blockIdx.y;
+  {
+    const T* qsrc = reinterpret_cast<const T*>(a.Qrows) + (int64_t)bh * Mp * kQRow<T> * D;
+    fill_tile<T, D, NT>(qh, F::kLo ? ql : nullptr, qsrc, qsrc + D, Mp, kQRow<T> * D, Mp);
+    fill_tile<T, D, NT>(zh, F::kLo ? zl : nullptr, reinterpret_cast<const T*>(a.dZop) + (int64_t)bh * Mp * D,
+                        reinterpret_cast<const T*>(a.dZ_lo) + (int64_t)bh * Mp * D, Mp, D, Mp);
+    fill_stats<NT>(sl, sc, a.lenc + (int64_t)bh * Mp, a.ce + (int64_t)bh * Mp, Mp);
+  }
+  __syncthreads();
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const int nlb = Mp / 32;
+  const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
+  const T* vbase = reinterpret_cast<const T*>(a.V) + (int64_t)bh * a.N * D;
+
+  for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
+    const int64_t tok = base + (lane & 31);
+    const bool valid = tok < t_end;
+    Op kb[KB], vb[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      const int64_t o = tok * D + 16 * kk + 8 * hh;
+      kb[kk] = valid ? F::gload(kbase + o) : F::zero();
+      vb[kk] = valid ? F::gload(vbase + o) : F::zero();
+    }
+    f32x16 accK = {}, accV = {};
+    for (int lb = 0; lb < nlb; lb++) {
+      const int r = 32 * lb + (lane & 31);
+      Pair qa[KB], za[KB];
+      f32x16 E = {}, dP = {};
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        qa[kk] = row_pair<F, D>(qh, ql, r, 16 * kk + 8 * hh);
+        za[kk] = row_pair<F, D>(zh, zl, r, 16 * kk + 8 * hh);
+        E = mma_pe<F>(qa[kk], kb[kk], E);
+        dP = mma_pe<F>(za[kk], vb[kk], dP);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        hold<F>(E, qa[kk]);
+        hold(E, kb[kk]);
+        hold<F>(dP, za[kk]);
+        hold(dP, vb[kk]);
+      }
+      // Latents past M: zero rows of c*Q and dZ, L = +inf, c = 0, so P and dS vanish there.
+      float Le[16], Ce[16];
+      load_stats16(sl + 32 * lb, hh, Le);
+      load_stats16(sc + 32 * lb, hh, Ce);
+      f32x16 P, dS;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const float p = exp2_fast(E[v] - Le[v]);
+        P[v] = p;
+        dS[v] = p * (dP[v] - Ce[v]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const Pair qk = krows_pair<F, D>(qh, ql, 32 * lb + 16 * t, lane);
+        const Pair sk = F::split(dS, t);
+        accK = mma_pp<F>(qk, sk, accK);
+        hold<F>(accK, qk);
+        hold<F>(accK, sk);
+        const Pair zk = krows_pair<F, D>(zh, zl, 32 * lb + 16 * t, lane);
+        const Pair pk = F::split(P, t);
+        accV = mma_pp<F>(zk, pk, accV);
+        hold<F>(accV, zk);
+        hold<F>(accV, pk);
+      }
+    }
+    if (valid) {
+      // dK = dK_dec + (1/sqrt(D)) dS Q = dK_dec + ln 2 * dS (c*Q).
+      const int64_t to = ((int64_t)bh * a.N + tok) * D;
+      T* dk = reinterpret_cast<T*>(a.dK) + to;
+      T* dv = reinterpret_cast<T*>(a.dV) + to;
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int d0 = row32(4 * gq, hh);
+        if (d0 < D) {
+          const f32x4 kd = *reinterpret_cast<const f32x4*>(a.dKdec + to + d0);
+          store4<T>(dk + d0, kd[0] + accK[4 * gq] * kLn2, kd[1] + accK[4 * gq + 1] * kLn2,
+                    kd[2] + accK[4 * gq + 2] * kLn2, kd[3] + accK[4 * gq + 3] * kLn2);
+          store4<T>(dv + d0, accV[4 * gq], accV[4 * gq + 1], accV[4 * gq + 2], accV[4 * gq + 3]);
+        }
+      }
+    }
+  }
+}
+
+// Synthesis call and N0, per token (Section 3.2, Eq. 5-6): with the seeds Qseed as queries and the
+// normalized keys Sn = N0(S) as keys and values,
+//   dSn_n = (1/sqrt(D)) sum_m dS[m][n] Qseed_m + sum_m P[m][n] G_m,   dS = N0'(S)^T dSn,
+// where N0'(s)^T u = r u - r^3 s mean(s * u), r = (mean(s^2) + eps)^(-1/2). LDS holds the seeds, G / c
+// (a pair) and the per-latent L and c of the call.
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenArgs a) {
+  using F = Frag<T>;
+  using Op = typename F::Op;
+  using Pair = typename F::Pair;
+  constexpr int KB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int NP = F::kLo ? 2 : 1;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;
+  T* qs = reinterpret_cast<T*>(smem);  // [Mp][D] seeds (rows >= M zero)
+  T* gh = qs + Mp * D;                  // [Mp][D] G / c hi
+  T* gl = gh + Mp * D;                  // lo (bf16)
+  float* sl = reinterpret_cast<float*>(gh + NP * Mp * D);  // [Mp] L_syn, stat_pos order
+  float* sc = sl + Mp;                                      // [Mp] c_syn
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int bh = blockIdx.y, h = bh % a.H;
+  {
+    const T* qsrc = reinterpret_cast<const T*>(a.Qseed) + (int64_t)h * a.M * D;
+    fill_tile<T, D, NT>(qs, nullptr, qsrc, qsrc, Mp, D, a.M);
+    fill_tile<T, D, NT>(gh, F::kLo ? gl : nullptr, reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D,
+                        reinterpret_cast<const T*>(a.G_lo) + (int64_t)bh * Mp * D, Mp, D, Mp);
+    fill_stats<NT>(sl, sc, a.lsyn + (int64_t)bh * Mp, a.cs + (int64_t)bh * Mp, Mp);
+  }
+  __syncthreads();
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const int nlb = Mp / 32;
+  const float c_scale = kLog2e * rsqrtf((float)D);
+  const T* sbase = reinterpret_cast<const T*>(a.S) + (int64_t)bh * a.N * D;
+
+  for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
+    const int64_t tok = base + (lane & 31);
+    const bool valid = tok < t_end;
+    // c * N0(S) of the lane's token as a pair: dims 16 kk + 8 (l / 32) .. + 7 here, the rest in
+    // lane l ^ 32.
+    float x[KB][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      const Op raw = valid ? F::gload(sbase + tok * D + 16 * kk + 8 * hh) : F::zero();
+      F::to_float(raw, x[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss += x[kk][e] * x[kk][e];
+    }
+    ss += shfl_xor(ss, 32);
+    const float rn = 1.0f / sqrtf(ss * (1.0f / D) + kRmsEps);
+    Pair sb[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) y[e] = x[kk][e] * (rn * c_scale);
+      sb[kk] = F::split8(y);
+    }
+    f32x16 accA = {}, accB = {};
+    for (int lb = 0; lb < nlb; lb++) {
+      const int r = 32 * lb + (lane & 31);
+      Op qa[KB];
+      Pair ga[KB];
+      f32x16 A = {}, dP = {};
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        qa[kk] = F::template row<D>(qs, r, 16 * kk + 8 * hh);
+        ga[kk] = row_pair<F, D>(gh, gl, r, 16 * kk + 8 * hh);
+        A = mma_ep<F>(qa[kk], sb[kk], A);
+        dP = mma_pp<F>(ga[kk], sb[kk], dP);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        hold(A, qa[kk]);
+        hold<F>(A, sb[kk]);
+        hold<F>(dP, ga[kk]);
+        hold<F>(dP, sb[kk]);
+      }
+      float Ls[16], Cs[16];
+      load_stats16(sl + 32 * lb, hh, Ls);
+      load_stats16(sc + 32 * lb, hh, Cs);
+      f32x16 P, dS;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const float p = exp2_fast(A[v] - Ls[v]);
+        P[v] = p;
+        dS[v] = p * (dP[v] - Cs[v]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const Op qk = F::template krows<D>(qs, 32 * lb + 16 * t, lane);
+        const Pair sk = F::split(dS, t);
+        accA = mma_ep<F>(qk, sk, accA);
+        hold(accA, qk);
+        hold<F>(accA, sk);
+        const Pair gk = krows_pair<F, D>(gh, gl, 32 * lb + 16 * t, lane);
+        const Pair pk = F::split(P, t);
+        accB = mma_pp<F>(gk, pk, accB);
+        hold<F>(accB, gk);
+        hold<F>(accB, pk);
+      }
+    }
+    // dSn in slot v: dim row32(v, l / 32) of the lane's token; with S at the same dims, the N0
+    // backward needs one sum over the token's D dims (this lane's and lane l ^ 32's).
+    const float s_scale = rsqrtf((float)D);
+    float dsn[16], sv[16];
+    float t = 0.f;
+#pragma unroll
+    for (int gq = 0; gq < 4; gq++) {
+      const int d0 = row32(4 * gq, hh);
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (d0 < D && valid) load4<T>(sbase + tok * D + d0, s4);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int v = 4 * gq + i;
+        dsn[v] = accA[v] * s_scale + accB[v] * c_scale;
+        sv[v] = s4[i];
+        if (d0 < D) t += sv[v] * dsn[v];
+      }
+    }
+    t += shfl_xor(t, 32);
+    if (valid) {
+      T* ds = reinterpret_cast<T*>(a.dS) + ((int64_t)bh * a.N + tok) * D;
+      const float r3 = rn * rn * rn * t * (1.0f / D);
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int d0 = row32(4 * gq, hh);
+        if (d0 < D) {
+          const int v = 4 * gq;
+          store4<T>(ds + d0, rn * dsn[v] - r3 * sv[v], rn * dsn[v + 1] - r3 * sv[v + 1],
+                    rn * dsn[v + 2] - r3 * sv[v + 2], rn * dsn[v + 3] - r3 * sv[v + 3]);
+        }
+      }
+    }
+  }
+}
+
+// Zero fill (a kernel rather than a memset node, so that the call can be captured in a graph).
+__global__ __launch_bounds__(256) void bwd_zero_kernel(uint32_t* p, int64_t words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < words) p[i] = 0u;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// Launchers.
+
+hipError_t launch_bwd_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+template <typename F>
+static hipError_t allow_lds_bwd(F* fn, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_center_t(const BwdCenterArgs& a, int BH, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_center_kernel<T, D>), dim3(BH), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, hipStream_t st) {
+  if (dtype == 1) return D == 32 ? launch_bwd_center_t<bf16, 32>(a, BH, st) : launch_bwd_center_t<bf16, 16>(a, BH, st);
+  return D == 32 ? launch_bwd_center_t<float, 32>(a, BH, st) : launch_bwd_center_t<float, 16>(a, BH, st);
+}
+
+template <typename T, int D, int CALL, int NW>
+static hipError_t launch_bwd_latent_t(const BwdLatentArgs& a, int gx, int BH, hipStream_t st) {
+  const size_t lds = (size_t)4 * kBwdStage * D * sizeof(T) + (CALL == kBwdDecode ? 4 * kBwdStage * sizeof(float) : 0);
+  hipError_t e = allow_lds_bwd(bwd_latent_kernel<T, D, CALL, NW>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_latent_kernel<T, D, CALL, NW>), dim3(gx, BH), dim3(NW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int CALL>
+static hipError_t launch_bwd_latent_c(const BwdLatentArgs& a, int nw, int gx, int BH, hipStream_t st) {
+  return nw == 8 ? launch_bwd_latent_t<T, D, CALL, 8>(a, gx, BH, st) : launch_bwd_latent_t<T, D, CALL, 4>(a, gx, BH, st);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_latent_d(const BwdLatentArgs& a, int call, int nw, int gx, int BH, hipStream_t st) {
+  switch (call) {
+    case kBwdDecode: return launch_bwd_latent_c<T, D, kBwdDecode>(a, nw, gx, BH, st);
+    case kBwdEncode: return launch_bwd_latent_c<T, D, kBwdEncode>(a, nw, gx, BH, st);
+    default: return launch_bwd_latent_c<T, D, kBwdSynthesis>(a, nw, gx, BH, st);
+  }
+}
+
+hipError_t launch_bwd_latent(const BwdLatentArgs& a, int dtype, int D, int call, int nw, int grid_x, int BH,
+                             hipStream_t st) {
+  if (dtype == 1)
+    return D == 32 ? launch_bwd_latent_d<bf16, 32>(a, call, nw, grid_x, BH, st)
+                   : launch_bwd_latent_d<bf16, 16>(a, call, nw, grid_x, BH, st);
+  return D == 32 ? launch_bwd_latent_d<float, 32>(a, call, nw, grid_x, BH, st)
+                 : launch_bwd_latent_d<float, 16>(a, call, nw, grid_x, BH, st);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_reduce_t(const BwdReduceArgs& a, int call, int BH, hipStream_t st) {
+  if (call == kBwdSynthesis) {
+    const unsigned gx = (unsigned)((a.M * D + 255) / 256);
+    hipLaunchKernelGGL((bwd_reduce_synthesis_kernel<T, D>), dim3(gx, a.H), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  const unsigned gx = (unsigned)((a.Mp * D + 255) / 256);
+  if (call == kBwdDecode)
+    hipLaunchKernelGGL((bwd_reduce_decode_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_reduce_gate_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const BwdReduceArgs& a, int dtype, int D, int call, int BH, hipStream_t st) {
+  if (dtype == 1) return D == 32 ? launch_bwd_reduce_t<bf16, 32>(a, call, BH, st) : launch_bwd_reduce_t<bf16, 16>(a, call, BH, st);
+  return D == 32 ? launch_bwd_reduce_t<float, 32>(a, call, BH, st) : launch_bwd_reduce_t<float, 16>(a, call, BH, st);
+}
+
+template <typename T, int D>
+static size_t bwd_token_lds_t(int Mp, int kind) {
+  constexpr size_t NP = sizeof(T) == 2 ? 2 : 1;  // tiles per pair
+  const size_t tile = (size_t)Mp * D * sizeof(T), stats = 2 * (size_t)Mp * sizeof(float);
+  switch (kind) {
+    case kBwdTokDecode: return 2 * NP * tile;
+    case kBwdTokEncode: return 2 * NP * tile + stats;
+    default: return (1 + NP) * tile + stats;
+  }
+}
+
+size_t bwd_token_lds_bytes(int dtype, int D, int Mp, int kind) {
+  if (dtype == 1) return D == 32 ? bwd_token_lds_t<bf16, 32>(Mp, kind) : bwd_token_lds_t<bf16, 16>(Mp, kind);
+  return D == 32 ? bwd_token_lds_t<float, 32>(Mp, kind) : bwd_token_lds_t<float, 16>(Mp, kind);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_token_t(const BwdTokenArgs& a, int kind, int gx, int BH, hipStream_t st) {
+  constexpr int NW = kBwdTokenWaves;
+  const size_t lds = bwd_token_lds_t<T, D>(a.Mp, kind);
+  auto go = [&](auto* fn) {
+    hipError_t e = allow_lds_bwd(fn, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(gx, BH), dim3(NW * 64), lds, st, a);
+    return hipGetLastError();
+  };
+  switch (kind) {
+    case kBwdTokDecode: return go(bwd_token_decode_kernel<T, D, NW>);
+    case kBwdTokEncode: return go(bwd_token_encode_kernel<T, D, NW>);
+    default: return go(bwd_token_synthesis_kernel<T, D, NW>);
+  }
+}
+
+hipError_t launch_bwd_token(const BwdTokenArgs& a, int dtype, int D, int kind, int grid_x, int BH,
+                            hipStream_t st) {
+  if (dtype == 1)
+    return D == 32 ? launch_bwd_token_t<bf16, 32>(a, kind, grid_x, BH, st)
+                   : launch_bwd_token_t<bf16, 16>(a, kind, grid_x, BH, st);
+  return D == 32 ? launch_bwd_token_t<float, 32>(a, kind, grid_x, BH, st)
+                 : launch_bwd_token_t<float, 16>(a, kind, grid_x, BH, st);
+}
+
+}  // namespace flarepp

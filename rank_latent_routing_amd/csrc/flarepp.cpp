@@ -22,10 +22,14 @@ namespace {
 
 using flarepp::kStage;
 
-constexpr int kVersion = 200;  // 0.2.0
-constexpr int kNumKinds = 6;
+constexpr int kVersion = 300;  // 0.3.0
+constexpr int kNumKinds = 16;
 const char* const kKindNames[kNumKinds] = {"synthesis_partial", "merge_gate", "encode_partial",
-                                           "merge", "decode", "query_prep"};
+                                           "merge", "decode", "query_prep",
+                                           "bwd_center", "bwd_token_decode", "bwd_latent_decode",
+                                           "bwd_reduce_decode", "bwd_latent_encode", "bwd_reduce_gate",
+                                           "bwd_latent_synthesis", "bwd_reduce_synthesis",
+                                           "bwd_token_encode", "bwd_token_synthesis"};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -196,13 +200,21 @@ int validate_pointers(const void* K, const void* V, const void* S, const void* Q
   return FLAREPP_OK;
 }
 
+// Softmax normalizers the forward kernels leave for the backward pass (log2 units; null: not kept).
+struct Saved {
+  float* lsyn = nullptr;  // [BH][Mp32] synthesis, per latent
+  float* lenc = nullptr;  // [BH][Mp32] encode, per latent
+  bool exact = false;     // split-N partials on the exact (hi/lo, running maximum) path
+  bool no_decode = false; // stop after the encode merge
+};
+
 // Encode partials, merge and decode on the routing-query rows already in the workspace.
 int enqueue_routing(const void* K, const void* V, int64_t N, int M, int D, int dtype, void* out, float* dZ,
-                    void* ws, const Plan& p, hipStream_t st);
+                    void* ws, const Plan& p, hipStream_t st, const Saved& sv = Saved());
 
 int enqueue(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
             int B, int H, int64_t N, int M, int D, int dtype, void* out, float* dQd, float* dQ, float* dZ,
-            void* ws, const Plan& p, hipStream_t st) {
+            void* ws, const Plan& p, hipStream_t st, const Saved& sv = Saved()) {
   char* w = static_cast<char*>(ws);
   float* acc = reinterpret_cast<float*>(w + p.off_acc);
   float* pl = reinterpret_cast<float*>(w + p.off_l);
@@ -214,21 +226,22 @@ int enqueue(const void* K, const void* V, const void* S, const void* Qseed, cons
   flarepp::PartialArgs pa{};
   pa.K = S; pa.V = S; pa.Q = Qseed; pa.H = H; pa.Mq = M; pa.Mp = p.Mp16; pa.N = N;
   pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
-  pa.force_exact = g_force_exact.load(); pa.part_l = pl; pa.part_m = pm;
+  pa.force_exact = (g_force_exact.load() || sv.exact) ? 1 : 0; pa.part_l = pl; pa.part_m = pm;
   if (run_kernel(0, st, [&] { return flarepp::launch_partial(pa, dtype, D, true, p.part_plan, gx_part, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
   flarepp::MergeArgs ma{};
   ma.part_acc = acc; ma.part_l = pl; ma.part_m = pm; ma.nchunk = p.nchunk; ma.Mp = p.Mp16; ma.M = M;
   ma.Mout = p.Mp32; ma.H = H; ma.Qf = Qf; ma.g = g; ma.out = qbuf; ma.dbg_qd = dQd; ma.dbg_out = dQ;
+  ma.lse = sv.lsyn;
   if (run_kernel(1, st, [&] { return flarepp::launch_merge(ma, dtype, D, true, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
-  return enqueue_routing(K, V, N, M, D, dtype, out, dZ, ws, p, st);
+  return enqueue_routing(K, V, N, M, D, dtype, out, dZ, ws, p, st, sv);
 }
 
 int enqueue_routing(const void* K, const void* V, int64_t N, int M, int D, int dtype, void* out, float* dZ,
-                    void* ws, const Plan& p, hipStream_t st) {
+                    void* ws, const Plan& p, hipStream_t st, const Saved& sv) {
   char* w = static_cast<char*>(ws);
   float* acc = reinterpret_cast<float*>(w + p.off_acc);
   float* pl = reinterpret_cast<float*>(w + p.off_l);
@@ -239,15 +252,17 @@ int enqueue_routing(const void* K, const void* V, int64_t N, int M, int D, int d
   flarepp::PartialArgs pa{};
   pa.K = K; pa.V = V; pa.Q = qbuf; pa.H = p.H; pa.Mq = p.Mp32; pa.Mp = p.Mp16; pa.N = N;
   pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
-  pa.force_exact = g_force_exact.load(); pa.part_l = pl; pa.part_m = pm;
+  pa.force_exact = (g_force_exact.load() || sv.exact) ? 1 : 0; pa.part_l = pl; pa.part_m = pm;
   if (run_kernel(2, st, [&] { return flarepp::launch_partial(pa, dtype, D, false, p.part_plan, p.part_gx, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
   flarepp::MergeArgs ma{};
   ma.part_acc = acc; ma.part_l = pl; ma.part_m = pm; ma.nchunk = p.nchunk; ma.Mp = p.Mp16; ma.M = M;
   ma.Mout = p.Mp32; ma.H = p.H; ma.Qf = nullptr; ma.g = nullptr; ma.out = zbuf; ma.dbg_qd = nullptr; ma.dbg_out = dZ;
+  ma.lse = sv.lenc;
   if (run_kernel(3, st, [&] { return flarepp::launch_merge(ma, dtype, D, false, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
+  if (sv.no_decode) return FLAREPP_OK;
 
   flarepp::DecodeArgs da{};
   da.K = K; da.Q = qbuf; da.Z = zbuf; da.out = out; da.N = N; da.M = M; da.Mp = p.Mp32; da.tokens_per_wg = p.dec_tpw;
@@ -319,6 +334,214 @@ int flare_common(const void* K, const void* V, const void* Q, int B, int H, int6
   return rc;
 }
 
+// ---- Backward pass
+//
+// The synthesis and encode calls are recomputed on the exact path with their normalizers kept, Z
+// is centered, and the decode kernel forms every token's statistics and the decode call's part of
+// dK; then, per routing call in reverse order (Appendix B.5, Eq. 46-49): the latent-side partials
+// and their reduction for the decode call (dZ, dQ_dec) and the encode call (dQ_enc, then the gate),
+// the synthesis call (dQseed and the batch sums), and the token-side kernels of the encode call
+// (dK, dV) and the synthesis call (dS).
+struct BwdPlan {
+  Plan f;
+  int Mp = 0;
+  int lat_nw = 4, lat_nlg = 1, lat_nchunk = 0, lat_gx = 0;
+  int64_t lat_chunk = 0;
+  int tok_gx = 0;
+  int64_t tok_tpw = 0;
+  size_t off_qd = 0, off_z32 = 0, off_lsyn = 0, off_lenc = 0, off_zc = 0, off_zc_lo = 0, off_ldec = 0;
+  size_t off_cd = 0, off_dkdec = 0, off_p0 = 0, off_p1 = 0, off_dz32 = 0, off_dzop = 0, off_dzop_lo = 0;
+  size_t off_ce = 0, off_dqdec = 0, off_dqf = 0, off_gop = 0, off_gop_lo = 0, off_cs = 0, off_rowdot = 0;
+  size_t total = 0;
+};
+
+BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
+  BwdPlan p;
+  p.f = make_plan(B, H, N, M, D, dtype);
+  const int BH = p.f.BH;
+  p.Mp = p.f.Mp32;
+  // Latent side: one wave per 32 latents, groups of 4 or 8 waves; about 1024 (8-wave) or 2048
+  // (4-wave) workgroups over the token chunks.
+  p.lat_nw = flarepp::bwd_latent_waves(p.Mp);
+  p.lat_nlg = (int)ceil_div(p.Mp, 32 * p.lat_nw);
+  const int64_t target = env_int("FLAREPP_BWD_LATENT_WORKGROUPS", p.lat_nw == 8 ? 1024 : 2048);
+  int64_t nchunk = ceil_div(target, (int64_t)BH * p.lat_nlg);
+  const int64_t max_chunks = ceil_div(N, (int64_t)flarepp::kBwdStage);
+  if (nchunk > max_chunks) nchunk = max_chunks;
+  if (nchunk < 1) nchunk = 1;
+  p.lat_chunk = ceil_div(ceil_div(N, nchunk), (int64_t)flarepp::kBwdStage) * flarepp::kBwdStage;
+  p.lat_nchunk = (int)ceil_div(N, p.lat_chunk);
+  p.lat_gx = p.lat_nlg == 1 ? p.lat_nchunk : (int)(ceil_div(p.lat_nchunk, 8) * 8 * p.lat_nlg);
+  // Token side: about 512 workgroups of 8 waves, 32-token blocks.
+  const int64_t tok_target = env_int("FLAREPP_BWD_TOKEN_WORKGROUPS", 512);
+  int64_t gx = ceil_div(tok_target, (int64_t)BH);
+  const int64_t max_gx = ceil_div(N, (int64_t)32 * flarepp::kBwdTokenWaves);
+  if (gx > max_gx) gx = max_gx;
+  if (gx < 1) gx = 1;
+  p.tok_tpw = ceil_div(ceil_div(N, gx), (int64_t)32) * 32;
+  p.tok_gx = (int)ceil_div(N, p.tok_tpw);
+
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t lat = (size_t)BH * p.Mp;  // latent rows
+  size_t off = p.f.total;
+  p.off_qd = off;     off = align256(off + (size_t)BH * M * D * 4);
+  p.off_z32 = off;    off = align256(off + (size_t)BH * M * D * 4);
+  p.off_lsyn = off;   off = align256(off + lat * 4);
+  p.off_lenc = off;   off = align256(off + lat * 4);
+  p.off_zc = off;     off = align256(off + lat * D * es);
+  p.off_zc_lo = off;  off = align256(off + lat * D * es);
+  p.off_ldec = off;   off = align256(off + (size_t)BH * N * 4);
+  p.off_cd = off;     off = align256(off + (size_t)BH * N * 4);
+  // The decode call's part of dK in fp32 (fp32 runs keep it in dK itself).
+  p.off_dkdec = off;  off = align256(off + (dtype == FLAREPP_BF16 ? (size_t)BH * N * D * 4 : 0));
+  p.off_p0 = off;     off = align256(off + (size_t)BH * p.lat_nchunk * p.Mp * D * 4);
+  p.off_p1 = off;     off = align256(off + (size_t)BH * p.lat_nchunk * p.Mp * D * 4);
+  p.off_dz32 = off;   off = align256(off + lat * D * 4);
+  p.off_dzop = off;   off = align256(off + lat * D * es);
+  p.off_dzop_lo = off; off = align256(off + lat * D * es);
+  p.off_ce = off;     off = align256(off + lat * 4);
+  p.off_dqdec = off;  off = align256(off + lat * D * 4);
+  p.off_dqf = off;    off = align256(off + lat * D * 4);
+  p.off_gop = off;    off = align256(off + lat * D * es);
+  p.off_gop_lo = off; off = align256(off + lat * D * es);
+  p.off_cs = off;     off = align256(off + lat * 4);
+  p.off_rowdot = off; off = align256(off + lat * 4);
+  p.total = off;
+  return p;
+}
+
+// Sizes the backward kernels support beyond the forward's: the token-side kernels keep the latent
+// tensors of one (batch, head) in LDS (160 KiB).
+int validate_bwd_sizes(int B, int H, int64_t N, int M, int D, int dtype, bool* empty) {
+  int rc = validate_sizes(B, H, N, M, D, dtype, empty);
+  if (rc != FLAREPP_OK) return rc;
+  const int Mp = (M + 31) / 32 * 32;
+  for (int kind : {flarepp::kBwdTokDecode, flarepp::kBwdTokEncode, flarepp::kBwdTokSynthesis})
+    if (flarepp::bwd_token_lds_bytes(dtype, D, Mp, kind) > 160 * 1024) return FLAREPP_UNSUPPORTED;
+  return FLAREPP_OK;
+}
+
+int enqueue_backward(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                     const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype, void* dK,
+                     void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* ws, const BwdPlan& p,
+                     hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  const int BH = p.f.BH;
+  Saved sv;
+  sv.lsyn = F(p.off_lsyn);
+  sv.lenc = F(p.off_lenc);
+  sv.exact = true;
+  sv.no_decode = true;
+  int rc = enqueue(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, nullptr, F(p.off_qd), nullptr, F(p.off_z32), ws,
+                   p.f, st, sv);
+  if (rc != FLAREPP_OK) return rc;
+  void* qrows = w + p.f.off_q;
+  float* ldec = F(p.off_ldec);
+  float* cd = F(p.off_cd);
+  float* dkdec = dtype == FLAREPP_BF16 ? F(p.off_dkdec) : static_cast<float*>(dK);
+
+  flarepp::BwdCenterArgs ca{};
+  ca.Z32 = F(p.off_z32); ca.Zc = w + p.off_zc; ca.Zc_lo = w + p.off_zc_lo; ca.M = M; ca.Mp = p.Mp;
+  if (run_kernel(6, st, [&] { return flarepp::launch_bwd_center(ca, dtype, D, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  flarepp::BwdTokenArgs ta{};
+  ta.K = K; ta.V = V; ta.dY = dY; ta.S = S; ta.tl = ldec; ta.tc = cd; ta.dKdec = dkdec; ta.Qrows = qrows;
+  ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
+  ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
+  ta.lsyn = sv.lsyn; ta.cs = F(p.off_cs); ta.dK = dK; ta.dV = dV; ta.dS = dS; ta.N = N;
+  ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H;
+  if (run_kernel(7, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokDecode, p.tok_gx, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  flarepp::BwdLatentArgs la{};
+  la.N = N; la.chunk = p.lat_chunk; la.nchunk = p.lat_nchunk; la.nlg = p.lat_nlg; la.M = M; la.Mp = p.Mp; la.H = H;
+  la.part0 = F(p.off_p0); la.part1 = F(p.off_p1);
+  flarepp::BwdReduceArgs ra{};
+  ra.part0 = la.part0; ra.part1 = la.part1; ra.nchunk = p.lat_nchunk; ra.M = M; ra.Mp = p.Mp; ra.H = H; ra.B = B;
+  ra.Z32 = F(p.off_z32); ra.dZ32 = F(p.off_dz32); ra.dZop = w + p.off_dzop; ra.dZop_lo = w + p.off_dzop_lo;
+  ra.ce = F(p.off_ce); ra.dQdec = F(p.off_dqdec); ra.Qf = Qf; ra.g = g; ra.Qd32 = F(p.off_qd);
+  ra.dQf_bh = F(p.off_dqf); ra.Gop = w + p.off_gop; ra.Gop_lo = w + p.off_gop_lo; ra.cs = F(p.off_cs);
+  ra.rowdot = F(p.off_rowdot); ra.dQseed = dQseed; ra.dQf = dQf; ra.dg = dg;
+
+  // Decode call: dZ and dQ_dec.
+  la.X = K; la.W = dY; la.tl = ldec; la.tc = cd; la.Qr = qrows; la.Wr = w + p.off_zc; la.Wr_lo = w + p.off_zc_lo;
+  la.ll = nullptr; la.lc = nullptr;
+  if (run_kernel(8, st, [&] { return flarepp::launch_bwd_latent(la, dtype, D, flarepp::kBwdDecode, p.lat_nw, p.lat_gx, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  if (run_kernel(9, st, [&] { return flarepp::launch_bwd_reduce(ra, dtype, D, flarepp::kBwdDecode, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  // Encode call: dQ_enc, then the gate.
+  la.X = K; la.W = V; la.tl = nullptr; la.tc = nullptr; la.Qr = qrows; la.Wr = w + p.off_dzop;
+  la.Wr_lo = w + p.off_dzop_lo; la.ll = sv.lenc; la.lc = F(p.off_ce);
+  if (run_kernel(10, st, [&] { return flarepp::launch_bwd_latent(la, dtype, D, flarepp::kBwdEncode, p.lat_nw, p.lat_gx, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  if (run_kernel(11, st, [&] { return flarepp::launch_bwd_reduce(ra, dtype, D, flarepp::kBwdEncode, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  // Synthesis call: dQseed, and the batch sums of the shared parameters.
+  la.X = S; la.W = nullptr; la.Qr = Qseed; la.Wr = w + p.off_gop; la.Wr_lo = w + p.off_gop_lo; la.ll = sv.lsyn;
+  la.lc = F(p.off_cs);
+  if (run_kernel(12, st, [&] { return flarepp::launch_bwd_latent(la, dtype, D, flarepp::kBwdSynthesis, p.lat_nw, p.lat_gx, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  if (run_kernel(13, st, [&] { return flarepp::launch_bwd_reduce(ra, dtype, D, flarepp::kBwdSynthesis, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+
+  if (run_kernel(14, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokEncode, p.tok_gx, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  if (run_kernel(15, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokSynthesis, p.tok_gx, BH, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  return FLAREPP_OK;
+}
+
+int backward_common(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
+                    const void* dY, int B, int H, int64_t N, int M, int D, int dtype, void* dK, void* dV, void* dS,
+                    void* dQseed, void* dQf, float* dg, void* ws, size_t ws_bytes, bool own_ws, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_bwd_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK) return rc;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t nbig = (size_t)B * H * N * D * es, nq = (size_t)H * M * D * es, ng = (size_t)H * sizeof(float);
+  struct Buf { const void* p; size_t n; bool out; };
+  const Buf bufs[] = {{K, nbig, false}, {V, nbig, false}, {S, nbig, false}, {Qseed, nq, false}, {Qf, nq, false},
+                      {g, ng, false}, {dY, nbig, false}, {dK, nbig, true}, {dV, nbig, true}, {dS, nbig, true},
+                      {dQseed, nq, true}, {dQf, nq, true}, {dg, ng, true}};
+  for (const Buf& b : bufs) {
+    if (!b.p && b.n) return FLAREPP_INVALID_ARGUMENT;
+    if ((uintptr_t)b.p & 15) return FLAREPP_MISALIGNED;
+  }
+  // Every output is disjoint from every other buffer.
+  for (const Buf& a : bufs)
+    for (const Buf& b : bufs)
+      if (&a != &b && (a.out || b.out) && a.n && b.n && overlaps(a.p, a.n, b.p, b.n)) return FLAREPP_INVALID_ARGUMENT;
+  if (empty) {
+    // No token reaches an output: the shared parameters' cotangents are zero.
+    if (nq == 0) return FLAREPP_OK;
+    rc = check_device();
+    if (rc != FLAREPP_OK) return rc;
+    if (flarepp::launch_bwd_zero(dQseed, nq, st) != hipSuccess || flarepp::launch_bwd_zero(dQf, nq, st) != hipSuccess ||
+        flarepp::launch_bwd_zero(dg, ng, st) != hipSuccess)
+      return FLAREPP_LAUNCH_FAILED;
+    return FLAREPP_OK;
+  }
+  const BwdPlan p = make_bwd_plan(B, H, N, M, D, dtype);
+  if (!own_ws) {
+    if (!ws || ws_bytes < p.total) return FLAREPP_INVALID_ARGUMENT;
+    if ((uintptr_t)ws & 255) return FLAREPP_MISALIGNED;
+  }
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  if (own_ws) {
+    if (hipMallocAsync(&ws, p.total, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLAREPP_OUT_OF_MEMORY;
+    }
+  }
+  rc = enqueue_backward(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, ws, p, st);
+  if (own_ws) (void)hipFreeAsync(ws, st);
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +583,27 @@ int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Q
     if ((uintptr_t)p & 15) return FLAREPP_MISALIGNED;
   return mix_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, Qd, Q, Z, workspace, workspace_bytes,
                     false, stream);
+}
+
+size_t flarepp_backward_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype) {
+  bool empty = false;
+  if (validate_bwd_sizes(B, H, N, M, D, dtype, &empty) != FLAREPP_OK || empty) return 0;
+  return make_bwd_plan(B, H, N, M, D, dtype).total;
+}
+
+int flarepp_mix_backward(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                         const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype, void* dK,
+                         void* dV, void* dS, void* dQseed, void* dQf, float* dg, hipStream_t stream) {
+  return backward_common(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, nullptr, 0,
+                         true, stream);
+}
+
+int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                            const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype,
+                            void* dK, void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return backward_common(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, workspace,
+                         workspace_bytes, false, stream);
 }
 
 int flarepp_debug_force_exact(int enable) { return g_force_exact.exchange(enable != 0); }

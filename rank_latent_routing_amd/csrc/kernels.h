@@ -1,4 +1,5 @@
-// Internal interface between the host library (flarepp.cpp) and the HIP kernels (kernels.hip).
+// Internal interface between the host library (flarepp.cpp) and the HIP kernels (kernels.hip:
+// forward; backward.hip: backward).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -66,6 +67,8 @@ struct MergeArgs {
   void* out;       // gate: c*Q [BH][Mout][R*D] (R parts as above); merge: Z [BH][Mout][D]
   float* dbg_qd;   // optional fp32 [BH][M][D] (gate only): Qd
   float* dbg_out;  // optional fp32 [BH][M][D]: Q (gate) or Z (merge)
+  float* lse;      // optional [BH][Mout]: log2 of each row's softmax normalizer in the logits' log2
+                   // units (rows >= M: +inf, so that 2^(logit - lse) = 0 there)
 };
 
 struct DecodeArgs {
@@ -86,6 +89,105 @@ struct QueryPrepArgs {
   int H, M, Mout;  // rows per (b, h) block in the output; rows in [M, Mout) are zero
   void* out;       // c*Q rows [BH][Mout][R*D] as for the gate
 };
+
+// ---- Backward pass (backward.hip).
+//
+// Logits are in log2 units throughout: l = c q.k with c = log2(e)/sqrt(D), and every probability is
+// 2^(l - L) with L the row's log2 normalizer. Computed bf16 operands travel as hi + lo pairs
+// (hi = bf16(x), lo = bf16(x - hi)); "_lo" pointers hold the lo parts (unused for fp32).
+enum BwdCall { kBwdDecode = 0, kBwdEncode = 1, kBwdSynthesis = 2 };
+
+// Latent-side kernel of one routing call: the cotangents of the latent-indexed tensors, which sum
+// over tokens, as per-chunk partials. Score logits X_n . Qr_m (X: K, or c*N0(S) for synthesis);
+// dP = W_n . Wr_m (W: dY for decode with Wr = Zc, V for encode with Wr = dZ, c*N0(S) for synthesis
+// with Wr = G/c).
+struct BwdLatentArgs {
+  const void* X;     // [BH][N][D] dtype: K (decode, encode) or S (synthesis, normalized in-kernel)
+  const void* W;     // [BH][N][D] dtype: dY (decode) or V (encode); unused by synthesis
+  const float* tl;   // decode: [BH][N] per-token log2 normalizer
+  const float* tc;   // decode: [BH][N] per-token c = sum_m P dP
+  const void* Qr;    // decode/encode: c*Q workspace rows [BH][Mp][R*D]; synthesis: Qseed [H][M][D]
+  const void* Wr;    // [BH][Mp][D] dtype hi part: Zc (decode), dZ (encode), G/c (synthesis); rows >= M zero
+  const void* Wr_lo; // the lo part
+  const float* ll;   // encode/synthesis: [BH][Mp] per-latent log2 normalizer (rows >= M: +inf)
+  const float* lc;   // encode/synthesis: [BH][Mp] per-latent <dZ, Z> or <G, Qd>, with dZ and G as the
+                     // dP operand carries them (rows >= M: 0)
+  float* part0;      // decode: [BH][nchunk][Mp][D] sum_n P dY
+  float* part1;      // [BH][nchunk][Mp][D] sum_n dS X
+  int64_t N;
+  int64_t chunk;     // tokens per chunk (a multiple of the stage)
+  int nchunk, nlg, M, Mp, H;
+};
+
+// Sums of the latent-side partials and the latent-sized steps between the calls.
+struct BwdReduceArgs {
+  const float* part0;
+  const float* part1;
+  int nchunk, M, Mp, H, B;
+  // decode -> encode
+  const float* Z32;   // [BH][M][D] fp32 Z
+  float* dZ32;        // [BH][Mp][D]
+  void* dZop;         // [BH][Mp][D] dtype hi part of dZ
+  void* dZop_lo;      // lo part
+  float* ce;          // [BH][Mp]
+  float* dQdec;       // [BH][Mp][D] (already scaled by 1/sqrt(D))
+  // encode -> gate -> synthesis
+  const void* Qf;     // [H][M][D] dtype
+  const float* g;     // [H]
+  const float* Qd32;  // [BH][M][D] fp32 Qd
+  float* dQf_bh;      // [BH][Mp][D]
+  void* Gop;          // [BH][Mp][D] dtype hi part of g dQ / c
+  void* Gop_lo;       // lo part
+  float* cs;          // [BH][Mp]: <g dQ, Qd>
+  float* rowdot;      // [BH][Mp]: <dQ, Qd>
+  // synthesis -> parameter cotangents
+  void* dQseed;       // [H][M][D] dtype
+  void* dQf;          // [H][M][D] dtype
+  float* dg;          // [H]
+};
+
+// Token-side kernels: per-token quantities that sum over latents. Decode: the normalizer L_n of each
+// token's softmax over latents, c_n = sum_m P_nm dP_nm, and the decode call's part of dK (fp32).
+// Encode: dK (adding the decode part) and dV. Synthesis: dS.
+struct BwdTokenArgs {
+  const void* K; const void* V; const void* dY; const void* S;  // [BH][N][D] dtype
+  float* tl; float* tc;  // decode per-token L and c (written by the decode kernel)
+  float* dKdec;          // [BH][N][D] fp32: the decode call's dK (written by decode, read by encode)
+  const void* Qrows;     // c*Q workspace rows [BH][Mp][R*D] (hi, lo parts)
+  const void* Zc; const void* Zc_lo;      // [BH][Mp][D] dtype: Z minus its mean over latents
+  const void* dZop; const void* dZ_lo;    // [BH][Mp][D] dtype
+  const float* lenc; const float* ce;     // [BH][Mp]
+  const void* Qseed;                      // [H][M][D] dtype
+  const void* Gop; const void* G_lo;      // [BH][Mp][D] dtype: G / c
+  const float* lsyn; const float* cs;     // [BH][Mp]
+  void* dK; void* dV; void* dS;           // [BH][N][D] dtype
+  int64_t N;
+  int64_t tokens_per_wg;
+  int M, Mp, H;
+};
+enum BwdTokenKind { kBwdTokDecode = 0, kBwdTokEncode = 1, kBwdTokSynthesis = 2 };
+
+// Z centered over the latents, Zc_m = Z_m - mean_m Z_m, as the decode call's dP operand: the shift
+// cancels in dP - c, and rounding then scales with the spread of Z rather than with its mean.
+struct BwdCenterArgs {
+  const float* Z32;  // [BH][M][D]
+  void* Zc;          // [BH][Mp][D] dtype hi part (rows >= M zero)
+  void* Zc_lo;       // lo part
+  int M, Mp;
+};
+
+constexpr int kBwdStage = 64;  // tokens per LDS stage of the latent-side kernel
+inline int bwd_latent_waves(int Mp) { return Mp >= 256 ? 8 : 4; }
+constexpr int kBwdTokenWaves = 8;
+
+hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, hipStream_t st);
+hipError_t launch_bwd_latent(const BwdLatentArgs& a, int dtype, int D, int call, int nw, int grid_x, int BH,
+                             hipStream_t st);
+hipError_t launch_bwd_reduce(const BwdReduceArgs& a, int dtype, int D, int call, int BH, hipStream_t st);
+hipError_t launch_bwd_token(const BwdTokenArgs& a, int dtype, int D, int kind, int grid_x, int BH,
+                            hipStream_t st);
+size_t bwd_token_lds_bytes(int dtype, int D, int Mp, int kind);
+hipError_t launch_bwd_zero(void* p, size_t bytes, hipStream_t st);  // bytes: a multiple of 4
 
 hipError_t launch_query_prep(const QueryPrepArgs& a, int dtype, int D, int BH, hipStream_t stream);
 hipError_t launch_partial(const PartialArgs& a, int dtype, int D, bool synth, int plan, int grid_x,

@@ -36,7 +36,11 @@ def test_version_and_strings(L):
         assert isinstance(fl.flarepp_strerror(s), str) and fl.flarepp_strerror(s)
     assert [fl.flarepp_kernel_name(i) for i in range(6)] == [
         "synthesis_partial", "merge_gate", "encode_partial", "merge", "decode", "query_prep"]
-    assert fl.flarepp_kernel_name(6) is None
+    assert [fl.flarepp_kernel_name(i) for i in range(6, 16)] == [
+        "bwd_center", "bwd_token_decode", "bwd_latent_decode", "bwd_reduce_decode", "bwd_latent_encode",
+        "bwd_reduce_gate", "bwd_latent_synthesis", "bwd_reduce_synthesis", "bwd_token_encode",
+        "bwd_token_synthesis"]
+    assert fl.flarepp_kernel_name(16) is None
 
 
 def _mix(L, K=0x1000, V=0x2000, S=0x3000, Qs=0x4000, Qf=0x5000, g=0x6000, B=1, H=1, N=64, M=8, D=16,
@@ -102,7 +106,7 @@ def test_workspace_too_small_is_rejected(L):
 def test_timing_read_without_records(L):
     fl.flarepp_timing_enable(False)
     t = fl.flarepp_timing_read()
-    assert set(t) == {"synthesis_partial", "merge_gate", "encode_partial", "merge", "decode", "query_prep"}
+    assert set(t) == {fl.flarepp_kernel_name(i) for i in range(16)}
     assert all(v == (0.0, 0) for v in t.values())
 
 
@@ -124,3 +128,46 @@ def test_flare_validation(L):
     rc = L.flarepp_flare_ws(vp(0x1000), vp(0x2000), vp(0x4000), 1, 1, 64, 8, 16, 1, vp(0x7000000), vp(0x9000000),
                             need - 1, vp(0))
     assert rc == fl.FLAREPP_INVALID_ARGUMENT
+
+
+def _bwd(L, K=0x1000, V=0x2000, S=0x3000, Qs=0x4000, Qf=0x5000, g=0x6000, dY=0x8000000, B=1, H=1, N=64, M=8,
+         D=16, dtype=1, dK=0x9000000, dV=0xA000000, dS=0xB000000, dQs=0xC000000, dQf=0xD000000, dg=0xE000000,
+         ws=None, ws_bytes=0):
+    vp = ctypes.c_void_p
+    args = [vp(K), vp(V), vp(S), vp(Qs), vp(Qf), vp(g), vp(dY), B, H, N, M, D, dtype, vp(dK), vp(dV), vp(dS),
+            vp(dQs), vp(dQf), vp(dg)]
+    if ws is None:
+        return L.flarepp_mix_backward(*args, vp(0))
+    return L.flarepp_mix_backward_ws(*args, vp(ws), ws_bytes, vp(0))
+
+
+def test_backward_validation(L):
+    assert _bwd(L, D=24) == fl.FLAREPP_UNSUPPORTED
+    assert _bwd(L, M=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _bwd(L, M=513) == fl.FLAREPP_UNSUPPORTED
+    assert _bwd(L, dY=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _bwd(L, dg=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _bwd(L, dQs=0xC000004) == fl.FLAREPP_MISALIGNED
+    # Outputs must not overlap inputs or each other.
+    assert _bwd(L, dK=0x1000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _bwd(L, dV=0x9000000 + 32) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _bwd(L, dg=0xD000000) == fl.FLAREPP_INVALID_ARGUMENT
+    need = fl.flarepp_backward_workspace_bytes(1, 1, 64, 8, 16, 1)
+    assert _bwd(L, ws=0xF0000000, ws_bytes=need - 1) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _bwd(L, ws=0xF0000010, ws_bytes=need) == fl.FLAREPP_MISALIGNED
+
+
+def test_backward_workspace_bytes(L):
+    assert fl.flarepp_backward_workspace_bytes(1, 1, 100, 0, 16, 1) == 0
+    assert fl.flarepp_backward_workspace_bytes(1, 1, 0, 8, 16, 1) == 0
+    assert fl.flarepp_backward_workspace_bytes(1, 1, 100, 513, 32, 0) == 0
+    assert fl.flarepp_backward_workspace_bytes(1, 1, 100, 512, 32, 0) > 0
+    for (B, H, N, M, D, dt) in [(1, 2, 1024, 32, 16, 0), (4, 8, 16384, 64, 16, 1), (1, 8, 1 << 20, 512, 32, 1)]:
+        ws = fl.flarepp_backward_workspace_bytes(B, H, N, M, D, dt)
+        es = 2 if dt == 1 else 4
+        assert ws % 256 == 0
+        # At least the forward's workspace and two per-token statistics, and for bf16 the decode
+        # call's part of dK in fp32; nothing else token-sized.
+        extra = B * H * N * (8 + (4 * D if dt == 1 else 0))
+        assert ws >= fl.flarepp_workspace_bytes(B, H, N, M, D, dt) + extra
+        assert ws < extra + 512 * 2 ** 20

@@ -1,0 +1,183 @@
+"""GPU parity of the HIP mixer backward pass (flarepp_mix_backward, through the C ABI) against the
+float64 oracle's mix_head_backward: the SDPA backward of Appendix B.5 (Eq. 46-49) applied to the
+decode, encode and synthesis calls (Section 3.2, Eq. 6 and Eq. 8), through the gate (Eq. 7) and
+N0 (Eq. 5).
+
+Bars, per tensor: fp32 max|x - x_ref| / max|x_ref| <= 1e-5 (the forward pass's bar). bf16: every
+element within 2e-2 RMS(x_ref) + 2^-8 |x_ref|. The cotangents are stored in bf16, whose rounding alone
+moves an element by up to 2^-9 of itself, and they are heavy-tailed (single elements reach 30 times
+the tensor's RMS), so a bar on 2e-2 RMS alone would fail on storage; 2^-8 |x_ref| is that rounding
+with one more of the same size (the forward's bar for its heavy-tailed outputs has the same form).
+dK, dV, dS per (b, h) slice; dQseed and dQf (summed over the batch) per head; dg per head against
+sum_b sum_{m,d} |dQ Qd|, the size of the terms it sums, so that cancellation among them neither
+loosens nor tightens the bar.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import say, slice_err, tol, to_device
+from workloads import make_cotangent, make_workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_routing_amd as fl
+    fl.lib()  # fails loudly when the library is missing
+
+
+def _device(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def run_backward(w, dY, workspace=False, grads=None):
+    import rank_latent_routing_amd as fl
+    dev = to_device(w)
+    dy = _device(dY, w.dtype)
+    ws = None
+    if workspace:
+        need = fl.flarepp_backward_workspace_bytes(w.B, w.H, w.N, w.M, w.D, 1 if w.dtype == "bf16" else 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = fl.flarepp_mix_backward(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"], dy,
+                                  grads=grads, workspace=ws)
+    torch.cuda.synchronize()
+    return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def oracle_backward(w, dY):
+    """The oracle's cotangents, slice by slice, plus the dg scale sum_b sum |dQ Qd| per head."""
+    K, V, S = w.f64("K"), w.f64("V"), w.f64("S")
+    Qs, Qf = w.f64("Qseed"), w.f64("Qf")
+    from workloads import to_float64
+    dy = to_float64(dY, w.dtype)
+    out = {"dK": np.zeros(K.shape), "dV": np.zeros(K.shape), "dS": np.zeros(K.shape),
+           "dQseed": np.zeros(Qs.shape), "dQf": np.zeros(Qs.shape), "dg": np.zeros(w.H),
+           "dg_scale": np.zeros(w.H)}
+    for b in range(w.B):
+        for h in range(w.H):
+            g = float(w.g[h])
+            r = oracle.mix_head_backward(K[b, h], V[b, h], S[b, h], Qs[h], Qf[h], g, dy[b, h])
+            Qd = oracle.synthesis(Qs[h], S[b, h])
+            out["dK"][b, h], out["dV"][b, h], out["dS"][b, h] = r["dK"], r["dV"], r["dS"]
+            out["dQseed"][h] += r["dQseed"]
+            out["dQf"][h] += r["dQf"]
+            out["dg"][h] += r["dg"]
+            out["dg_scale"][h] += np.abs(r["dQ"] * Qd).sum()
+    return out
+
+
+def _err(got, ref, dtype):
+    if dtype == "fp32":
+        return slice_err(got, ref, dtype)
+    excess = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)
+    return max(float(excess.max()), 0.0) / max(np.sqrt(np.mean(ref * ref)), 1e-30)
+
+
+def _check(w, dY=None, label=""):
+    say(f"[bwd] {label or w.name}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    dY = make_cotangent(w) if dY is None else dY
+    got = run_backward(w, dY)
+    for k, v in got.items():
+        assert np.isfinite(v).all(), k
+    ref = oracle_backward(w, dY)
+    worst = {}
+    for k in ("dK", "dV", "dS"):
+        for b in range(w.B):
+            for h in range(w.H):
+                worst[k] = max(worst.get(k, 0.0), _err(got[k][b, h], ref[k][b, h], w.dtype))
+    for k in ("dQseed", "dQf"):
+        for h in range(w.H):
+            worst[k] = max(worst.get(k, 0.0), _err(got[k][h], ref[k][h], w.dtype))
+    worst["dg"] = float(np.max(np.abs(got["dg"] - ref["dg"]) / np.maximum(ref["dg_scale"], 1e-30)))
+    say(f"[bwd] {label or w.name}: worst {worst} (bar {tol(w.dtype)})")
+    for k, e in worst.items():
+        assert e <= tol(w.dtype), (k, e)
+    return got, ref
+
+
+def test_bwd_cfg1_fp32():
+    _check(make_workload(1))
+
+
+@pytest.mark.parametrize("N,M,D", [(64, 1, 16), (100, 33, 32), (3001, 17, 16), (777, 100, 32), (2048, 512, 32)])
+def test_bwd_fp32_shapes(N, M, D):
+    _check(make_workload(1, N=N, M=M, D=D, seed=300 + N + M), label=f"fp32 N={N} M={M} D={D}")
+
+
+@pytest.mark.parametrize("M,D", [(1, 16), (40, 32)])
+def test_bwd_single_token_closed_form(M, D):
+    # With one token every token-axis softmax is 1: Z_m = V and Qd_m = N0(S) for every latent, so
+    # Y = V whatever K, S, Qseed, Qf and g hold. Hence dV = dY and every other cotangent is zero.
+    w = make_workload(1, B=2, N=1, M=M, D=D, seed=11 + M)
+    dY = make_cotangent(w)
+    say(f"[bwd] single token M={M} D={D}")
+    got = run_backward(w, dY)
+    dy = w.f64("K") * 0 + dY.astype(np.float64)
+    assert np.abs(got["dV"] - dy).max() <= 1e-6 * np.abs(dy).max()
+    for k in ("dK", "dS", "dQseed", "dQf", "dg"):
+        assert np.abs(got[k]).max() <= 1e-5 * np.abs(dy).max(), k
+
+
+def test_bwd_cfg2_bf16():
+    _check(make_workload(2, B=2, H=2, N=5000))
+
+
+def test_bwd_cfg3_bf16_gate_zero_head():
+    w = make_workload(3, B=2, H=2, N=2000)
+    got, _ = _check(w)
+    # Head 0 has g = 0: the synthesis call does not reach the output, so its cotangents vanish
+    # exactly (Eq. 7: Q = N0(Qf) + g Qd).
+    assert not got["dS"][:, 0].any()
+    assert not got["dQseed"][0].any()
+    assert got["dS"][:, 1].any() and got["dQseed"][1].any()
+
+
+@pytest.mark.parametrize("M", [100, 300, 512])
+def test_bwd_bf16_latent_counts(M):
+    _check(make_workload(4, B=1, H=2, N=20000, M=M, seed=400 + M), label=f"bf16 M={M}")
+
+
+def test_bwd_bf16_gaussian_d16_ragged():
+    _check(make_workload(1, B=2, H=2, N=3001, M=77, D=16, dtype="bf16", seed=77), label="bf16 gauss D=16")
+
+
+def test_bwd_peaked():
+    _check(make_workload(4, peaked=True, B=1, H=2, N=20000), label="cfg4 peaked")
+
+
+def test_bwd_cfg5_shape_one_head():
+    # cfg5's head shape (M = 512, D = 32, surface inputs) at 65536 tokens.
+    _check(make_workload(5, H=1, N=65536), label="cfg5 N=65536 H=1")
+
+
+def test_bwd_determinism_and_entry_points_agree():
+    w = make_workload(4, B=1, H=2, N=5000, M=200, seed=9)
+    dY = make_cotangent(w)
+    a = run_backward(w, dY)
+    b = run_backward(w, dY, workspace=True)
+    c = run_backward(w, dY)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(a[k], c[k]), k
+
+
+def test_bwd_empty_problem_zeroes_parameter_cotangents():
+    import rank_latent_routing_amd as fl
+    w = make_workload(1, N=0)
+    dev = to_device(w)
+    dy = torch.empty_like(dev["K"])
+    grads = {"dK": torch.empty_like(dev["K"]), "dV": torch.empty_like(dev["K"]), "dS": torch.empty_like(dev["K"]),
+             "dQseed": torch.full_like(dev["Qseed"], 7.0), "dQf": torch.full_like(dev["Qf"], 7.0),
+             "dg": torch.full_like(dev["g"], 7.0)}
+    fl.flarepp_mix_backward(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"], dy, grads=grads)
+    torch.cuda.synchronize()
+    for k in ("dQseed", "dQf", "dg"):
+        assert not grads[k].any(), k

@@ -15,19 +15,23 @@ import tempfile
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "rank_latent_routing_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "rank_latent_routing_amd", "csrc")
+SOURCES = [os.path.join(CSRC, n) for n in ("kernels.hip", "backward.hip")]
 
 
 @pytest.fixture(scope="module")
 def asm():
+    text = []
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "kernels.s")
-        cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-I" + os.path.join(ROOT, "include"), "-I" + os.path.dirname(SRC), "-x", "hip", SRC, "-o", out]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        assert r.returncode == 0, r.stderr[-2000:]
-        return open(out).read()
+        for src in SOURCES:
+            out = os.path.join(d, os.path.basename(src) + ".s")
+            cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                   "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-x", "hip", src, "-o", out]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            assert r.returncode == 0, r.stderr[-2000:]
+            text.append(open(out).read())
+    return "\n".join(text)
 
 
 def _regs(tok):

@@ -173,3 +173,10 @@ def make_workload(cfg: int, *, B: int | None = None, H: int | None = None, N: in
         gv = np.broadcast_to(np.asarray(g, dtype=np.float32), (H,)).copy()
     name = f"cfg{cfg}" + ("-peaked" if peaked else "")
     return Workload(name, B, H, N, M, D, dtype, K, V, S, Qseed, Qf, gv)
+
+
+def make_cotangent(w: Workload, seed: int | None = None) -> np.ndarray:
+    """Seeded output cotangent dY for a workload: i.i.d. N(0, 1) of Y's shape [B, H, N, D], cast
+    to the workload's storage dtype like the inputs."""
+    rng = np.random.Generator(np.random.PCG64(workload_seed(0) + 7919 if seed is None else seed))
+    return _store(rng.standard_normal((w.B, w.H, w.N, w.D)), w.dtype)
