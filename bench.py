@@ -6,8 +6,11 @@ bf16 inputs with fp32 accumulation, inputs resident in HBM. The JSON line report
 the achieved TFLOP/s (12 N M D flops per head), per-kernel event timings, the roofline position of
 the dominant kernel and the float64 CPU oracle timed on a bounded sample of the same workload.
 
+The backward pass (flarepp_mix_backward with a seeded output cotangent, the forward recomputed
+inside it) is timed afterwards in a region of its own and reported under "backward".
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
-                      [--cpu-sample-heads H] [--copy-calibration]
+                      [--cpu-sample-heads H] [--copy-calibration] [--no-backward]
 """
 import argparse
 import json
@@ -26,14 +29,29 @@ PEAK_HBM_GBS = 8000.0
 PEAK_EXP_PER_S = 256 * 2.4e9 * 32
 
 KERNELS = ["synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"]
-KERNEL_SRC = os.path.join(ROOT, "rank_latent_routing_amd", "csrc", "kernels.hip")
+# Backward kernels (flarepp_mix_backward) and the recomputed forward kernels it launches.
+BWD_KERNELS = ["synthesis_partial", "merge_gate", "encode_partial", "merge", "bwd_center", "bwd_token_decode",
+               "bwd_latent_decode", "bwd_reduce_decode", "bwd_latent_encode", "bwd_reduce_gate",
+               "bwd_latent_synthesis", "bwd_reduce_synthesis", "bwd_token_encode", "bwd_token_synthesis"]
+# Algorithmic flops per (token, latent) pair per D of each backward kernel, counting each distinct
+# product of the method once (the hi/lo operand pairs are not counted): scores and dP recomputed
+# where a kernel needs them, and the products it accumulates.
+BWD_FLOPS_PER_NMD = {"synthesis_partial": 4, "encode_partial": 4, "bwd_token_decode": 10, "bwd_latent_decode": 8,
+                     "bwd_latent_encode": 6, "bwd_latent_synthesis": 6, "bwd_token_encode": 8,
+                     "bwd_token_synthesis": 8}
+# The forward kernels' sources, in the order their bytes enter the profile's fingerprint.
+KERNEL_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n in ("kernels.hip", "device.h")]
 PROFILE = os.path.join(ROOT, "profiles", "flarepp_mixer_1M_tokens.md")
 
 
 def kernel_source_hash():
+    """sha256 over the forward kernel sources (kernels.hip, then device.h)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for src in KERNEL_SRCS:
+        with open(src, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def profiled_traffic(kernel):
@@ -48,7 +66,7 @@ def profiled_traffic(kernel):
     for ln in lines:
         if ln.startswith("traffic-json: "):
             rec = json.loads(ln[len("traffic-json: "):])
-    if not rec or rec.get("kernels_hip_sha256") != kernel_source_hash():
+    if not rec or rec.get("forward_sources_sha256") != kernel_source_hash():
         return None
     k = rec.get("per_launch_bytes", {}).get(kernel)
     return None if k is None else float(k)
@@ -62,6 +80,7 @@ def _parse():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=2)
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (a reference "
                          "dispatch for scaling the HBM byte counters of a profile)")
@@ -109,6 +128,54 @@ def cpu_baseline(w, heads):
     return {"value": heads * w.N / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} (b, h) slices (b=0, h<{heads}), all {w.N} tokens, M={w.M}, D={w.D}, "
                       f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded"}
+
+
+def backward(args, w, dev, dt_code, peak):
+    """The mixer's backward pass (flarepp_mix_backward, forward recomputed inside) on the same inputs
+    with a seeded cotangent dY, timed like the forward in a region of its own."""
+    import numpy as np
+    import torch
+
+    import rank_latent_routing_amd as fl
+    from workloads import make_cotangent
+
+    dy = np.ascontiguousarray(make_cotangent(w))
+    dY = (torch.from_numpy(dy.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" else torch.from_numpy(dy)).cuda()
+    grads = {k: torch.empty_like(dev[src]) for k, src in (("dK", "K"), ("dV", "K"), ("dS", "K"), ("dQseed", "Qseed"),
+                                                           ("dQf", "Qf"), ("dg", "g"))}
+    ws = torch.empty(fl.flarepp_backward_workspace_bytes(w.B, w.H, w.N, w.M, w.D, dt_code), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: fl.flarepp_mix_backward(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"], dY,
+                                           grads=grads, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    fl.flarepp_timing_enable(True)
+    fl.flarepp_timing_read()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fl.flarepp_timing_enable(False)
+    per_kernel = fl.flarepp_timing_read()
+    ms = max(ev0.elapsed_time(ev1), wall * 1e3) / args.steps
+    kern = {k: per_kernel[k][0] / max(per_kernel[k][1], 1) for k in BWD_KERNELS}
+    nmd = float(w.N) * w.M * w.D * w.B * w.H
+    dom = max(kern, key=kern.get)
+    dom_flops = BWD_FLOPS_PER_NMD.get(dom, 0) * nmd
+    achieved = dom_flops / (kern[dom] * 1e-3) * 1e-12
+    return {"ms_per_step": ms, "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "tokens*heads/s",
+            "algorithmic_tflops": sum(BWD_FLOPS_PER_NMD.values()) * nmd / (ms * 1e-3) * 1e-12,
+            "kernels": {k: round(v, 4) for k, v in kern.items()},
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "kernel_ms": round(kern[dom], 4),
+                         "flops_per_launch": dom_flops}}
 
 
 def main():
@@ -212,6 +279,8 @@ def main():
         "kernels": {k: round(v["ms_avg"], 4) for k, v in kern.items()},
         "roofline": roofline,
     }
+    if not args.no_backward:
+        res["backward"] = backward(args, w, dev, dt_code, peak)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
     print(json.dumps(res), flush=True)
