@@ -210,6 +210,34 @@ def flare(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return decode(K, Q, encode(Q, K, V))
 
 
+def simplified_mix_head(K, V, Sk, Sv, Qseed, block: int | None = None) -> dict:
+    """One (batch, head) slice of simplified FLARE++ (Appendix A.8, Eq. 20): the routing queries are
+    the synthesized correction alone, Q = Qd = SDPA(Qseed, Sk, Sv), with no fixed query, no gate and
+    separate synthesis values; then Z = SDPA(Q, K, V) and Y = SDPA(K, Q, Z) as in Eq. 8. The learned
+    scales of Qseed and Sk are the caller's (as for the mixer's Qseed and K), so the keys Sk and values
+    Sv are used as given. Returns ``Qd`` (= ``Q``), ``Z`` and ``Y``."""
+    Qd = sdpa(Qseed, Sk, Sv) if block is None else sdpa_tokens(Qseed, Sk, Sv, block)
+    Z = encode(Qd, K, V, block)
+    Y = decode(K, Qd, Z, block)
+    return {"Qd": Qd, "Q": Qd, "Z": Z, "Y": Y}
+
+
+def simplified_mix(K, V, Sk, Sv, Qseed, block: int | None = None) -> dict:
+    """``simplified_mix_head`` over all batch elements and heads (Qseed [H, M, D] shared over the
+    batch). Returns stacked Qd, Z [B, H, M, D] and Y [B, H, N, D]."""
+    B, H = K.shape[:2]
+    out = {"Qd": [], "Z": [], "Y": []}
+    for b in range(B):
+        rows = {key: [] for key in out}
+        for h in range(H):
+            r = simplified_mix_head(K[b, h], V[b, h], Sk[b, h], Sv[b, h], Qseed[h], block)
+            for key in out:
+                rows[key].append(r[key])
+        for key in out:
+            out[key].append(np.stack(rows[key]))
+    return {key: np.stack(val) for key, val in out.items()}
+
+
 def encode_sharded(Q: np.ndarray, K: np.ndarray, V: np.ndarray, bounds) -> tuple:
     """The token-sharded encoder of Appendix B.2-B.3: each shard r (token range bounds[r]) gives
     its local log-normalizer L_r (Eq. 25) and local output Z_r (Eq. 26); the stable schedule of
