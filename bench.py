@@ -6,11 +6,12 @@ bf16 inputs with fp32 accumulation, inputs resident in HBM. The JSON line report
 the achieved TFLOP/s (12 N M D flops per head), per-kernel event timings, the roofline position of
 the dominant kernel and the float64 CPU oracle timed on a bounded sample of the same workload.
 
-The backward pass (flarepp_mix_backward with a seeded output cotangent, the forward recomputed
-inside it) is timed afterwards in a region of its own and reported under "backward".
+Plain FLARE and simplified FLARE++ on the same workload ("variants") and the backward pass
+(flarepp_mix_backward with a seeded output cotangent, the forward recomputed inside it; "backward")
+are timed afterwards, each in a region of its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
-                      [--cpu-sample-heads H] [--copy-calibration] [--no-backward]
+                      [--cpu-sample-heads H] [--copy-calibration] [--no-backward] [--no-variants]
 """
 import argparse
 import json
@@ -81,6 +82,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=2)
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-variants", action="store_true", help="skip plain FLARE and simplified FLARE++")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (a reference "
                          "dispatch for scaling the HBM byte counters of a profile)")
@@ -128,6 +130,47 @@ def cpu_baseline(w, heads):
     return {"value": heads * w.N / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} (b, h) slices (b=0, h<{heads}), all {w.N} tokens, M={w.M}, D={w.D}, "
                       f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded"}
+
+
+def _time_steps(args, call):
+    """Warm-up, then K calls in a region bracketed by synchronizations, timed with HIP events on the
+    current stream and the wall clock; returns ms per call."""
+    import torch
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return max(ev0.elapsed_time(ev1), (time.perf_counter() - t0) * 1e3) / args.steps
+
+
+def variants(args, w, dev, dt_code):
+    """Plain FLARE (Eq. 3, the fixed queries Qf used as given) and simplified FLARE++ (Eq. 20, S as
+    the synthesis keys and seeded separate synthesis values) on the same workload."""
+    import numpy as np
+    import torch
+
+    import rank_latent_routing_amd as fl
+    from workloads import make_synthesis_values
+
+    sv = np.ascontiguousarray(make_synthesis_values(w))
+    Sv = (torch.from_numpy(sv.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" else torch.from_numpy(sv)).cuda()
+    out = torch.empty_like(dev["K"])
+    ws = torch.empty(fl.flarepp_workspace_bytes(w.B, w.H, w.N, w.M, w.D, dt_code), dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, call in (
+            ("flare", lambda: fl.flarepp_flare(dev["K"], dev["V"], dev["Qf"], out=out, workspace=ws)),
+            ("simplified", lambda: fl.flarepp_mix_simplified(dev["K"], dev["V"], dev["S"], Sv, dev["Qseed"], out=out,
+                                                             workspace=ws))):
+        ms = _time_steps(args, call)
+        res[name] = {"ms_per_step": ms, "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "tokens*heads/s"}
+    return res
 
 
 def backward(args, w, dev, dt_code, peak):
@@ -279,6 +322,8 @@ def main():
         "kernels": {k: round(v["ms_avg"], 4) for k, v in kern.items()},
         "roofline": roofline,
     }
+    if not args.no_variants:
+        res["variants"] = variants(args, w, dev, dt_code)
     if not args.no_backward:
         res["backward"] = backward(args, w, dev, dt_code, peak)
     if not args.no_cpu_baseline:

@@ -117,6 +117,25 @@ int flarepp_flare_ws(const void* K, const void* V, const void* Q, int B, int H, 
                      hipStream_t stream);
 
 /*
+ * Simplified FLARE++ (Appendix A.8, Eq. 20): the routing queries are the synthesized correction
+ * alone, Q = SDPA(Qseed, Sk, Sv), with no fixed query and no gate; then Z = SDPA(Q, K, V) and
+ * out = SDPA(K, Q, Z) as in Eq. 8. Sk and Sv are the synthesis keys and the separate synthesis
+ * values [B, H, N, D], used as given: the learned-scale normalization the pages apply to the seeds
+ * and the synthesis keys is the caller's, as for flarepp_mix's Qseed and K. Qseed [H, M, D] is
+ * shared over the batch. Layouts, support, semantics and errors as for flarepp_mix; out must not
+ * overlap any input. Workspace: stream-ordered (flarepp_mix_simplified) or the caller's
+ * (flarepp_mix_simplified_ws, at least flarepp_workspace_bytes(B, H, N, M, D, dtype) bytes, 256-byte
+ * aligned).
+ */
+int flarepp_mix_simplified(const void* K, const void* V, const void* Sk, const void* Sv,
+                           const void* Qseed, int B, int H, int64_t N, int M, int D, int dtype,
+                           void* out, hipStream_t stream);
+int flarepp_mix_simplified_ws(const void* K, const void* V, const void* Sk, const void* Sv,
+                              const void* Qseed, int B, int H, int64_t N, int M, int D, int dtype,
+                              void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * Backward pass of flarepp_mix: given the same inputs and the cotangent dY of `out`
  * ([B, H, N, D], dtype), writes the cotangents of every input (Appendix B.5, Eq. 46-49 applied to
  * the decode, encode and synthesis calls of Section 3.2 Eq. 6 and Eq. 8 in reverse order, through

@@ -56,6 +56,11 @@ def lib() -> ctypes.CDLL:
     L.flarepp_flare.restype = i32
     L.flarepp_flare_ws.argtypes = flare_args + [vp, sz, vp]
     L.flarepp_flare_ws.restype = i32
+    simp_args = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp]
+    L.flarepp_mix_simplified.argtypes = simp_args + [vp]
+    L.flarepp_mix_simplified.restype = i32
+    L.flarepp_mix_simplified_ws.argtypes = simp_args + [vp, sz, vp]
+    L.flarepp_mix_simplified_ws.restype = i32
     bwd_args = mix_args[:6] + [vp, i32, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.flarepp_mix_backward.argtypes = bwd_args + [vp]
     L.flarepp_mix_backward.restype = i32
@@ -255,6 +260,33 @@ def flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=None, workspace=None, 
     return grads
 
 
+def flarepp_mix_simplified(K, V, Sk, Sv, Qseed, out=None, workspace=None, stream=None):
+    """Simplified FLARE++ (Eq. 20): routing queries Qd = SDPA(Qseed, Sk, Sv) alone, then encode and
+    decode. K, V, Sk, Sv: [B, H, N, D]; Qseed: [H, M, D] (one dtype). With `workspace` (a uint8 tensor
+    of flarepp_workspace_bytes bytes) the caller owns the workspace (flarepp_mix_simplified_ws)."""
+    import torch
+    if K.dim() != 4 or any(t.shape != K.shape for t in (V, Sk, Sv)):
+        raise ValueError("K, V, Sk, Sv must be [B, H, N, D] of one shape")
+    B, H, N, D = K.shape
+    if Qseed.dim() != 3 or Qseed.shape[0] != H or Qseed.shape[2] != D:
+        raise ValueError("Qseed must be [H, M, D]")
+    for t in (K, V, Sk, Sv, Qseed):
+        if not t.is_contiguous() or t.dtype != K.dtype:
+            raise ValueError("all tensors must be contiguous and share one dtype")
+    M = Qseed.shape[1]
+    dt = _dtype_code(K)
+    if out is None:
+        out = torch.empty_like(K)
+    args = [_ptr(K), _ptr(V), _ptr(Sk), _ptr(Sv), _ptr(Qseed), B, H, N, M, D, dt, _ptr(out)]
+    if workspace is None:
+        st = lib().flarepp_mix_simplified(*args, _stream_ptr(stream, K.device))
+        _check(st, "flarepp_mix_simplified")
+    else:
+        st = lib().flarepp_mix_simplified_ws(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream, K.device))
+        _check(st, "flarepp_mix_simplified_ws")
+    return out
+
+
 def flarepp_debug_force_exact(enable: bool = True) -> bool:
     """Test hook: force the exact (running-maximum) softmax path for all later calls in this
     process. Returns the previous setting."""
@@ -277,6 +309,6 @@ def flarepp_timing_read() -> dict:
 
 
 __all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
-           "flarepp_flare", "flarepp_mix_backward", "flarepp_backward_workspace_bytes",
+           "flarepp_flare", "flarepp_mix_simplified", "flarepp_mix_backward", "flarepp_backward_workspace_bytes",
            "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
            "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

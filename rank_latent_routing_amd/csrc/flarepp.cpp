@@ -334,6 +334,62 @@ int flare_common(const void* K, const void* V, const void* Q, int B, int H, int6
   return rc;
 }
 
+// Simplified FLARE++ (Appendix A.8, Eq. 20): the seeds as fixed queries of the encode engine over
+// the caller's synthesis keys Sk and values Sv give Qd, which the gate merge (without Qf) emits as
+// the routing queries; then encode, merge and decode as for the mixer.
+int simplified_common(const void* K, const void* V, const void* Sk, const void* Sv, const void* Qseed, int B, int H,
+                      int64_t N, int M, int D, int dtype, void* out, void* ws, size_t ws_bytes, bool own_ws,
+                      hipStream_t st) {
+  bool empty = false;
+  int rc = validate_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  if (!K || !V || !Sk || !Sv || !Qseed || !out) return FLAREPP_INVALID_ARGUMENT;
+  const void* ptrs[] = {K, V, Sk, Sv, Qseed, out};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return FLAREPP_MISALIGNED;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t nbig = (size_t)B * H * N * D * es, nq = (size_t)H * M * D * es;
+  if (overlaps(out, nbig, K, nbig) || overlaps(out, nbig, V, nbig) || overlaps(out, nbig, Sk, nbig) ||
+      overlaps(out, nbig, Sv, nbig) || overlaps(out, nbig, Qseed, nq))
+    return FLAREPP_INVALID_ARGUMENT;
+  const Plan p = make_plan(B, H, N, M, D, dtype);
+  if (!own_ws) {
+    if (!ws || ws_bytes < p.total) return FLAREPP_INVALID_ARGUMENT;
+    if ((uintptr_t)ws & 255) return FLAREPP_MISALIGNED;
+  }
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  if (own_ws) {
+    if (hipMallocAsync(&ws, p.total, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLAREPP_OUT_OF_MEMORY;
+    }
+  }
+  char* w = static_cast<char*>(ws);
+  void* qbuf = w + p.off_q;
+  float* acc = reinterpret_cast<float*>(w + p.off_acc);
+  float* pl = reinterpret_cast<float*>(w + p.off_l);
+  float* pm = reinterpret_cast<float*>(w + p.off_m);
+  rc = FLAREPP_OK;
+  flarepp::QueryPrepArgs qa{};
+  qa.Q = Qseed; qa.H = H; qa.M = M; qa.Mout = p.Mp32; qa.out = qbuf;
+  flarepp::PartialArgs pa{};
+  pa.K = Sk; pa.V = Sv; pa.Q = qbuf; pa.H = H; pa.Mq = p.Mp32; pa.Mp = p.Mp16; pa.N = N;
+  pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
+  pa.force_exact = g_force_exact.load(); pa.part_l = pl; pa.part_m = pm;
+  flarepp::MergeArgs ma{};
+  ma.part_acc = acc; ma.part_l = pl; ma.part_m = pm; ma.nchunk = p.nchunk; ma.Mp = p.Mp16; ma.M = M;
+  ma.Mout = p.Mp32; ma.H = H; ma.Qf = nullptr; ma.g = nullptr; ma.out = qbuf;
+  if (run_kernel(5, st, [&] { return flarepp::launch_query_prep(qa, dtype, D, p.BH, st); }) != hipSuccess ||
+      run_kernel(0, st, [&] { return flarepp::launch_partial(pa, dtype, D, false, p.part_plan, p.part_gx, p.BH, st); }) != hipSuccess ||
+      run_kernel(1, st, [&] { return flarepp::launch_merge(ma, dtype, D, true, p.BH, st); }) != hipSuccess)
+    rc = FLAREPP_LAUNCH_FAILED;
+  else
+    rc = enqueue_routing(K, V, N, M, D, dtype, out, nullptr, ws, p, st);
+  if (own_ws) (void)hipFreeAsync(ws, st);
+  return rc;
+}
+
 // ---- Backward pass
 //
 // The synthesis and encode calls are recomputed on the exact path with their normalizers kept, Z
@@ -583,6 +639,18 @@ int flarepp_mix_debug(const void* K, const void* V, const void* S, const void* Q
     if ((uintptr_t)p & 15) return FLAREPP_MISALIGNED;
   return mix_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, Qd, Q, Z, workspace, workspace_bytes,
                     false, stream);
+}
+
+int flarepp_mix_simplified(const void* K, const void* V, const void* Sk, const void* Sv, const void* Qseed, int B,
+                           int H, int64_t N, int M, int D, int dtype, void* out, hipStream_t stream) {
+  return simplified_common(K, V, Sk, Sv, Qseed, B, H, N, M, D, dtype, out, nullptr, 0, true, stream);
+}
+
+int flarepp_mix_simplified_ws(const void* K, const void* V, const void* Sk, const void* Sv, const void* Qseed,
+                              int B, int H, int64_t N, int M, int D, int dtype, void* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return simplified_common(K, V, Sk, Sv, Qseed, B, H, N, M, D, dtype, out, workspace, workspace_bytes, false,
+                           stream);
 }
 
 size_t flarepp_backward_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype) {

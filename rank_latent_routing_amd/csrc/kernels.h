@@ -62,8 +62,8 @@ struct MergeArgs {
   int M;           // valid latents
   int Mout;        // rows of the output block per (b, h) (M rounded up to 32; extra rows zero)
   int H;
-  const void* Qf;  // gate only: [H][M][D] dtype
-  const float* g;  // gate only: [H]
+  const void* Qf;  // gate only: [H][M][D] dtype; null: Q = Qd (no fixed query, no gate)
+  const float* g;  // gate only: [H] (unused when Qf is null)
   void* out;       // gate: c*Q [BH][Mout][R*D] (R parts as above); merge: Z [BH][Mout][D]
   float* dbg_qd;   // optional fp32 [BH][M][D] (gate only): Qd
   float* dbg_out;  // optional fp32 [BH][M][D]: Q (gate) or Z (merge)

@@ -886,12 +886,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
   if (row >= a.Mout) return;  // rows past M up to Mout are written as zeros below
   if constexpr (GATE) {
+    // Without Qf the routing queries are Qd alone (simplified FLARE++, Appendix A.8 Eq. 20).
     const int h = bh % a.H;
-    const float f = (row < a.M) ? to_f(reinterpret_cast<const T*>(a.Qf)[((int64_t)h * a.M + row) * D + d]) : 0.f;
+    const bool fixed = a.Qf != nullptr;
+    const float f = (fixed && row < a.M) ? to_f(reinterpret_cast<const T*>(a.Qf)[((int64_t)h * a.M + row) * D + d]) : 0.f;
     float ss = f * f;
 #pragma unroll
     for (int m = 1; m < D; m <<= 1) ss += shfl_xor(ss, m);
-    const float gv = a.g[h];
+    const float gv = fixed ? a.g[h] : 1.0f;
     res = (row < a.M) ? f / sqrtf(ss * (1.0f / D) + kRmsEps) + gv * qd : 0.f;
     if (a.dbg_qd && row < a.M) a.dbg_qd[((int64_t)bh * a.M + row) * D + d] = qd;
     if (a.dbg_out && row < a.M) a.dbg_out[((int64_t)bh * a.M + row) * D + d] = res;

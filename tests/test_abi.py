@@ -171,3 +171,15 @@ def test_backward_workspace_bytes(L):
         extra = B * H * N * (8 + (4 * D if dt == 1 else 0))
         assert ws >= fl.flarepp_workspace_bytes(B, H, N, M, D, dt) + extra
         assert ws < extra + 512 * 2 ** 20
+
+
+def test_simplified_validation(L):
+    vp = ctypes.c_void_p
+    def call(K=0x1000, V=0x2000, Sk=0x3000, Sv=0x4000, Qs=0x5000, N=64, M=8, D=16, dtype=1, out=0x7000000):
+        return L.flarepp_mix_simplified(vp(K), vp(V), vp(Sk), vp(Sv), vp(Qs), 1, 1, N, M, D, dtype, vp(out), vp(0))
+    assert call(D=24) == fl.FLAREPP_UNSUPPORTED
+    assert call(M=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(Sv=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(Sk=0x3008) == fl.FLAREPP_MISALIGNED
+    assert call(out=0x4000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(N=0) == fl.FLAREPP_OK

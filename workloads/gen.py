@@ -180,3 +180,10 @@ def make_cotangent(w: Workload, seed: int | None = None) -> np.ndarray:
     to the workload's storage dtype like the inputs."""
     rng = np.random.Generator(np.random.PCG64(workload_seed(0) + 7919 if seed is None else seed))
     return _store(rng.standard_normal((w.B, w.H, w.N, w.D)), w.dtype)
+
+
+def make_synthesis_values(w: Workload, seed: int | None = None) -> np.ndarray:
+    """Seeded separate synthesis values (the simplified variant's Sv) for a workload: i.i.d. N(0, 1)
+    of shape [B, H, N, D], cast to the workload's storage dtype like the inputs."""
+    rng = np.random.Generator(np.random.PCG64(workload_seed(0) + 104729 if seed is None else seed))
+    return _store(rng.standard_normal((w.B, w.H, w.N, w.D)), w.dtype)
