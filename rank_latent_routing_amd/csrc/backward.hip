@@ -97,27 +97,28 @@ struct Frag<bf16> {
   };
   __device__ static Op zero() { return Op{}; }
   __device__ static f32x16 mma(const Op& a, const Op& b, const f32x16& c) { return mfma_32x32(a, b, c); }
+  // Eight values as a pair: hi = the upper 16 bits of each value (bf16 by truncation), lo = the exact
+  // residual x - hi rounded to bf16; hi + lo keeps about 16 significant bits. Two values share one
+  // byte permute (hi) and one packed conversion (lo).
+  __device__ static Pair split8(const float* v) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint32_t b0 = __float_as_uint(v[2 * i]), b1 = __float_as_uint(v[2 * i + 1]);
+      h[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+      const f32x2 r = {v[2 * i] - __uint_as_float(b0 & 0xffff0000u), v[2 * i + 1] - __uint_as_float(b1 & 0xffff0000u)};
+      l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+    }
+    return Pair{__builtin_bit_cast(Op, h), __builtin_bit_cast(Op, l)};
+  }
   // Slots 8t .. 8t + 7 of a result tile as a pair.
   __device__ static Pair split(const f32x16& x, int t) {
-    Pair p;
+    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const float v = x[8 * t + e];
-      const bf16 hv = (bf16)v;
-      p.h[e] = hv;
-      p.l[e] = (bf16)(v - (float)hv);
-    }
-    return p;
-  }
-  __device__ static Pair split8(const float* v) {
-    Pair p;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const bf16 hv = (bf16)v[e];
-      p.h[e] = hv;
-      p.l[e] = (bf16)(v[e] - (float)hv);
-    }
-    return p;
+    for (int e = 0; e < 8; e++) v[e] = x[8 * t + e];
+    return split8(v);
   }
   __device__ static void to_float(const Op& o, float* x) {
 #pragma unroll
@@ -457,7 +458,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
   };
 
   f32x16 acc0 = {}, acc1 = {};
-  auto compute = [&](int buf, int nvalid) __attribute__((always_inline)) {
+  // MASKED: the chunk's last stage, whose tokens past nvalid are out of the softmax.
+  auto compute = [&](int buf, auto MASKED, int nvalid) __attribute__((always_inline)) {
     const T* xt = xs + buf * ST * D;
     const T* wt = ws + buf * ST * D;
 #pragma unroll
@@ -502,7 +504,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         float p = exp2_fast(s[v] - (DEC ? Lt[v] : Ll));
-        if (nvalid < ST && r0 + row32(v, hh) >= nvalid) p = 0.f;
+        if constexpr (decltype(MASKED)::value)
+          if (r0 + row32(v, hh) >= nvalid) p = 0.f;
         P[v] = p;
         dS[v] = p * (dp[v] - (DEC ? Ct[v] : Lc));
       }
@@ -537,7 +540,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
     const int buf = stage & 1;
     if (stage + 1 < nstage) load(stage + 1);
     const int64_t left = n_end - (n_begin + (int64_t)stage * ST);
-    if (active) compute(buf, left < ST ? (int)left : ST);
+    if (active) {
+      if (left < ST)
+        compute(buf, std::true_type{}, (int)left);
+      else
+        compute(buf, std::false_type{}, ST);
+    }
     if (stage + 1 < nstage) store(buf ^ 1);
     __syncthreads();
   }
@@ -772,7 +780,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       yb[kk] = valid ? F::gload(ybase + o) : F::zero();
     }
     // Logits and dP of latent block lb (C[latent][token], lane = token), masked past M.
-    auto scores = [&](int lb, f32x16& E, f32x16& dP) __attribute__((always_inline)) {
+    // MASKED: the last block when M is not a multiple of 32 (peeled, so the other blocks carry no
+    // mask instructions).
+    auto scores = [&](int lb, f32x16& E, f32x16& dP, auto MASKED) __attribute__((always_inline)) {
       const int r = 32 * lb + (lane & 31);
       Pair qa[KB], za[KB];
       E = f32x16{};
@@ -791,17 +801,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
         hold<F>(dP, za[kk]);
         hold(dP, yb[kk]);
       }
-      if (ragged && lb == nlb - 1) {
+      if constexpr (decltype(MASKED)::value) {
 #pragma unroll
         for (int v = 0; v < 16; v++)
           if (32 * lb + row32(v, hh) >= a.M) E[v] = -INFINITY;
       }
     };
+    // Runs body(lb, MASKED) over the latent blocks, the ragged last one masked.
+    auto over_blocks = [&](auto&& body) __attribute__((always_inline)) {
+      for (int lb = 0; lb < nlb - 1; lb++) body(lb, std::false_type{});
+      if (ragged)
+        body(nlb - 1, std::true_type{});
+      else
+        body(nlb - 1, std::false_type{});
+    };
 
     float mrun = -INFINITY, l = 0.f, u = 0.f;
-    for (int lb = 0; lb < nlb; lb++) {
+    over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
       f32x16 E, dP;
-      scores(lb, E, dP);
+      scores(lb, E, dP, MASKED);
       float bm = E[0];
 #pragma unroll
       for (int v = 1; v < 16; v++) bm = fmaxf(bm, E[v]);
@@ -817,7 +835,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
         u += p * dP[v];
       }
       mrun = mn;
-    }
+    });
     // The token's other 16 latents of every block are in lane l ^ 32.
     const float mo = shfl_xor(mrun, 32), lo = shfl_xor(l, 32), uo = shfl_xor(u, 32);
     const float mt = fmaxf(mrun, mo);
@@ -832,9 +850,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
     }
 
     f32x16 accK = {};
-    for (int lb = 0; lb < nlb; lb++) {
+    over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
       f32x16 E, dP;
-      scores(lb, E, dP);
+      scores(lb, E, dP, MASKED);
       f32x16 dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) dS[v] = exp2_fast(E[v] - Ld) * (dP[v] - cd);
@@ -846,7 +864,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
         hold<F>(accK, qk);
         hold<F>(accK, sk);
       }
-    }
+    });
     if (valid) {
       // dK_dec = (1/sqrt(D)) dS Q = ln 2 * dS (c*Q); slot v holds dim row32(v, l / 32).
       float* dk = a.dKdec + ((int64_t)bh * a.N + tok) * D;
