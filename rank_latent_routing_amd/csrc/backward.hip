@@ -83,6 +83,41 @@ __device__ __forceinline__ int stat_pos(int m) {
   return (m & ~31) + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
+// Element offsets, inside one block of 32 tile rows, of what a lane reads: the row operand (row l % 32,
+// dims 16 kk + 8 (l / 32) .. + 7; fp32 as two 4-element chunks) and the transposed A operand of one
+// 16-row k block (bf16: the two 4 x 16 transposed reads; fp32: its eight elements). The swizzle's
+// XOR term depends on a row only through (row / RPB) % CPR, the same in every block of 16 rows, so
+// these offsets serve every block: block b of 32 rows starts 32 b D elements further, k block t of
+// a 32-row block 16 t D further.
+template <typename T, int D>
+struct LaneOffs {
+  int row[D / 16][2];
+  int kr[8];
+};
+template <typename T, int D>
+__device__ __forceinline__ LaneOffs<T, D> lane_offsets(int lane) {
+  using S = Swz<T, D>;
+  LaneOffs<T, D> o;
+  const int hh = lane >> 5, l = lane & 31;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; kk++) {
+    o.row[kk][0] = S::off(l, 16 * kk + 8 * hh);
+    o.row[kk][1] = S::off(l, 16 * kk + 8 * hh + 4);
+  }
+  if constexpr (sizeof(T) == 2) {
+    const int i = lane & 15, cb = ((lane >> 4) & 1) & (D / 16 - 1);
+    const int col = 16 * cb + 4 * (i & 3);
+    o.kr[0] = S::off(4 * hh + (i >> 2), col);
+    o.kr[1] = S::off(8 + 4 * hh + (i >> 2), col);
+#pragma unroll
+    for (int e = 2; e < 8; e++) o.kr[e] = 0;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; e++) o.kr[e] = S::off(row32(e, hh), l & (D - 1));
+  }
+  return o;
+}
+
 // Operands of one 32x32x16 step. Op holds the eight k values of a lane; Pair is an operand with its
 // rounding residual (bf16) or the operand alone (fp32).
 template <typename T>
@@ -129,6 +164,26 @@ struct Frag<bf16> {
   template <int D>
   __device__ static Op row(const bf16* tile, int r, int col) {
     return *reinterpret_cast<const bf16x8*>(tile + Swz<bf16, D>::off(r, col));
+  }
+  // The row operand of 32-row block `blk` (lane offsets o), k block kk.
+  template <int D>
+  __device__ static Op row_at(const bf16* blk, const LaneOffs<bf16, D>& o, int kk) {
+    return *reinterpret_cast<const bf16x8*>(blk + o.row[kk][0]);
+  }
+  // The transposed A operand of the 16-row k block starting at `blk`: lane l gets its rows row32(e,
+  // l / 32) of column l % 32 (D = 16: column l % 16; the upper 16 result rows then repeat the lower
+  // ones and are not used).
+  template <int D>
+  __device__ static Op krows_at(const bf16* blk, const LaneOffs<bf16, D>& o) {
+    const bf16x4 lo = lds_read_tr4(blk + o.kr[0]);
+    const bf16x4 hi = lds_read_tr4(blk + o.kr[1]);
+    Op r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      r[e] = lo[e];
+      r[4 + e] = hi[e];
+    }
+    return r;
   }
   // A operand along the tile's rows: lane l gets rows r0 + row32(e, l / 32) of column l % 32 (D = 16:
   // column l % 16; the upper 16 result rows then repeat the lower ones and are not used).
@@ -191,6 +246,19 @@ struct Frag<float> {
     return Op{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   template <int D>
+  __device__ static Op row_at(const float* blk, const LaneOffs<float, D>& o, int kk) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(blk + o.row[kk][0]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(blk + o.row[kk][1]);
+    return Op{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  template <int D>
+  __device__ static Op krows_at(const float* blk, const LaneOffs<float, D>& o) {
+    Op r;
+#pragma unroll
+    for (int e = 0; e < 8; e++) r[e] = blk[o.kr[e]];
+    return r;
+  }
+  template <int D>
   __device__ static Op krows(const float* tile, int r0, int lane) {
     const int hh = lane >> 5, col = (lane & 31) & (D - 1);
     Op o;
@@ -224,19 +292,19 @@ __device__ __forceinline__ void hold(f32x16& acc, const typename F::Pair& x) {
   hold(acc, x.h);
   if constexpr (F::kLo) hold(acc, x.l);
 }
-// Pair reads of two swizzled tiles (hi, lo).
-template <typename F, int D, typename T>
-__device__ __forceinline__ typename F::Pair row_pair(const T* th, const T* tl, int r, int col) {
+// Pair reads of two swizzled tiles (hi, lo) at a lane's precomputed offsets.
+template <typename F, int D, typename T, typename O>
+__device__ __forceinline__ typename F::Pair row_pair_at(const T* bh, const T* bl, const O& o, int kk) {
   typename F::Pair p;
-  p.h = F::template row<D>(th, r, col);
-  if constexpr (F::kLo) p.l = F::template row<D>(tl, r, col);
+  p.h = F::template row_at<D>(bh, o, kk);
+  if constexpr (F::kLo) p.l = F::template row_at<D>(bl, o, kk);
   return p;
 }
-template <typename F, int D, typename T>
-__device__ __forceinline__ typename F::Pair krows_pair(const T* th, const T* tl, int r0, int lane) {
+template <typename F, int D, typename T, typename O>
+__device__ __forceinline__ typename F::Pair krows_pair_at(const T* bh, const T* bl, const O& o) {
   typename F::Pair p;
-  p.h = F::template krows<D>(th, r0, lane);
-  if constexpr (F::kLo) p.l = F::template krows<D>(tl, r0, lane);
+  p.h = F::template krows_at<D>(bh, o);
+  if constexpr (F::kLo) p.l = F::template krows_at<D>(bl, o);
   return p;
 }
 template <typename F, typename T>
@@ -356,6 +424,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
   const bool active = lat0 < a.Mp;
   const int lrow = lat0 + (lane & 31);
   const float c_scale = kLog2e * rsqrtf((float)D);
+  const LaneOffs<T, D> lofs = lane_offsets<T, D>(lane);
 
   const T* xbase = reinterpret_cast<const T*>(a.X) + (int64_t)bh * a.N * D;
   const T* wbase = SYN ? xbase : reinterpret_cast<const T*>(a.W) + (int64_t)bh * a.N * D;
@@ -465,13 +534,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
 #pragma unroll
     for (int sub = 0; sub < ST / 32; sub++) {
       const int r0 = 32 * sub;
-      const int rr = r0 + (lane & 31);
       f32x16 s = {}, dp = {};
       if constexpr (SYN) {
         Pair xa[KB];
 #pragma unroll
         for (int kk = 0; kk < KB; kk++) {
-          xa[kk] = row_pair<F, D>(xt, wt, rr, 16 * kk + 8 * hh);
+          xa[kk] = row_pair_at<F, D>(xt + r0 * D, wt + r0 * D, lofs, kk);
           s = mma_pe<F>(xa[kk], qb[kk].h, s);
           dp = mma_pp<F>(xa[kk], wb[kk], dp);
         }
@@ -484,8 +552,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
         Op xa[KB], wa[KB];
 #pragma unroll
         for (int kk = 0; kk < KB; kk++) {
-          xa[kk] = F::template row<D>(xt, rr, 16 * kk + 8 * hh);
-          wa[kk] = F::template row<D>(wt, rr, 16 * kk + 8 * hh);
+          xa[kk] = F::template row_at<D>(xt + r0 * D, lofs, kk);
+          wa[kk] = F::template row_at<D>(wt + r0 * D, lofs, kk);
           s = mma_ep<F>(xa[kk], qb[kk], s);
           dp = mma_ep<F>(wa[kk], wb[kk], dp);
         }
@@ -513,17 +581,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
       for (int t = 0; t < 2; t++) {
         const Pair dsp = F::split(dS, t);
         if constexpr (SYN) {
-          const Pair xk = krows_pair<F, D>(xt, wt, r0 + 16 * t, lane);
+          const Pair xk = krows_pair_at<F, D>(xt + (r0 + 16 * t) * D, wt + (r0 + 16 * t) * D, lofs);
           acc1 = mma_pp<F>(xk, dsp, acc1);
           hold<F>(acc1, xk);
         } else {
-          const Op xk = F::template krows<D>(xt, r0 + 16 * t, lane);
+          const Op xk = F::template krows_at<D>(xt + (r0 + 16 * t) * D, lofs);
           acc1 = mma_ep<F>(xk, dsp, acc1);
           hold(acc1, xk);
         }
         hold<F>(acc1, dsp);
         if constexpr (DEC) {
-          const Op wk = F::template krows<D>(wt, r0 + 16 * t, lane);
+          const Op wk = F::template krows_at<D>(wt + (r0 + 16 * t) * D, lofs);
           const Pair pp = F::split(P, t);
           acc0 = mma_ep<F>(wk, pp, acc0);
           hold(acc0, wk);
@@ -703,20 +771,19 @@ __global__ __launch_bounds__(256) void bwd_center_kernel(BwdCenterArgs a) {
     store_pair<T>(oh, ol, (int64_t)m * D + d, m < a.M ? z[(int64_t)m * D + d] - mean : 0.f);
 }
 
-// Latent tensors of one (batch, head) as swizzled LDS tiles: rows of `stride` elements from sh (and,
-// for a bf16 pair, the lo part from sl into tl); rows >= rows_valid are zero.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void fill_tile(T* th, T* tl, const T* sh, const T* sl, int Mp, int stride, int rows_valid) {
+// Latent tensors of one (batch, head) in LDS, block-major: for every block of 32 latent rows, the
+// kernel's NTILE tiles follow each other (32 x D elements each, swizzled rows), so that a tile's
+// position inside a block is a compile-time offset. Tile j gets rows of `stride` elements from src
+// (rows >= rows_valid zero).
+template <typename T, int D, int NT, int NTILE>
+__device__ __forceinline__ void fill_blocked(T* lds, int j, const T* src, int stride, int rows_valid, int Mp) {
   using Sw = Swz<T, D>;
   constexpr int CH = 16 / sizeof(T), CPR = D / CH;
   for (int q = threadIdx.x; q < Mp * CPR; q += NT) {
     const int row = q / CPR, part = q % CPR;
-    const int o = Sw::off(row, part * CH);
-    const bool ok = row < rows_valid;
-    const int64_t so = (int64_t)row * stride + part * CH;
-    *reinterpret_cast<Chunk*>(th + o) = ok ? *reinterpret_cast<const Chunk*>(sh + so) : Chunk{0u, 0u, 0u, 0u};
-    if (tl != nullptr)
-      *reinterpret_cast<Chunk*>(tl + o) = ok ? *reinterpret_cast<const Chunk*>(sl + so) : Chunk{0u, 0u, 0u, 0u};
+    T* dst = lds + ((row >> 5) * NTILE + j) * 32 * D + Sw::off(row & 31, part * CH);
+    *reinterpret_cast<Chunk*>(dst) =
+        row < rows_valid ? *reinterpret_cast<const Chunk*>(src + (int64_t)row * stride + part * CH) : Chunk{0u, 0u, 0u, 0u};
   }
 }
 template <int NT>
@@ -744,23 +811,29 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
   constexpr int NT = NW * 64;
   constexpr int NP = F::kLo ? 2 : 1;  // tiles per pair
 
+  // Block-major LDS (fill_blocked): per 32 latents, c*Q hi, [lo], Zc hi, [lo].
+  constexpr int NTILE = 2 * NP;
+  constexpr int TQH = 0, TQL = 1, TZH = NP, TZL = NP + 1;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
-  T* qh = reinterpret_cast<T*>(smem);  // [Mp][D] c*Q hi
-  T* ql = qh + Mp * D;                  // lo (bf16)
-  T* zh = qh + NP * Mp * D;             // [Mp][D] Zc hi
-  T* zl = zh + Mp * D;                  // lo (bf16)
+  T* tiles = reinterpret_cast<T*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int bh = blockIdx.y;
   {
     const T* qsrc = reinterpret_cast<const T*>(a.Qrows) + (int64_t)bh * Mp * kQRow<T> * D;
-    fill_tile<T, D, NT>(qh, F::kLo ? ql : nullptr, qsrc, qsrc + D, Mp, kQRow<T> * D, Mp);
-    fill_tile<T, D, NT>(zh, F::kLo ? zl : nullptr, reinterpret_cast<const T*>(a.Zc) + (int64_t)bh * Mp * D,
-                        reinterpret_cast<const T*>(a.Zc_lo) + (int64_t)bh * Mp * D, Mp, D, Mp);
+    const T* zsrc = reinterpret_cast<const T*>(a.Zc) + (int64_t)bh * Mp * D;
+    fill_blocked<T, D, NT, NTILE>(tiles, TQH, qsrc, kQRow<T> * D, Mp, Mp);
+    fill_blocked<T, D, NT, NTILE>(tiles, TZH, zsrc, D, Mp, Mp);
+    if constexpr (F::kLo) {
+      fill_blocked<T, D, NT, NTILE>(tiles, TQL, qsrc + D, kQRow<T> * D, Mp, Mp);
+      fill_blocked<T, D, NT, NTILE>(tiles, TZL, reinterpret_cast<const T*>(a.Zc_lo) + (int64_t)bh * Mp * D, D, Mp, Mp);
+    }
   }
   __syncthreads();
+  const LaneOffs<T, D> lofs = lane_offsets<T, D>(lane);
+  auto tile = [&](int lb, int j) __attribute__((always_inline)) { return tiles + (lb * NTILE + j) * 32 * D; };
 
   const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
   const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
@@ -783,14 +856,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
     // MASKED: the last block when M is not a multiple of 32 (peeled, so the other blocks carry no
     // mask instructions).
     auto scores = [&](int lb, f32x16& E, f32x16& dP, auto MASKED) __attribute__((always_inline)) {
-      const int r = 32 * lb + (lane & 31);
       Pair qa[KB], za[KB];
       E = f32x16{};
       dP = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
-        qa[kk] = row_pair<F, D>(qh, ql, r, 16 * kk + 8 * hh);
-        za[kk] = row_pair<F, D>(zh, zl, r, 16 * kk + 8 * hh);
+        qa[kk] = row_pair_at<F, D>(tile(lb, TQH), tile(lb, TQL), lofs, kk);
+        za[kk] = row_pair_at<F, D>(tile(lb, TZH), tile(lb, TZL), lofs, kk);
         E = mma_pe<F>(qa[kk], kb[kk], E);
         dP = mma_pe<F>(za[kk], yb[kk], dP);
       }
@@ -858,7 +930,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       for (int v = 0; v < 16; v++) dS[v] = exp2_fast(E[v] - Ld) * (dP[v] - cd);
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const Pair qk = krows_pair<F, D>(qh, ql, 32 * lb + 16 * t, lane);
+        const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQL) + 16 * t * D, lofs);
         const Pair sk = F::split(dS, t);
         accK = mma_pp<F>(qk, sk, accK);
         hold<F>(accK, qk);
@@ -894,26 +966,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
   constexpr int NT = NW * 64;
   constexpr int NP = F::kLo ? 2 : 1;
 
+  // Block-major LDS (fill_blocked): per 32 latents, c*Q hi, [lo], dZ hi, [lo]; then the stats.
+  constexpr int NTILE = 2 * NP;
+  constexpr int TQH = 0, TQL = 1, TZH = NP, TZL = NP + 1;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
-  T* qh = reinterpret_cast<T*>(smem);  // [Mp][D] c*Q hi
-  T* ql = qh + Mp * D;                  // lo (bf16)
-  T* zh = qh + NP * Mp * D;             // [Mp][D] dZ hi
-  T* zl = zh + Mp * D;                  // lo (bf16)
-  float* sl = reinterpret_cast<float*>(zh + NP * Mp * D);  // [Mp] L_enc, stat_pos order
-  float* sc = sl + Mp;                                      // [Mp] c_enc
+  T* tiles = reinterpret_cast<T*>(smem);
+  float* sl = reinterpret_cast<float*>(tiles + NTILE * Mp * D);  // [Mp] L_enc, stat_pos order
+  float* sc = sl + Mp;                                            // [Mp] c_enc
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int bh = blockIdx.y;
   {
     const T* qsrc = reinterpret_cast<const T*>(a.Qrows) + (int64_t)bh * Mp * kQRow<T> * D;
-    fill_tile<T, D, NT>(qh, F::kLo ? ql : nullptr, qsrc, qsrc + D, Mp, kQRow<T> * D, Mp);
-    fill_tile<T, D, NT>(zh, F::kLo ? zl : nullptr, reinterpret_cast<const T*>(a.dZop) + (int64_t)bh * Mp * D,
-                        reinterpret_cast<const T*>(a.dZ_lo) + (int64_t)bh * Mp * D, Mp, D, Mp);
+    fill_blocked<T, D, NT, NTILE>(tiles, TQH, qsrc, kQRow<T> * D, Mp, Mp);
+    fill_blocked<T, D, NT, NTILE>(tiles, TZH, reinterpret_cast<const T*>(a.dZop) + (int64_t)bh * Mp * D, D, Mp, Mp);
+    if constexpr (F::kLo) {
+      fill_blocked<T, D, NT, NTILE>(tiles, TQL, qsrc + D, kQRow<T> * D, Mp, Mp);
+      fill_blocked<T, D, NT, NTILE>(tiles, TZL, reinterpret_cast<const T*>(a.dZ_lo) + (int64_t)bh * Mp * D, D, Mp, Mp);
+    }
     fill_stats<NT>(sl, sc, a.lenc + (int64_t)bh * Mp, a.ce + (int64_t)bh * Mp, Mp);
   }
   __syncthreads();
+  const LaneOffs<T, D> lofs = lane_offsets<T, D>(lane);
+  auto tile = [&](int lb, int j) __attribute__((always_inline)) { return tiles + (lb * NTILE + j) * 32 * D; };
 
   const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
   const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
@@ -933,13 +1010,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
     }
     f32x16 accK = {}, accV = {};
     for (int lb = 0; lb < nlb; lb++) {
-      const int r = 32 * lb + (lane & 31);
       Pair qa[KB], za[KB];
       f32x16 E = {}, dP = {};
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
-        qa[kk] = row_pair<F, D>(qh, ql, r, 16 * kk + 8 * hh);
-        za[kk] = row_pair<F, D>(zh, zl, r, 16 * kk + 8 * hh);
+        qa[kk] = row_pair_at<F, D>(tile(lb, TQH), tile(lb, TQL), lofs, kk);
+        za[kk] = row_pair_at<F, D>(tile(lb, TZH), tile(lb, TZL), lofs, kk);
         E = mma_pe<F>(qa[kk], kb[kk], E);
         dP = mma_pe<F>(za[kk], vb[kk], dP);
       }
@@ -963,12 +1039,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const Pair qk = krows_pair<F, D>(qh, ql, 32 * lb + 16 * t, lane);
+        const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQL) + 16 * t * D, lofs);
         const Pair sk = F::split(dS, t);
         accK = mma_pp<F>(qk, sk, accK);
         hold<F>(accK, qk);
         hold<F>(accK, sk);
-        const Pair zk = krows_pair<F, D>(zh, zl, 32 * lb + 16 * t, lane);
+        const Pair zk = krows_pair_at<F, D>(tile(lb, TZH) + 16 * t * D, tile(lb, TZL) + 16 * t * D, lofs);
         const Pair pk = F::split(P, t);
         accV = mma_pp<F>(zk, pk, accV);
         hold<F>(accV, zk);
@@ -1008,25 +1084,29 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
   constexpr int NT = NW * 64;
   constexpr int NP = F::kLo ? 2 : 1;
 
+  // Block-major LDS (fill_blocked): per 32 latents, the seeds (rows >= M zero), G / c hi, [lo];
+  // then the stats.
+  constexpr int NTILE = 1 + NP;
+  constexpr int TQS = 0, TGH = 1, TGL = 2;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
-  T* qs = reinterpret_cast<T*>(smem);  // [Mp][D] seeds (rows >= M zero)
-  T* gh = qs + Mp * D;                  // [Mp][D] G / c hi
-  T* gl = gh + Mp * D;                  // lo (bf16)
-  float* sl = reinterpret_cast<float*>(gh + NP * Mp * D);  // [Mp] L_syn, stat_pos order
-  float* sc = sl + Mp;                                      // [Mp] c_syn
+  T* tiles = reinterpret_cast<T*>(smem);
+  float* sl = reinterpret_cast<float*>(tiles + NTILE * Mp * D);  // [Mp] L_syn, stat_pos order
+  float* sc = sl + Mp;                                            // [Mp] c_syn
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int bh = blockIdx.y, h = bh % a.H;
   {
-    const T* qsrc = reinterpret_cast<const T*>(a.Qseed) + (int64_t)h * a.M * D;
-    fill_tile<T, D, NT>(qs, nullptr, qsrc, qsrc, Mp, D, a.M);
-    fill_tile<T, D, NT>(gh, F::kLo ? gl : nullptr, reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D,
-                        reinterpret_cast<const T*>(a.G_lo) + (int64_t)bh * Mp * D, Mp, D, Mp);
+    fill_blocked<T, D, NT, NTILE>(tiles, TQS, reinterpret_cast<const T*>(a.Qseed) + (int64_t)h * a.M * D, D, a.M, Mp);
+    fill_blocked<T, D, NT, NTILE>(tiles, TGH, reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D, D, Mp, Mp);
+    if constexpr (F::kLo)
+      fill_blocked<T, D, NT, NTILE>(tiles, TGL, reinterpret_cast<const T*>(a.G_lo) + (int64_t)bh * Mp * D, D, Mp, Mp);
     fill_stats<NT>(sl, sc, a.lsyn + (int64_t)bh * Mp, a.cs + (int64_t)bh * Mp, Mp);
   }
   __syncthreads();
+  const LaneOffs<T, D> lofs = lane_offsets<T, D>(lane);
+  auto tile = [&](int lb, int j) __attribute__((always_inline)) { return tiles + (lb * NTILE + j) * 32 * D; };
 
   const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
   const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
@@ -1060,14 +1140,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
     }
     f32x16 accA = {}, accB = {};
     for (int lb = 0; lb < nlb; lb++) {
-      const int r = 32 * lb + (lane & 31);
       Op qa[KB];
       Pair ga[KB];
       f32x16 A = {}, dP = {};
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
-        qa[kk] = F::template row<D>(qs, r, 16 * kk + 8 * hh);
-        ga[kk] = row_pair<F, D>(gh, gl, r, 16 * kk + 8 * hh);
+        qa[kk] = F::template row_at<D>(tile(lb, TQS), lofs, kk);
+        ga[kk] = row_pair_at<F, D>(tile(lb, TGH), tile(lb, TGL), lofs, kk);
         A = mma_ep<F>(qa[kk], sb[kk], A);
         dP = mma_pp<F>(ga[kk], sb[kk], dP);
       }
@@ -1090,12 +1169,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const Op qk = F::template krows<D>(qs, 32 * lb + 16 * t, lane);
+        const Op qk = F::template krows_at<D>(tile(lb, TQS) + 16 * t * D, lofs);
         const Pair sk = F::split(dS, t);
         accA = mma_ep<F>(qk, sk, accA);
         hold(accA, qk);
         hold<F>(accA, sk);
-        const Pair gk = krows_pair<F, D>(gh, gl, 32 * lb + 16 * t, lane);
+        const Pair gk = krows_pair_at<F, D>(tile(lb, TGH) + 16 * t * D, tile(lb, TGL) + 16 * t * D, lofs);
         const Pair pk = F::split(P, t);
         accB = mma_pp<F>(gk, pk, accB);
         hold<F>(accB, gk);
