@@ -1,4 +1,6 @@
-"""Plain float64 CPU oracle of the FLARE++ mixer forward pass.
+"""Plain float64 CPU oracle of the FLARE++ mixer: its forward and backward passes, the plain-FLARE and
+simplified variants, and the block around it (feature projections, per-head normalizations, gate
+logit, output projection).
 
 TEST INFRASTRUCTURE ONLY. This module is the reference against which the GPU library is checked.
 Only the test suite, the smoke check and the CPU-baseline leg of the benchmark may import it; the
@@ -16,6 +18,10 @@ Readings where the pages leave a step open:
   Section 3.2 / Appendix A.3-A.4 is outside the mixer); N0 is applied to S and to Qf only.
 * g is the gate value itself (the pages write g = sigmoid(gamma)).
 * Decode normalizes over the M latents (softmax of the transposed scores, Section 3.1, Eq. 4).
+* The block (``mixer_block``): projections are X W (+ b) with W [C_in, C_out] as the pages write
+  them, biases optional (Appendix A.5 initializes them at zero); the per-head normalizations are RMS
+  normalizations for every dtype, with epsilon 1e-6, N_a carrying one scale vector of D entries shared
+  by the heads; the gate is sigmoid(gamma).
 """
 from __future__ import annotations
 
@@ -265,3 +271,65 @@ def encode_sharded(Q: np.ndarray, K: np.ndarray, V: np.ndarray, bounds) -> tuple
 def decode_rows(K_rows: np.ndarray, Q: np.ndarray, Z: np.ndarray) -> np.ndarray:
     """Decode (Eq. 8, second call) for a chosen subset of token rows only."""
     return sdpa(K_rows, Q, Z)
+
+
+# ---- The block around the mixer: feature projections, per-head normalizations, output projection --
+
+def rms_normalize_scaled(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """N_a: RMS normalization over the head width with a learned per-channel scale (Section 3.2, where
+    N_a and N0 are introduced; Appendix C.2 names its places: the synthesis seeds and the routing keys).
+    One scale vector of D entries serves every head (Appendix A.7: a per-head normalization carries D
+    parameters)."""
+    return rms_normalize(x) * np.asarray(scale, dtype=np.float64)
+
+
+def split_heads(T: np.ndarray, H: int) -> np.ndarray:
+    """[B, N, C] -> [B, H, N, D], D = C / H: head h owns channels h D .. h D + D - 1 (Section 2, the
+    projections split into H heads of width D = C / H)."""
+    B, N, C = T.shape
+    return np.ascontiguousarray(T.reshape(B, N, H, C // H).transpose(0, 2, 1, 3))
+
+
+def merge_heads(Y: np.ndarray) -> np.ndarray:
+    """[B, H, N, D] -> [B, N, H D]: the head outputs concatenated along the channels (Section 2)."""
+    B, H, N, D = Y.shape
+    return np.ascontiguousarray(Y.transpose(0, 2, 1, 3).reshape(B, N, H * D))
+
+
+def linear(X: np.ndarray, W: np.ndarray, b: np.ndarray | None = None) -> np.ndarray:
+    """X W (+ b): a pointwise projection with W [C_in, C_out], as the pages write it."""
+    y = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64)
+    return y if b is None else y + np.asarray(b, dtype=np.float64)
+
+
+def project(X, Wk, Wv, Ws, H, nk, bk=None, bv=None, bs=None):
+    """The projections in front of the mixer for X [B, N, C]: routing keys K = N_a(X W_K) (Section 3.2,
+    before Eq. 8), values V = X W_V, and synthesis keys S = X W~_K (Eq. 5, which the mixer normalizes
+    with N0 itself). Returns K, V, S as [B, H, N, D]."""
+    K = rms_normalize_scaled(split_heads(linear(X, Wk, bk), H), nk)
+    V = split_heads(linear(X, Wv, bv), H)
+    S = split_heads(linear(X, Ws, bs), H)
+    return K, V, S
+
+
+def out_project(Y, Wo, bo=None):
+    """The output projection: heads concatenated, then W_O (Section 2). Y [B, H, N, D] -> [B, N, C]."""
+    return linear(merge_heads(Y), Wo, bo)
+
+
+def sigmoid(x):
+    """The logistic function; the gate is g = sigmoid(gamma) (Section 3.2, Eq. 7)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def mixer_block(X, Wk, Wv, Ws, Wo, Qseed, Qf, gamma, nq, nk, bk=None, bv=None, bs=None, bo=None,
+                block: int | None = None) -> dict:
+    """The mixer with its projections (Section 3.2, Eq. 5-8; Appendix A.6-A.7, C.2), then the output
+    projection: K, V, S from ``project``; synthesis seeds N_a(Qseed) with scale nq; g = sigmoid(gamma);
+    the mixer (``mix``) on them; out = concat_h(Y_h) W_O. X [B, N, C]; W_* [C, C] (X W); Qseed, Qf
+    [H, M, D]; gamma [H]; nq, nk [D]. Returns K, V, S, Y [B, H, N, D] and ``out`` [B, N, C]."""
+    H = Qseed.shape[0]
+    K, V, S = project(X, Wk, Wv, Ws, H, nk, bk, bv, bs)
+    r = mix(K, V, S, rms_normalize_scaled(Qseed, nq), Qf, sigmoid(gamma), block)
+    return {"K": K, "V": V, "S": S, "Y": r["Y"], "out": out_project(r["Y"], Wo, bo)}
