@@ -1,5 +1,6 @@
 /*
- * flarepp.h - C ABI of the FLARE++ token mixer forward pass on MI355X (gfx950).
+ * flarepp.h - C ABI of the FLARE++ token mixer on MI355X (gfx950): the forward pass, its variants,
+ * its backward pass, and the block of projections around it.
  *
  * Source: "FLARE++: Low-rank attention with attention-synthesized routing" (arXiv 2608.11519 v2),
  * Section 3.2, Eq. 5-8, restated as one block in Appendix A.1, Eq. 11. For each batch element b and
@@ -165,6 +166,58 @@ int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const v
                             int M, int D, int dtype, void* dK, void* dV, void* dS, void* dQseed,
                             void* dQf, float* dg, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * The block around the mixer: the feature projections in front of it, the per-head normalizations
+ * and the output projection (Section 3.2: the synthesis keys of Eq. 5, the routing keys and values
+ * before Eq. 8, the seeds and the gate of Eq. 6-7; Appendix C.2 for which tensors carry the learned-
+ * scale normalization N_a; Section 2 for the head split and the output projection).
+ *
+ * Layouts (row-major, contiguous, element type `dtype` unless stated):
+ *   X, out         : [B, N, C] with C = H * D; head h owns channels h*D .. h*D + D - 1
+ *   Wk, Wv, Ws, Wo : [C, C], row o holding the input weights of output channel o (the layout of
+ *                    torch.nn.Linear's weight): a projection computes x . W^T + b, so the pages'
+ *                    matrix W_K is Wk transposed
+ *   bk, bv, bs, bo : [C] biases, or NULL for none
+ *   nk, nq         : [D] learned scales of N_a on the routing keys and on the seeds (one vector
+ *                    shared by all heads), or NULL for a unit scale
+ *   gamma          : [H] float32 gate logits; the gate is g = 1 / (1 + exp(-gamma))
+ * N_a(x) = x / sqrt(mean(x^2) + 1e-6) * scale over each head's D channels, in fp32.
+ * Support: dtype FLAREPP_FP32 or FLAREPP_BF16, D in {16, 32}, C <= 512 (bf16) or C <= 256 (fp32),
+ * N <= 2^35, B <= 65535, gfx950. Tensor pointers 16-byte aligned (biases and scales: aligned to
+ * their element). Outputs must not overlap any input or each other. Products accumulate in fp32;
+ * outputs are rounded once to `dtype` (bf16: to nearest even).
+ *
+ * flarepp_project writes K = N_a(X Wk^T + bk) with scale nk, V = X Wv^T + bv and S = X Ws^T + bs,
+ * each [B, H, N, D] (S un-normalized: the mixer applies N0 to it), ready for flarepp_mix.
+ * flarepp_out_project writes out[b, n] = concat_h(Y[b, h, n]) Wo^T + bo for Y [B, H, N, D].
+ * B*H*N == 0 does nothing.
+ */
+int flarepp_project(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* bk,
+                    const void* bv, const void* bs, const void* nk, int B, int H, int64_t N, int D,
+                    int dtype, void* K, void* V, void* S, hipStream_t stream);
+int flarepp_out_project(const void* Y, const void* Wo, const void* bo, int B, int H, int64_t N, int D,
+                        int dtype, void* out, hipStream_t stream);
+
+/*
+ * The whole block: flarepp_project, then the mixer (flarepp_mix) with the seeds N_a(Qseed) (scale
+ * nq, rounded to dtype) and the gates sigmoid(gamma), then flarepp_out_project of its output. Qseed
+ * and Qf are [H, M, D] as for flarepp_mix (Qf is normalized by the mixer with N0). Support: the
+ * union of the mixer's and the projections' conditions (1 <= M <= 512, B*H <= 65535). flarepp_block
+ * allocates its workspace stream-ordered; flarepp_block_ws takes the caller's, at least
+ * flarepp_block_workspace_bytes(B, H, N, M, D, dtype) bytes (0 for invalid sizes), 256-byte aligned.
+ * It holds K, V, S and the mixer output (4 B H N D elements) besides the mixer's own workspace.
+ */
+size_t flarepp_block_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype);
+int flarepp_block(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* Wo,
+                  const void* bk, const void* bv, const void* bs, const void* bo, const void* Qseed,
+                  const void* Qf, const float* gamma, const void* nq, const void* nk, int B, int H,
+                  int64_t N, int M, int D, int dtype, void* out, hipStream_t stream);
+int flarepp_block_ws(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* Wo,
+                     const void* bk, const void* bv, const void* bs, const void* bo, const void* Qseed,
+                     const void* Qf, const float* gamma, const void* nq, const void* nk, int B, int H,
+                     int64_t N, int M, int D, int dtype, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /* Test hook: while enabled (non-zero), every call skips the zero-shift pass and computes all three
  * softmaxes with exact running maxima (the path the library otherwise takes only for rows whose

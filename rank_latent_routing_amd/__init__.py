@@ -68,6 +68,17 @@ def lib() -> ctypes.CDLL:
     L.flarepp_mix_backward_ws.restype = i32
     L.flarepp_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.flarepp_backward_workspace_bytes.restype = sz
+    L.flarepp_project.argtypes = [vp] * 8 + [i32, i32, i64, i32, i32, vp, vp, vp, vp]
+    L.flarepp_project.restype = i32
+    L.flarepp_out_project.argtypes = [vp, vp, vp, i32, i32, i64, i32, i32, vp, vp]
+    L.flarepp_out_project.restype = i32
+    L.flarepp_block_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.flarepp_block_workspace_bytes.restype = sz
+    block_args = [vp] * 14 + [i32, i32, i64, i32, i32, i32, vp]
+    L.flarepp_block.argtypes = block_args + [vp]
+    L.flarepp_block.restype = i32
+    L.flarepp_block_ws.argtypes = block_args + [vp, sz, vp]
+    L.flarepp_block_ws.restype = i32
     L.flarepp_debug_force_exact.argtypes = [i32]
     L.flarepp_debug_force_exact.restype = i32
     L.flarepp_timing_enable.argtypes = [i32]
@@ -287,6 +298,100 @@ def flarepp_mix_simplified(K, V, Sk, Sv, Qseed, out=None, workspace=None, stream
     return out
 
 
+def _linear_args(X, weights, biases, scales, H):
+    """Checks of the projections' arguments: X [B, N, C] (C = H D), weights [C, C] in torch Linear's
+    [out, in] layout, biases [C] and scales [D] optional, one dtype, contiguous."""
+    if X.dim() != 3 or X.shape[-1] % H:
+        raise ValueError("X must be [B, N, C] with C divisible by H")
+    C = X.shape[-1]
+    D = C // H
+    for W in weights:
+        if W.shape != (C, C):
+            raise ValueError("projection weights must be [C, C]")
+    for b in biases:
+        if b is not None and b.shape != (C,):
+            raise ValueError("biases must be [C]")
+    for sc in scales:
+        if sc is not None and sc.shape != (D,):
+            raise ValueError("normalization scales must be [D]")
+    for t in (X, *weights, *biases, *scales):
+        if t is not None and (not t.is_contiguous() or t.dtype != X.dtype):
+            raise ValueError("all tensors must be contiguous and share X's dtype")
+    return X.shape[0], X.shape[1], C, D
+
+
+def flarepp_project(X, Wk, Wv, Ws, H, bk=None, bv=None, bs=None, nk=None, out=None, stream=None):
+    """The projections in front of the mixer: K = N_a(X Wk^T + bk) (scale nk), V = X Wv^T + bv and
+    S = X Ws^T + bs, each [B, H, N, D]. X: [B, N, C]; W*: [C, C] (torch Linear layout); biases [C] and
+    nk [D] optional. Returns (K, V, S); `out` may supply them."""
+    import torch
+    B, N, C, D = _linear_args(X, (Wk, Wv, Ws), (bk, bv, bs), (nk,), H)
+    if out is None:
+        out = tuple(torch.empty((B, H, N, D), dtype=X.dtype, device=X.device) for _ in range(3))
+    K, V, S = out
+    st = lib().flarepp_project(_ptr(X), _ptr(Wk), _ptr(Wv), _ptr(Ws), _ptr(bk), _ptr(bv), _ptr(bs), _ptr(nk),
+                               B, H, N, D, _dtype_code(X), _ptr(K), _ptr(V), _ptr(S), _stream_ptr(stream, X.device))
+    _check(st, "flarepp_project")
+    return K, V, S
+
+
+def flarepp_out_project(Y, Wo, bo=None, out=None, stream=None):
+    """The output projection: out[b, n] = concat_h(Y[b, h, n]) Wo^T + bo for Y [B, H, N, D]; Wo [C, C]
+    (torch Linear layout), bo [C] optional. Returns out [B, N, C]."""
+    import torch
+    if Y.dim() != 4:
+        raise ValueError("Y must be [B, H, N, D]")
+    B, H, N, D = Y.shape
+    C = H * D
+    if Wo.shape != (C, C) or (bo is not None and bo.shape != (C,)):
+        raise ValueError("Wo must be [C, C] and bo [C]")
+    for t in (Y, Wo, bo):
+        if t is not None and (not t.is_contiguous() or t.dtype != Y.dtype):
+            raise ValueError("all tensors must be contiguous and share Y's dtype")
+    if out is None:
+        out = torch.empty((B, N, C), dtype=Y.dtype, device=Y.device)
+    st = lib().flarepp_out_project(_ptr(Y), _ptr(Wo), _ptr(bo), B, H, N, D, _dtype_code(Y), _ptr(out),
+                                   _stream_ptr(stream, Y.device))
+    _check(st, "flarepp_out_project")
+    return out
+
+
+def flarepp_block_workspace_bytes(B: int, H: int, N: int, M: int, D: int, dtype: int) -> int:
+    return int(lib().flarepp_block_workspace_bytes(B, H, N, M, D, dtype))
+
+
+def flarepp_block(X, Wk, Wv, Ws, Wo, Qseed, Qf, gamma, bk=None, bv=None, bs=None, bo=None, nq=None, nk=None,
+                  out=None, workspace=None, stream=None):
+    """The mixer block: projections, the mixer with seeds N_a(Qseed) (scale nq) and gates
+    sigmoid(gamma), and the output projection. X: [B, N, C]; W*: [C, C] (torch Linear layout);
+    Qseed, Qf: [H, M, D]; gamma: [H] float32; biases [C], nq and nk [D] optional. Returns out
+    [B, N, C]. With `workspace` (a uint8 tensor of flarepp_block_workspace_bytes bytes) the caller
+    owns the workspace (flarepp_block_ws)."""
+    import torch
+    if Qseed.dim() != 3 or Qf.shape != Qseed.shape:
+        raise ValueError("Qseed and Qf must be [H, M, D]")
+    H, M, D = Qseed.shape
+    B, N, C, D2 = _linear_args(X, (Wk, Wv, Ws, Wo), (bk, bv, bs, bo), (nq, nk), H)
+    if D2 != D:
+        raise ValueError("X's channels must be H * D")
+    for t in (Qseed, Qf):
+        if not t.is_contiguous() or t.dtype != X.dtype:
+            raise ValueError("Qseed and Qf must be contiguous and share X's dtype")
+    if gamma.shape != (H,) or gamma.dtype != torch.float32 or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float32 tensor of shape [H]")
+    if out is None:
+        out = torch.empty((B, N, C), dtype=X.dtype, device=X.device)
+    args = [_ptr(t) for t in (X, Wk, Wv, Ws, Wo, bk, bv, bs, bo, Qseed, Qf, gamma, nq, nk)]
+    args += [B, H, N, M, D, _dtype_code(X), _ptr(out)]
+    if workspace is None:
+        st = lib().flarepp_block(*args, _stream_ptr(stream, X.device))
+        _check(st, "flarepp_block")
+    else:
+        st = lib().flarepp_block_ws(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream, X.device))
+        _check(st, "flarepp_block_ws")
+    return out
+
+
 def flarepp_debug_force_exact(enable: bool = True) -> bool:
     """Test hook: force the exact (running-maximum) softmax path for all later calls in this
     process. Returns the previous setting."""
@@ -310,5 +415,6 @@ def flarepp_timing_read() -> dict:
 
 __all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
            "flarepp_flare", "flarepp_mix_simplified", "flarepp_mix_backward", "flarepp_backward_workspace_bytes",
+           "flarepp_project", "flarepp_out_project", "flarepp_block", "flarepp_block_workspace_bytes",
            "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
            "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

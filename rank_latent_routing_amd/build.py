@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflarepp.so")
-SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "backward.hip", "flarepp.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "backward.hip", "project.hip", "flarepp.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",

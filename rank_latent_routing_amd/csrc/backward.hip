@@ -54,15 +54,6 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 
-// The register allocator may place an MFMA's destination on top of an A or B operand that dies at
-// that instruction, and the double-depth gfx950 MFMA forms then return wrong products. hold(acc, x)
-// keeps x live past the MFMA that produced acc: an empty asm that reads x and rewrites acc, so it can
-// only come after that MFMA, whatever order instruction selection and scheduling choose.
-template <typename O>
-__device__ __forceinline__ void hold(f32x16& acc, const O& x) {
-  asm volatile("" : "+v"(acc) : "v"(x));
-}
-
 // Rows of D elements in LDS whose 16-byte chunks are permuted by an XOR with (row / RPB) % CPR, where
 // RPB rows span the 64 banks: the row reads of 32 lanes (32 rows, one chunk each) and the transposed
 // reads (4 rows x 32 bytes per group of 16 lanes) then touch distinct banks.

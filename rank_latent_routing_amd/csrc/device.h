@@ -63,6 +63,14 @@ __device__ __forceinline__ f32x16 mfma_32x32_f16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ void keep_live(const f32x16& x) { asm volatile("" ::"v"(x)); }
+// The register allocator may place an MFMA's destination on top of an A or B operand that dies at
+// that instruction, and the double-depth gfx950 MFMA forms then return wrong products. hold(acc, x)
+// keeps x live past the MFMA that produced acc: an empty asm that reads x and rewrites acc, so it can
+// only come after that MFMA, whatever order instruction selection and scheduling choose.
+template <typename O>
+__device__ __forceinline__ void hold(f32x16& acc, const O& x) {
+  asm volatile("" : "+v"(acc) : "v"(x));
+}
 __device__ __forceinline__ void keep_live(const f16x8& x) { asm volatile("" ::"v"(x)); }
 // bf16 -> fp16, rounding to nearest even (exact inside the fp16 range; overflow gives inf, which
 // the range check of the zero-shift pass catches).

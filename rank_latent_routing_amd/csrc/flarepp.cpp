@@ -22,14 +22,15 @@ namespace {
 
 using flarepp::kStage;
 
-constexpr int kVersion = 300;  // 0.3.0
-constexpr int kNumKinds = 16;
+constexpr int kVersion = 400;  // 0.4.0
+constexpr int kNumKinds = 19;
 const char* const kKindNames[kNumKinds] = {"synthesis_partial", "merge_gate", "encode_partial",
                                            "merge", "decode", "query_prep",
                                            "bwd_center", "bwd_token_decode", "bwd_latent_decode",
                                            "bwd_reduce_decode", "bwd_latent_encode", "bwd_reduce_gate",
                                            "bwd_latent_synthesis", "bwd_reduce_synthesis",
-                                           "bwd_token_encode", "bwd_token_synthesis"};
+                                           "bwd_token_encode", "bwd_token_synthesis", "project",
+                                           "out_project", "block_params"};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -598,6 +599,217 @@ int backward_common(const void* K, const void* V, const void* S, const void* Qse
   return rc;
 }
 
+// ---- Projections around the mixer and the whole block --------------------------------------
+
+// Largest channel width C = H * D whose weight rows fit the projection kernel's registers.
+int proj_max_channels(int dtype) { return dtype == FLAREPP_BF16 ? 512 : 256; }
+
+int validate_proj_sizes(int B, int H, int64_t N, int D, int dtype, bool* empty) {
+  *empty = false;
+  if (dtype != FLAREPP_FP32 && dtype != FLAREPP_BF16) return FLAREPP_UNSUPPORTED;
+  if (B < 0 || H < 0 || N < 0) return FLAREPP_INVALID_ARGUMENT;
+  if (D != 16 && D != 32) return FLAREPP_UNSUPPORTED;
+  if ((int64_t)H * D > proj_max_channels(dtype)) return FLAREPP_UNSUPPORTED;
+  // Token tiles are counted in int; elements in int64.
+  if (N > ((int64_t)1 << 35) || B > 65535) return FLAREPP_INVALID_ARGUMENT;
+  if ((int64_t)B * H * N == 0) *empty = true;
+  return FLAREPP_OK;
+}
+
+struct ProjPlan {
+  flarepp::ProjArgs a{};
+  int grid = 0;
+};
+
+ProjPlan make_proj_plan(int B, int H, int64_t N, int D, int dtype, int nproj) {
+  ProjPlan p;
+  const int C = H * D;
+  const int64_t groups = ceil_div((int64_t)nproj * C, 32);
+  const int64_t ngb = ceil_div(groups, (int64_t)flarepp::proj_waves(dtype, C));
+  const int64_t ntiles = ceil_div(N, flarepp::kProjTile);
+  // About 1024 workgroups (one or two per CU at a time, several rounds); at least 8 tiles each so
+  // that a workgroup's weight loads stay small against its token work.
+  const int64_t target = env_int("FLAREPP_PROJECT_WORKGROUPS", 1024);
+  int64_t tpw = ceil_div((int64_t)B * ntiles * ngb, target);
+  if (tpw < 8) tpw = 8;
+  const int64_t nranges = ceil_div(ntiles, tpw);
+  p.a.H = H;
+  p.a.C = C;
+  p.a.nproj = nproj;
+  p.a.ngb = (int)ngb;
+  p.a.N = N;
+  p.a.ntiles = (int)ntiles;
+  p.a.tiles_per_wg = (int)tpw;
+  p.a.nranges = (int)nranges;
+  p.a.nwg = (int)(B * nranges * ngb);
+  p.grid = (int)(ceil_div(p.a.nwg, 8) * 8);
+  return p;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int enqueue_project(const void* X, const void* const W[3], const void* const bias[3], const void* scale,
+                    void* const outs[3], int B, int H, int64_t N, int D, int dtype, bool front, hipStream_t st) {
+  ProjPlan p = make_proj_plan(B, H, N, D, dtype, front ? 3 : 1);
+  p.a.X = X;
+  for (int i = 0; i < 3; i++) {
+    p.a.W[i] = W[i];
+    p.a.bias[i] = bias[i];
+    p.a.out[i] = outs[i];
+  }
+  p.a.scale = scale;
+  if (run_kernel(front ? 16 : 17, st, [&] { return flarepp::launch_project(p.a, dtype, D, front, p.grid, st); }) != hipSuccess)
+    return FLAREPP_LAUNCH_FAILED;
+  return FLAREPP_OK;
+}
+
+// Pointer checks shared by the projection entry points: the listed tensors non-null where required
+// and 16-byte aligned (optional ones: element-aligned), outputs disjoint from every input and from
+// each other.
+struct Span {
+  const void* p;
+  size_t n;
+};
+bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
+  for (int i = 0; i < no; i++) {
+    for (int j = 0; j < ni; j++)
+      if (ins[j].p && overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return true;
+    for (int j = i + 1; j < no; j++)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return true;
+  }
+  return false;
+}
+
+int project_common(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* bk, const void* bv,
+                   const void* bs, const void* nk, int B, int H, int64_t N, int D, int dtype, void* K, void* V,
+                   void* S, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_proj_sizes(B, H, N, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  if (!X || !Wk || !Wv || !Ws || !K || !V || !S) return FLAREPP_INVALID_ARGUMENT;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  for (const void* q : {X, Wk, Wv, Ws, (const void*)K, (const void*)V, (const void*)S})
+    if (!aligned(q, 16)) return FLAREPP_MISALIGNED;
+  for (const void* q : {bk, bv, bs, nk})
+    if (q && !aligned(q, es)) return FLAREPP_MISALIGNED;
+  const size_t C = (size_t)H * D, big = (size_t)B * N * C * es;
+  const Span outs[] = {{K, big}, {V, big}, {S, big}};
+  const Span ins[] = {{X, big}, {Wk, C * C * es}, {Wv, C * C * es}, {Ws, C * C * es},
+                      {bk, C * es}, {bv, C * es}, {bs, C * es}, {nk, D * es}};
+  if (any_overlap(outs, 3, ins, 8)) return FLAREPP_INVALID_ARGUMENT;
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  const void* W[3] = {Wk, Wv, Ws};
+  const void* bias[3] = {bk, bv, bs};
+  void* o[3] = {K, V, S};
+  return enqueue_project(X, W, bias, nk, o, B, H, N, D, dtype, true, st);
+}
+
+int out_project_common(const void* Y, const void* Wo, const void* bo, int B, int H, int64_t N, int D, int dtype,
+                       void* out, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_proj_sizes(B, H, N, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  if (!Y || !Wo || !out) return FLAREPP_INVALID_ARGUMENT;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  for (const void* q : {Y, Wo, (const void*)out})
+    if (!aligned(q, 16)) return FLAREPP_MISALIGNED;
+  if (bo && !aligned(bo, es)) return FLAREPP_MISALIGNED;
+  const size_t C = (size_t)H * D, big = (size_t)B * N * C * es;
+  const Span outs[] = {{out, big}};
+  const Span ins[] = {{Y, big}, {Wo, C * C * es}, {bo, C * es}};
+  if (any_overlap(outs, 1, ins, 3)) return FLAREPP_INVALID_ARGUMENT;
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  const void* W[3] = {Wo, nullptr, nullptr};
+  const void* bias[3] = {bo, nullptr, nullptr};
+  void* o[3] = {out, nullptr, nullptr};
+  return enqueue_project(Y, W, bias, nullptr, o, B, H, N, D, dtype, false, st);
+}
+
+// Workspace of the block: the mixer's own, then K, V, S, Y [B][H][N][D], the normalized seeds
+// [H][M][D] and the gates [H].
+struct BlockPlan {
+  Plan mix;
+  size_t off_k = 0, off_v = 0, off_s = 0, off_y = 0, off_qs = 0, off_g = 0, total = 0;
+};
+
+BlockPlan make_block_plan(int B, int H, int64_t N, int M, int D, int dtype) {
+  BlockPlan bp;
+  bp.mix = make_plan(B, H, N, M, D, dtype);
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  const size_t big = (size_t)B * H * N * D * es;
+  size_t off = align256(bp.mix.total);
+  bp.off_k = off; off = align256(off + big);
+  bp.off_v = off; off = align256(off + big);
+  bp.off_s = off; off = align256(off + big);
+  bp.off_y = off; off = align256(off + big);
+  bp.off_qs = off; off = align256(off + (size_t)H * M * D * es);
+  bp.off_g = off; off = align256(off + (size_t)H * sizeof(float));
+  bp.total = off;
+  return bp;
+}
+
+int validate_block_sizes(int B, int H, int64_t N, int M, int D, int dtype, bool* empty) {
+  int rc = validate_sizes(B, H, N, M, D, dtype, empty);
+  if (rc != FLAREPP_OK) return rc;
+  bool e2 = false;
+  return validate_proj_sizes(B, H, N, D, dtype, &e2);
+}
+
+int block_common(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* Wo, const void* bk,
+                 const void* bv, const void* bs, const void* bo, const void* Qseed, const void* Qf,
+                 const float* gamma, const void* nq, const void* nk, int B, int H, int64_t N, int M, int D,
+                 int dtype, void* out, void* ws, size_t ws_bytes, bool own_ws, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_block_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  if (!X || !Wk || !Wv || !Ws || !Wo || !Qseed || !Qf || !gamma || !out) return FLAREPP_INVALID_ARGUMENT;
+  const size_t es = dtype == FLAREPP_BF16 ? 2 : 4;
+  for (const void* q : {X, Wk, Wv, Ws, Wo, Qseed, Qf, (const void*)gamma, (const void*)out})
+    if (!aligned(q, 16)) return FLAREPP_MISALIGNED;
+  for (const void* q : {bk, bv, bs, bo, nq, nk})
+    if (q && !aligned(q, es)) return FLAREPP_MISALIGNED;
+  const size_t C = (size_t)H * D, big = (size_t)B * N * C * es, ww = C * C * es, nqs = (size_t)H * M * D * es;
+  const Span outs[] = {{out, big}};
+  const Span ins[] = {{X, big},    {Wk, ww},     {Wv, ww},     {Ws, ww},        {Wo, ww},
+                      {bk, C * es}, {bv, C * es}, {bs, C * es}, {bo, C * es},    {Qseed, nqs},
+                      {Qf, nqs},   {gamma, H * sizeof(float)}, {nq, D * es}, {nk, D * es}};
+  if (any_overlap(outs, 1, ins, 14)) return FLAREPP_INVALID_ARGUMENT;
+  const BlockPlan bp = make_block_plan(B, H, N, M, D, dtype);
+  if (!own_ws) {
+    if (!ws || ws_bytes < bp.total) return FLAREPP_INVALID_ARGUMENT;
+    if (!aligned(ws, 256)) return FLAREPP_MISALIGNED;
+  }
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  if (own_ws) {
+    if (hipMallocAsync(&ws, bp.total, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLAREPP_OUT_OF_MEMORY;
+    }
+  }
+  char* w = static_cast<char*>(ws);
+  void *K = w + bp.off_k, *V = w + bp.off_v, *S = w + bp.off_s, *Y = w + bp.off_y, *Qs = w + bp.off_qs;
+  float* g = reinterpret_cast<float*>(w + bp.off_g);
+  flarepp::BlockParamArgs pa{Qseed, nq, gamma, Qs, g, H, M};
+  const void* W[3] = {Wk, Wv, Ws};
+  const void* bias[3] = {bk, bv, bs};
+  void* kvs[3] = {K, V, S};
+  const void* Wout[3] = {Wo, nullptr, nullptr};
+  const void* bout[3] = {bo, nullptr, nullptr};
+  void* o[3] = {out, nullptr, nullptr};
+  rc = FLAREPP_OK;
+  if (run_kernel(18, st, [&] { return flarepp::launch_block_params(pa, dtype, D, st); }) != hipSuccess)
+    rc = FLAREPP_LAUNCH_FAILED;
+  if (rc == FLAREPP_OK) rc = enqueue_project(X, W, bias, nk, kvs, B, H, N, D, dtype, true, st);
+  if (rc == FLAREPP_OK)
+    rc = enqueue(K, V, S, Qs, Qf, g, B, H, N, M, D, dtype, Y, nullptr, nullptr, nullptr, ws, bp.mix, st);
+  if (rc == FLAREPP_OK) rc = enqueue_project(Y, Wout, bout, nullptr, o, B, H, N, D, dtype, false, st);
+  if (own_ws) (void)hipFreeAsync(ws, st);
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -672,6 +884,39 @@ int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const v
                             size_t workspace_bytes, hipStream_t stream) {
   return backward_common(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, workspace,
                          workspace_bytes, false, stream);
+}
+
+int flarepp_project(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* bk, const void* bv,
+                    const void* bs, const void* nk, int B, int H, int64_t N, int D, int dtype, void* K, void* V,
+                    void* S, hipStream_t stream) {
+  return project_common(X, Wk, Wv, Ws, bk, bv, bs, nk, B, H, N, D, dtype, K, V, S, stream);
+}
+
+int flarepp_out_project(const void* Y, const void* Wo, const void* bo, int B, int H, int64_t N, int D, int dtype,
+                        void* out, hipStream_t stream) {
+  return out_project_common(Y, Wo, bo, B, H, N, D, dtype, out, stream);
+}
+
+size_t flarepp_block_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype) {
+  bool empty = false;
+  if (validate_block_sizes(B, H, N, M, D, dtype, &empty) != FLAREPP_OK || empty) return 0;
+  return make_block_plan(B, H, N, M, D, dtype).total;
+}
+
+int flarepp_block(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* Wo, const void* bk,
+                  const void* bv, const void* bs, const void* bo, const void* Qseed, const void* Qf,
+                  const float* gamma, const void* nq, const void* nk, int B, int H, int64_t N, int M, int D,
+                  int dtype, void* out, hipStream_t stream) {
+  return block_common(X, Wk, Wv, Ws, Wo, bk, bv, bs, bo, Qseed, Qf, gamma, nq, nk, B, H, N, M, D, dtype, out,
+                      nullptr, 0, true, stream);
+}
+
+int flarepp_block_ws(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* Wo, const void* bk,
+                     const void* bv, const void* bs, const void* bo, const void* Qseed, const void* Qf,
+                     const float* gamma, const void* nq, const void* nk, int B, int H, int64_t N, int M, int D,
+                     int dtype, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return block_common(X, Wk, Wv, Ws, Wo, bk, bv, bs, bo, Qseed, Qf, gamma, nq, nk, B, H, N, M, D, dtype, out,
+                      workspace, workspace_bytes, false, stream);
 }
 
 int flarepp_debug_force_exact(int enable) { return g_force_exact.exchange(enable != 0); }

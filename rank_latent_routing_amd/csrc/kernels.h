@@ -198,4 +198,39 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int grid
 size_t decode_lds_bytes(int dtype, int D, int Mp, int nw);
 size_t partial_lds_bytes(int dtype, int D, int plan);
 
+// ---- Projections around the mixer (project.hip) ----------------------------------------------
+// Out = X W^T per 32-token tile; each wave keeps the weight rows of its 32-channel output group in
+// registers. Front end: X [B][N][C] -> K = N_a(X Wk^T + bk), V = X Wv^T + bv, S = X Ws^T + bs, each
+// [B][H][N][D]. Output projection: Y [B][H][N][D] (heads concatenated) -> Y Wo^T + bo, [B][N][C].
+constexpr int kProjTile = 32;   // tokens per LDS stage
+struct ProjArgs {
+  const void* X;        // front end: X [B][N][C]; output projection: Y [B][H][N][D]
+  const void* W[3];     // [C][C] each, row o = the weights of output channel o (torch Linear layout)
+  const void* bias[3];  // [C] or null
+  const void* scale;    // front end: the key scale [D] of N_a (null: 1)
+  void* out[3];         // front end: K, V, S [B][H][N][D]; output projection: out [B][N][C]
+  int H, C;
+  int nproj;            // 3 (front end) or 1
+  int ngb;              // workgroups sharing one token range (one 32-channel group per wave)
+  int64_t N;
+  int ntiles;           // 32-token tiles per batch element
+  int tiles_per_wg;     // tiles per token range
+  int nranges;          // token ranges per batch element
+  int nwg;              // workgroups with work; the grid rounds it up to a multiple of 8
+};
+int proj_waves(int dtype, int C);  // waves per workgroup for channel width C
+size_t proj_lds_bytes(int dtype, int C, int nproj);
+hipError_t launch_project(const ProjArgs& a, int dtype, int D, bool front, int grid, hipStream_t st);
+
+// Synthesis seeds N_a(Qseed) and gates sigmoid(gamma) for the block.
+struct BlockParamArgs {
+  const void* Qseed;    // [H][M][D]
+  const void* nq;       // [D] seed scale or null (1)
+  const float* gamma;   // [H] gate logits
+  void* Qs;             // [H][M][D] out, the model dtype
+  float* g;             // [H] out
+  int H, M;
+};
+hipError_t launch_block_params(const BlockParamArgs& a, int dtype, int D, hipStream_t st);
+
 }  // namespace flarepp

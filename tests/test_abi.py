@@ -40,7 +40,8 @@ def test_version_and_strings(L):
         "bwd_center", "bwd_token_decode", "bwd_latent_decode", "bwd_reduce_decode", "bwd_latent_encode",
         "bwd_reduce_gate", "bwd_latent_synthesis", "bwd_reduce_synthesis", "bwd_token_encode",
         "bwd_token_synthesis"]
-    assert fl.flarepp_kernel_name(16) is None
+    assert [fl.flarepp_kernel_name(i) for i in range(16, 19)] == ["project", "out_project", "block_params"]
+    assert fl.flarepp_kernel_name(19) is None
 
 
 def _mix(L, K=0x1000, V=0x2000, S=0x3000, Qs=0x4000, Qf=0x5000, g=0x6000, B=1, H=1, N=64, M=8, D=16,
@@ -106,7 +107,7 @@ def test_workspace_too_small_is_rejected(L):
 def test_timing_read_without_records(L):
     fl.flarepp_timing_enable(False)
     t = fl.flarepp_timing_read()
-    assert set(t) == {fl.flarepp_kernel_name(i) for i in range(16)}
+    assert set(t) == {fl.flarepp_kernel_name(i) for i in range(19)}
     assert all(v == (0.0, 0) for v in t.values())
 
 
@@ -183,3 +184,68 @@ def test_simplified_validation(L):
     assert call(Sk=0x3008) == fl.FLAREPP_MISALIGNED
     assert call(out=0x4000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
     assert call(N=0) == fl.FLAREPP_OK
+
+
+def _proj(L, X=0x1000, Wk=0x2000, Wv=0x3000, Ws=0x4000, bk=0, bv=0, bs=0, nk=0, B=1, H=2, N=64, D=16, dtype=1,
+          K=0x7000000, V=0x8000000, S=0x9000000):
+    vp = ctypes.c_void_p
+    return L.flarepp_project(vp(X), vp(Wk), vp(Wv), vp(Ws), vp(bk), vp(bv), vp(bs), vp(nk), B, H, N, D, dtype,
+                             vp(K), vp(V), vp(S), vp(0))
+
+
+def test_project_validation(L):
+    assert _proj(L, D=24) == fl.FLAREPP_UNSUPPORTED
+    assert _proj(L, dtype=3) == fl.FLAREPP_UNSUPPORTED
+    assert _proj(L, H=17, D=32) == fl.FLAREPP_UNSUPPORTED  # C = 544 > 512
+    assert _proj(L, H=9, D=32, dtype=0) == fl.FLAREPP_UNSUPPORTED  # fp32 C = 288 > 256
+    assert _proj(L, N=-1) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, N=(1 << 35) + 1) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, X=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, S=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, Wv=0x3008) == fl.FLAREPP_MISALIGNED
+    assert _proj(L, bk=0x5001) == fl.FLAREPP_MISALIGNED  # biases: element alignment
+    # Outputs must not overlap the inputs or each other.
+    assert _proj(L, K=0x1000 + 32) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, V=0x7000000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, bk=0x9000000 + 2) == fl.FLAREPP_INVALID_ARGUMENT
+    assert _proj(L, N=0) == fl.FLAREPP_OK
+    assert _proj(L, H=0) == fl.FLAREPP_OK
+
+
+def test_out_project_validation(L):
+    vp = ctypes.c_void_p
+    def call(Y=0x1000, Wo=0x2000, bo=0, H=2, N=64, D=16, dtype=1, out=0x7000000):
+        return L.flarepp_out_project(vp(Y), vp(Wo), vp(bo), 1, H, N, D, dtype, vp(out), vp(0))
+    assert call(D=8) == fl.FLAREPP_UNSUPPORTED
+    assert call(Y=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(out=0x7000008) == fl.FLAREPP_MISALIGNED
+    assert call(out=0x1000 + 16) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(N=0) == fl.FLAREPP_OK
+
+
+def test_block_validation_and_workspace(L):
+    vp = ctypes.c_void_p
+    def call(X=0x1000, Qs=0x5000, gamma=0x6000, M=8, D=16, H=2, N=64, out=0x7000000, ws=None, ws_bytes=0):
+        args = [vp(X), vp(0x10000), vp(0x20000), vp(0x30000), vp(0x40000), vp(0), vp(0), vp(0), vp(0), vp(Qs),
+                vp(0x50000), vp(gamma), vp(0), vp(0), 1, H, N, M, D, 1, vp(out)]
+        if ws is None:
+            return L.flarepp_block(*args, vp(0))
+        return L.flarepp_block_ws(*args, vp(ws), ws_bytes, vp(0))
+    assert call(M=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(M=513) == fl.FLAREPP_UNSUPPORTED
+    assert call(D=24) == fl.FLAREPP_UNSUPPORTED
+    assert call(H=17, D=32) == fl.FLAREPP_UNSUPPORTED
+    assert call(gamma=0) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(Qs=0x5004) == fl.FLAREPP_MISALIGNED
+    assert call(out=0x1000 + 64) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(N=0) == fl.FLAREPP_OK
+    need = fl.flarepp_block_workspace_bytes(1, 2, 64, 8, 16, 1)
+    assert call(ws=0xF0000000, ws_bytes=need - 1) == fl.FLAREPP_INVALID_ARGUMENT
+    assert call(ws=0xF0000010, ws_bytes=need) == fl.FLAREPP_MISALIGNED
+    assert fl.flarepp_block_workspace_bytes(1, 2, 64, 0, 16, 1) == 0
+    for (B, H, N, M, D, dt) in [(1, 2, 1024, 32, 16, 0), (1, 8, 1 << 20, 512, 32, 1)]:
+        es = 2 if dt == 1 else 4
+        ws = fl.flarepp_block_workspace_bytes(B, H, N, M, D, dt)
+        # The mixer's workspace plus K, V, S and the mixer output, the seeds and the gates.
+        assert ws >= fl.flarepp_workspace_bytes(B, H, N, M, D, dt) + 4 * B * H * N * D * es + H * M * D * es
+        assert ws < fl.flarepp_workspace_bytes(B, H, N, M, D, dt) + 4 * B * H * N * D * es + H * M * D * es + 2048

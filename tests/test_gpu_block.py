@@ -1,0 +1,239 @@
+"""GPU parity of the projections around the mixer and of the whole block (flarepp_project,
+flarepp_out_project, flarepp_block, through the C ABI) against the float64 oracle (``project``,
+``out_project``, ``mixer_block``): Section 3.2 Eq. 5-8, Appendix A.6-A.7 and C.2, Section 2.
+
+Bars:
+* projections, fp32: max |x - x_ref| / max |x_ref| <= 1e-5 per (b, h) slice (per b for the output
+  projection).
+* projections, bf16: every element within 2^-8 |x_ref| + 1e-4 RMS(x_ref). The kernel accumulates in
+  fp32 and rounds once to bf16 (round to nearest even moves a value by at most 2^-8 of itself); the
+  fp32 accumulation error over C <= 512 products is below 1e-6 of the RMS, so 1e-4 RMS is a wide
+  margin for it, and a wrong weight, bias, scale or index fails by orders of magnitude more.
+* block, fp32: 1e-5 relative, as the mixer.
+* block, bf16: every element within 2e-2 RMS(out_ref) + 2^-8 |out_ref| per batch element: the
+  mixer's bar plus the rounding of the stored output.
+Full-size checks use the 1M-token workload's shape (B = 1, N = 2^20, H = 8, D = 32) in the launch
+configuration the benchmark times, on sampled token rows the oracle computes one by one.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import say
+from workloads import make_block_inputs, make_workload, to_float64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_routing_amd as fl
+    fl.lib()  # fails loudly when the library is missing
+
+
+def _dev(arr, dtype):
+    if arr is None:
+        return None
+    a = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _wdev(W, dtype):
+    """A pages-orientation matrix [C_in, C_out] in the library's [out, in] layout."""
+    return _dev(np.ascontiguousarray(W.T), dtype)
+
+
+def _err(got, ref, dtype, rms_term):
+    """fp32: max relative error; bf16: worst excess over 2^-8 |ref|, in units of RMS(ref) (to be
+    compared with ``rms_term``)."""
+    if dtype == "fp32":
+        return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+    excess = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)
+    return max(float(excess.max()), 0.0) / max(float(np.sqrt(np.mean(ref * ref))), 1e-30)
+
+
+def _bar(dtype, rms_term):
+    return 1e-5 if dtype == "fp32" else rms_term
+
+
+def _project_gpu(w, bi, with_bias=True, with_scale=True):
+    import rank_latent_routing_amd as fl
+    d = w.dtype
+    K, V, S = fl.flarepp_project(_dev(bi.X, d), _wdev(bi.Wk, d), _wdev(bi.Wv, d), _wdev(bi.Ws, d), w.H,
+                                 bk=_dev(bi.bk, d) if with_bias else None, bv=_dev(bi.bv, d) if with_bias else None,
+                                 bs=_dev(bi.bs, d) if with_bias else None, nk=_dev(bi.nk, d) if with_scale else None)
+    torch.cuda.synchronize()
+    return _np(K), _np(V), _np(S)
+
+
+def _check_project(w, bi, with_bias=True, with_scale=True, label=""):
+    say(f"[project] {label}: B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype} bias={with_bias} scale={with_scale}")
+    got = _project_gpu(w, bi, with_bias, with_scale)
+    f = bi.f64
+    ref = oracle.project(f("X"), f("Wk"), f("Wv"), f("Ws"), w.H, f("nk") if with_scale else np.ones(w.D),
+                         f("bk") if with_bias else None, f("bv") if with_bias else None, f("bs") if with_bias else None)
+    worst = 0.0
+    for g, r, name in zip(got, ref, "KVS"):
+        for b in range(w.B):
+            for h in range(w.H):
+                worst = max(worst, _err(g[b, h], r[b, h], w.dtype, 1e-4))
+    say(f"[project] {label}: worst {worst:.3g}")
+    assert worst <= _bar(w.dtype, 1e-4)
+
+
+def test_project_cfg1_fp32():
+    w = make_workload(1)
+    _check_project(w, make_block_inputs(w), label="cfg1")
+
+
+@pytest.mark.parametrize("B,H,N,D,dtype", [
+    (2, 8, 3001, 16, "bf16"),   # C = 128, ragged token tail
+    (1, 8, 4100, 32, "bf16"),   # C = 256 (the 1M-token workload's width)
+    (1, 3, 100, 16, "bf16"),    # C = 48: a channel group straddles the projections
+    (2, 1, 33, 16, "bf16"),     # C = 16: one head, one token past a tile
+    (1, 16, 777, 32, "bf16"),   # C = 512: the widest, four-wave workgroups
+    (1, 8, 500, 32, "fp32"),    # C = 256 fp32: four-wave workgroups
+    (1, 8, 257, 16, "fp32"),    # C = 128 fp32
+    (1, 5, 65, 16, "fp32"),     # C = 80
+])
+def test_project_shapes(B, H, N, D, dtype):
+    w = make_workload(2, B=B, H=H, N=N, D=D, M=8, dtype=dtype, seed=900 + H * D + N)
+    _check_project(w, make_block_inputs(w, seed=17 + N), label=f"{dtype} C={H * D}")
+
+
+def test_project_without_bias_or_scale():
+    w = make_workload(4, B=1, H=8, N=1000, M=8)
+    bi = make_block_inputs(w, seed=5)
+    _check_project(w, bi, with_bias=False, with_scale=False, label="no bias, unit scale")
+
+
+def test_project_identity_init():
+    # The pages' near-identity initialization (the benchmark's weights).
+    w = make_workload(5, H=8, N=3000, M=8)
+    _check_project(w, make_block_inputs(w, init="identity"), label="identity init")
+
+
+def _check_out_project(w, Y, Wo, bo, label=""):
+    import rank_latent_routing_amd as fl
+    say(f"[out_project] {label}: B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype}")
+    d = w.dtype
+    got = _np(fl.flarepp_out_project(_dev(Y, d), _wdev(Wo, d), _dev(bo, d)))
+    torch.cuda.synchronize()
+    ref = oracle.out_project(to_float64(Y, d), to_float64(Wo, d), None if bo is None else to_float64(bo, d))
+    worst = max(_err(got[b], ref[b], d, 1e-4) for b in range(w.B))
+    say(f"[out_project] {label}: worst {worst:.3g}")
+    assert worst <= _bar(d, 1e-4)
+
+
+@pytest.mark.parametrize("B,H,N,D,dtype", [(1, 2, 1024, 16, "fp32"), (2, 8, 3001, 16, "bf16"),
+                                           (1, 8, 4100, 32, "bf16"), (1, 3, 100, 16, "bf16"),
+                                           (1, 16, 300, 32, "bf16"), (1, 8, 300, 32, "fp32")])
+def test_out_project_shapes(B, H, N, D, dtype):
+    from workloads import make_cotangent
+    w = make_workload(2, B=B, H=H, N=N, D=D, M=8, dtype=dtype, seed=1300 + N)
+    bi = make_block_inputs(w, seed=23 + N)
+    Y = make_cotangent(w, seed=31 + N)  # a seeded N(0, 1) tensor of Y's shape and dtype
+    _check_out_project(w, Y, bi.Wo, bi.bo, label=f"{dtype} C={H * D}")
+    _check_out_project(w, Y, bi.Wo, None, label=f"{dtype} C={H * D} no bias")
+
+
+def _block_gpu(w, bi, workspace=False):
+    import rank_latent_routing_amd as fl
+    d = w.dtype
+    args = [_dev(bi.X, d), _wdev(bi.Wk, d), _wdev(bi.Wv, d), _wdev(bi.Ws, d), _wdev(bi.Wo, d), _dev(w.Qseed, d),
+            _dev(w.Qf, d), torch.from_numpy(bi.gamma).cuda()]
+    kw = dict(bk=_dev(bi.bk, d), bv=_dev(bi.bv, d), bs=_dev(bi.bs, d), bo=_dev(bi.bo, d), nq=_dev(bi.nq, d),
+              nk=_dev(bi.nk, d))
+    if workspace:
+        need = fl.flarepp_block_workspace_bytes(w.B, w.H, w.N, w.M, w.D, 1 if d == "bf16" else 0)
+        kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = fl.flarepp_block(*args, **kw)
+    torch.cuda.synchronize()
+    return _np(out)
+
+
+def _check_block(w, bi, label=""):
+    say(f"[block] {label}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    got = _block_gpu(w, bi)
+    f = bi.f64
+    ref = oracle.mixer_block(f("X"), f("Wk"), f("Wv"), f("Ws"), f("Wo"), w.f64("Qseed"), w.f64("Qf"), f("gamma"),
+                             f("nq"), f("nk"), f("bk"), f("bv"), f("bs"), f("bo"), block=4096)["out"]
+    assert np.isfinite(got).all()
+    worst = max(_err(got[b], ref[b], w.dtype, 2e-2) for b in range(w.B))
+    say(f"[block] {label}: worst {worst:.3g}")
+    assert worst <= _bar(w.dtype, 2e-2)
+    return got
+
+
+def test_block_cfg1_fp32():
+    w = make_workload(1)
+    _check_block(w, make_block_inputs(w), label="cfg1")
+
+
+def test_block_cfg2_shape_bf16():
+    w = make_workload(2, B=2, H=8, N=5000)
+    _check_block(w, make_block_inputs(w), label="cfg2 N=5000")
+
+
+def test_block_cfg4_shape_bf16_m300():
+    w = make_workload(4, B=1, H=8, N=20000, M=300)
+    _check_block(w, make_block_inputs(w, seed=3), label="cfg4 N=20000 M=300")
+
+
+def test_block_cfg5_shape_identity_init():
+    # The 1M-token workload's head shape (H = 8, D = 32, M = 512) at 65536 tokens, with the pages'
+    # near-identity projections.
+    w = make_workload(5, N=65536)
+    _check_block(w, make_block_inputs(w, init="identity"), label="cfg5 N=65536 identity")
+
+
+def test_block_odd_heads_fp32():
+    w = make_workload(1, B=2, H=3, N=333, M=17, D=16, seed=44)
+    _check_block(w, make_block_inputs(w, seed=45), label="fp32 H=3")
+
+
+def test_block_entry_points_agree_and_are_deterministic():
+    w = make_workload(2, B=1, H=8, N=3000, M=40, seed=8)
+    bi = make_block_inputs(w, seed=9)
+    a = _block_gpu(w, bi)
+    b = _block_gpu(w, bi, workspace=True)
+    c = _block_gpu(w, bi)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_full_size_projection_sampled_rows():
+    # The 1M-token workload's shape and the benchmark's launch configuration; 3000 sampled tokens.
+    import rank_latent_routing_amd as fl
+    # Only the shape and input family enter the block inputs (the mixer's own tensors are not needed).
+    w = types.SimpleNamespace(B=1, H=8, N=1 << 20, D=32, dtype="bf16", kind="surface")
+    bi = make_block_inputs(w, init="identity")
+    say(f"[project] full size: N={w.N} C={w.H * w.D}")
+    d = w.dtype
+    K, V, S = fl.flarepp_project(_dev(bi.X, d), _wdev(bi.Wk, d), _wdev(bi.Wv, d), _wdev(bi.Ws, d), w.H,
+                                 bk=_dev(bi.bk, d), bv=_dev(bi.bv, d), bs=_dev(bi.bs, d), nk=_dev(bi.nk, d))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1).choice(w.N, 3000, replace=False))
+    rows = np.concatenate([rows, [0, w.N - 1]])
+    f = bi.f64
+    Xr = to_float64(bi.X[:, rows], d)
+    ref = oracle.project(Xr, f("Wk"), f("Wv"), f("Ws"), w.H, f("nk"), f("bk"), f("bv"), f("bs"))
+    idx = torch.from_numpy(rows).cuda()
+    worst = 0.0
+    for g, r in zip((K, V, S), ref):
+        gs = _np(g[:, :, idx])
+        for h in range(w.H):
+            worst = max(worst, _err(gs[0, h], r[0, h], d, 1e-4))
+    say(f"[project] full size: worst {worst:.3g}")
+    assert worst <= 1e-4

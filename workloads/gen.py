@@ -94,6 +94,7 @@ class Workload:
     Qseed: np.ndarray
     Qf: np.ndarray
     g: np.ndarray
+    kind: str = "gauss"
 
     def f64(self, field: str) -> np.ndarray:
         """Exact float64 values of one stored tensor."""
@@ -172,7 +173,7 @@ def make_workload(cfg: int, *, B: int | None = None, H: int | None = None, N: in
     if g is not None:
         gv = np.broadcast_to(np.asarray(g, dtype=np.float32), (H,)).copy()
     name = f"cfg{cfg}" + ("-peaked" if peaked else "")
-    return Workload(name, B, H, N, M, D, dtype, K, V, S, Qseed, Qf, gv)
+    return Workload(name, B, H, N, M, D, dtype, K, V, S, Qseed, Qf, gv, kind)
 
 
 def make_cotangent(w: Workload, seed: int | None = None) -> np.ndarray:
@@ -187,3 +188,72 @@ def make_synthesis_values(w: Workload, seed: int | None = None) -> np.ndarray:
     of shape [B, H, N, D], cast to the workload's storage dtype like the inputs."""
     rng = np.random.Generator(np.random.PCG64(workload_seed(0) + 104729 if seed is None else seed))
     return _store(rng.standard_normal((w.B, w.H, w.N, w.D)), w.dtype)
+
+
+@dataclasses.dataclass
+class BlockInputs:
+    """Inputs of the mixer block around a workload: X [B, N, C] (C = H D), the projection matrices
+    Wk, Wv, Ws, Wo [C, C] in the pages' orientation (the block computes X W), biases bk, bv, bs, bo [C],
+    the key and seed scales nk, nq [D] (stored like the tensors), and the gate logits gamma [H]
+    (float32). The routing seeds and fixed queries are the workload's Qseed and Qf."""
+    X: np.ndarray
+    Wk: np.ndarray
+    Wv: np.ndarray
+    Ws: np.ndarray
+    Wo: np.ndarray
+    bk: np.ndarray
+    bv: np.ndarray
+    bs: np.ndarray
+    bo: np.ndarray
+    nk: np.ndarray
+    nq: np.ndarray
+    gamma: np.ndarray
+    dtype: str
+
+    def f64(self, field: str) -> np.ndarray:
+        if field == "gamma":
+            return self.gamma.astype(np.float64)
+        return to_float64(getattr(self, field), self.dtype)
+
+
+def make_block_inputs(w: Workload, init: str = "random", seed: int | None = None) -> BlockInputs:
+    """Seeded block inputs of the workload's shape and family.
+
+    X: ``gauss`` draws N(0, 1); the mesh kinds draw fresh points of their family and embed the same
+    11 features phi(x) with a pointwise input projection W_in in R^{11 x C} of N(0, 1/11) entries.
+    ``init="identity"`` is the pages' initialization of the feature projections (W = I + Delta W,
+    Delta W ~ N(0, 0.02^2) truncated at two standard deviations, zero biases, unit scales, gate logits
+    0.25); the output projection gets the same form. ``init="random"`` draws dense N(0, 1/C) matrices,
+    N(0, 0.1^2) biases, scales 1 + N(0, 0.2^2) and gate logits N(0.25, 1), so that no projection is
+    close to a symmetric one.
+    """
+    C = w.H * w.D
+    rng = np.random.Generator(np.random.PCG64(workload_seed(0) + 15485863 if seed is None else seed))
+    kind = w.kind
+    if kind == "gauss":
+        X = rng.standard_normal((w.B, w.N, C))
+    else:
+        freqs = rng.normal(0.0, 2.0, size=(8, 3))
+        w_in = rng.standard_normal((11, C)) / math.sqrt(11.0)
+        X = np.empty((w.B, w.N, C))
+        for b in range(w.B):
+            pts = rng.random((w.N, 3)) if kind == "cube" else _sphere_surface_points(rng, w.N)
+            X[b] = np.concatenate([pts, np.sin(pts @ freqs.T)], axis=1) @ w_in
+    if init == "identity":
+        def mat():
+            d = rng.standard_normal((C, C)) * 0.02
+            return np.eye(C) + np.clip(d, -0.04, 0.04)
+        Ws = [mat() for _ in range(4)]
+        bias = [np.zeros(C) for _ in range(4)]
+        nk, nq = np.ones(w.D), np.ones(w.D)
+        gamma = np.full(w.H, 0.25)
+    elif init == "random":
+        Ws = [rng.standard_normal((C, C)) / math.sqrt(C) for _ in range(4)]
+        bias = [rng.standard_normal(C) * 0.1 for _ in range(4)]
+        nk, nq = 1.0 + 0.2 * rng.standard_normal(w.D), 1.0 + 0.2 * rng.standard_normal(w.D)
+        gamma = 0.25 + rng.standard_normal(w.H)
+    else:
+        raise ValueError(f"unknown init {init!r}")
+    st = lambda a: _store(a, w.dtype)
+    return BlockInputs(st(X), *(st(m) for m in Ws), *(st(b) for b in bias), st(nk), st(nq),
+                       gamma.astype(np.float32), w.dtype)
