@@ -6,12 +6,15 @@ bf16 inputs with fp32 accumulation, inputs resident in HBM. The JSON line report
 the achieved TFLOP/s (12 N M D flops per head), per-kernel event timings, the roofline position of
 the dominant kernel and the float64 CPU oracle timed on a bounded sample of the same workload.
 
-Plain FLARE and simplified FLARE++ on the same workload ("variants") and the backward pass
+Plain FLARE and simplified FLARE++ on the same workload ("variants"), the backward pass
 (flarepp_mix_backward with a seeded output cotangent, the forward recomputed inside it; "backward")
-are timed afterwards, each in a region of its own.
+and the whole block (flarepp_block: projections of a seeded input X [B, N, H D] with the pages'
+near-identity weights, the mixer, the output projection; "block") are timed afterwards, each in a
+region of its own.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
                       [--cpu-sample-heads H] [--copy-calibration] [--no-backward] [--no-variants]
+                      [--no-block]
 """
 import argparse
 import json
@@ -83,6 +86,7 @@ def _parse():
     ap.add_argument("--cpu-sample-heads", type=int, default=2)
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true", help="skip plain FLARE and simplified FLARE++")
+    ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer + output projection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (a reference "
                          "dispatch for scaling the HBM byte counters of a profile)")
@@ -221,6 +225,63 @@ def backward(args, w, dev, dt_code, peak):
                          "flops_per_launch": dom_flops}}
 
 
+BLOCK_KERNELS = ["block_params", "project", "synthesis_partial", "merge_gate", "encode_partial", "merge", "decode",
+                 "out_project"]
+
+
+def block(args, w, dt_code):
+    """The block (flarepp_block_ws) on a seeded input X of the workload's shape and family with the
+    pages' near-identity projection weights: per-kernel event timings, and the projection kernels'
+    position against the HBM roofline on their algorithmic bytes (X read once, K, V, S written once,
+    the weights read once; the output projection: Y read once, out written once)."""
+    import numpy as np
+    import torch
+
+    import rank_latent_routing_amd as fl
+    from workloads import make_block_inputs
+
+    bi = make_block_inputs(w, init="identity")
+
+    def dev(arr, transpose=False):
+        a = np.ascontiguousarray(arr.T if transpose else arr)
+        return (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" else torch.from_numpy(a)).cuda()
+
+    X = dev(bi.X)
+    Wk, Wv, Ws, Wo = (dev(m, True) for m in (bi.Wk, bi.Wv, bi.Ws, bi.Wo))
+    bk, bv, bs, bo, nq, nk = (dev(v) for v in (bi.bk, bi.bv, bi.bs, bi.bo, bi.nq, bi.nk))
+    Qs, Qf = dev(w.Qseed), dev(w.Qf)
+    gamma = torch.from_numpy(bi.gamma).cuda()
+    out = torch.empty_like(X)
+    ws = torch.empty(fl.flarepp_block_workspace_bytes(w.B, w.H, w.N, w.M, w.D, dt_code), dtype=torch.uint8,
+                     device="cuda")
+    del bi
+    call = lambda: fl.flarepp_block(X, Wk, Wv, Ws, Wo, Qs, Qf, gamma, bk=bk, bv=bv, bs=bs, bo=bo, nq=nq, nk=nk,
+                                    out=out, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    fl.flarepp_timing_enable(True)
+    fl.flarepp_timing_read()
+    ms = _time_steps(argparse.Namespace(warmup=0, steps=args.steps), call)
+    fl.flarepp_timing_enable(False)
+    per_kernel = fl.flarepp_timing_read()
+    kern = {k: per_kernel[k][0] / max(per_kernel[k][1], 1) for k in BLOCK_KERNELS}
+    es = 2 if w.dtype == "bf16" else 4
+    C = w.H * w.D
+    big = float(w.B) * w.N * C * es
+    proj_bytes = 4 * big + 3 * C * C * es
+    outp_bytes = 2 * big + C * C * es
+    proj_flops = 2.0 * w.B * w.N * C * 3 * C
+    gbs = proj_bytes / (kern["project"] * 1e-3) * 1e-9
+    return {"ms_per_step": ms, "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "tokens*heads/s",
+            "kernels": {k: round(v, 4) for k, v in kern.items()},
+            "project_roofline": {"bound": "hbm", "kernel": "project", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                 "algorithmic_bytes_per_launch": proj_bytes, "kernel_ms": round(kern["project"], 4),
+                                 "mfma_tflops": round(proj_flops / (kern["project"] * 1e-3) * 1e-12, 1)},
+            "out_project_gbs": round(outp_bytes / (kern["out_project"] * 1e-3) * 1e-9, 1)}
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -326,6 +387,8 @@ def main():
         res["variants"] = variants(args, w, dev, dt_code)
     if not args.no_backward:
         res["backward"] = backward(args, w, dev, dt_code, peak)
+    if not args.no_block:
+        res["block"] = block(args, w, dt_code)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
     print(json.dumps(res), flush=True)

@@ -202,7 +202,7 @@ size_t partial_lds_bytes(int dtype, int D, int plan);
 // Out = X W^T per 32-token tile; each wave keeps the weight rows of its 32-channel output group in
 // registers. Front end: X [B][N][C] -> K = N_a(X Wk^T + bk), V = X Wv^T + bv, S = X Ws^T + bs, each
 // [B][H][N][D]. Output projection: Y [B][H][N][D] (heads concatenated) -> Y Wo^T + bo, [B][N][C].
-constexpr int kProjTile = 32;   // tokens per LDS stage
+constexpr int kProjTile = 64;   // tokens per LDS stage (two 32-token blocks)
 struct ProjArgs {
   const void* X;        // front end: X [B][N][C]; output projection: Y [B][H][N][D]
   const void* W[3];     // [C][C] each, row o = the weights of output channel o (torch Linear layout)
@@ -213,7 +213,7 @@ struct ProjArgs {
   int nproj;            // 3 (front end) or 1
   int ngb;              // workgroups sharing one token range (one 32-channel group per wave)
   int64_t N;
-  int ntiles;           // 32-token tiles per batch element
+  int ntiles;           // kProjTile-token tiles per batch element
   int tiles_per_wg;     // tiles per token range
   int nranges;          // token ranges per batch element
   int nwg;              // workgroups with work; the grid rounds it up to a multiple of 8
