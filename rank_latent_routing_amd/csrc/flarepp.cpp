@@ -627,9 +627,10 @@ ProjPlan make_proj_plan(int B, int H, int64_t N, int D, int dtype, int nproj) {
   const int64_t groups = ceil_div((int64_t)nproj * C, 32);
   const int64_t ngb = ceil_div(groups, (int64_t)flarepp::proj_waves(dtype, C));
   const int64_t ntiles = ceil_div(N, flarepp::kProjTile);
-  // About 1024 workgroups (one or two per CU at a time, several rounds); at least 8 tiles each so
-  // that a workgroup's weight loads stay small against its token work.
-  const int64_t target = env_int("FLAREPP_PROJECT_WORKGROUPS", 1024);
+  // About 2048 workgroups (one per CU at a time, eight rounds: shorter token ranges even out the
+  // finish); at least 8 tiles each so that a workgroup's weight loads stay small against its token
+  // work.
+  const int64_t target = env_int("FLAREPP_PROJECT_WORKGROUPS", 2048);
   int64_t tpw = ceil_div((int64_t)B * ntiles * ngb, target);
   if (tpw < 8) tpw = 8;
   const int64_t nranges = ceil_div(ntiles, tpw);

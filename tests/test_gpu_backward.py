@@ -4,10 +4,11 @@ decode, encode and synthesis calls (Section 3.2, Eq. 6 and Eq. 8), through the g
 N0 (Eq. 5).
 
 Bars, per tensor: fp32 max|x - x_ref| / max|x_ref| <= 1e-5 (the forward pass's bar). bf16: every
-element within 2e-2 RMS(x_ref) + 2^-8 |x_ref|. The cotangents are stored in bf16, whose rounding alone
-moves an element by up to 2^-9 of itself, and they are heavy-tailed (single elements reach 30 times
-the tensor's RMS), so a bar on 2e-2 RMS alone would fail on storage; 2^-8 |x_ref| is that rounding
-with one more of the same size (the forward's bar for its heavy-tailed outputs has the same form).
+element within 2e-2 RMS(x_ref) + 2^-8 |x_ref|. The cotangents are stored in bf16, whose rounding to
+nearest alone moves an element by up to 2^-8 of itself (the unit roundoff of an 8-bit significand),
+and they are heavy-tailed (single elements reach 30 times the tensor's RMS), so a bar on 2e-2 RMS
+alone would fail on storage; 2^-8 |x_ref| is that storage rounding (the forward's bar for its
+heavy-tailed outputs has the same form).
 dK, dV, dS per (b, h) slice; dQseed and dQf (summed over the batch) per head; dg per head against
 sum_b sum_{m,d} |dQ Qd|, the size of the terms it sums, so that cancellation among them neither
 loosens nor tightens the bar.
