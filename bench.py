@@ -46,31 +46,34 @@ BWD_FLOPS_PER_NMD = {"synthesis_partial": 4, "encode_partial": 4, "bwd_token_dec
 # The forward kernels' sources, in the order their bytes enter the profile's fingerprint.
 KERNEL_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n in ("kernels.hip", "device.h")]
 PROFILE = os.path.join(ROOT, "profiles", "flarepp_mixer_1M_tokens.md")
+# The projection kernel's sources and the block's counter summary.
+PROJECT_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n in ("project.hip", "device.h")]
+BLOCK_PROFILE = os.path.join(ROOT, "profiles", "flarepp_block_1M_tokens.md")
 
 
-def kernel_source_hash():
-    """sha256 over the forward kernel sources (kernels.hip, then device.h)."""
+def kernel_source_hash(srcs=None):
+    """sha256 over kernel sources (default: the forward's, kernels.hip then device.h)."""
     import hashlib
     h = hashlib.sha256()
-    for src in KERNEL_SRCS:
+    for src in srcs or KERNEL_SRCS:
         with open(src, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def profiled_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary: FETCH_SIZE and
+def profiled_traffic(kernel, profile=PROFILE, key="forward_sources_sha256", srcs=None):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter summary: FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch) scaled by the factors a 256 MiB device copy measured in the same
     runs. None when the summary is missing or was taken on a different kernel source."""
     try:
-        lines = open(PROFILE).read().splitlines()
+        lines = open(profile).read().splitlines()
     except OSError:
         return None
     rec = None
     for ln in lines:
         if ln.startswith("traffic-json: "):
             rec = json.loads(ln[len("traffic-json: "):])
-    if not rec or rec.get("forward_sources_sha256") != kernel_source_hash():
+    if not rec or rec.get(key) != kernel_source_hash(srcs):
         return None
     k = rec.get("per_launch_bytes", {}).get(kernel)
     return None if k is None else float(k)
@@ -276,7 +279,9 @@ def block(args, w, dt_code):
     return {"ms_per_step": ms, "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "tokens*heads/s",
             "kernels": {k: round(v, 4) for k, v in kern.items()},
             "project_roofline": {"bound": "hbm", "kernel": "project", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "traffic": profiled_traffic("project", BLOCK_PROFILE, "project_sources_sha256",
+                                                             PROJECT_SRCS) if args.config == 5 else None,
                                  "algorithmic_bytes_per_launch": proj_bytes, "kernel_ms": round(kern["project"], 4),
                                  "mfma_tflops": round(proj_flops / (kern["project"] * 1e-3) * 1e-12, 1)},
             "out_project_gbs": round(outp_bytes / (kern["out_project"] * 1e-3) * 1e-9, 1)}
