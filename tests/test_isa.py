@@ -16,7 +16,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "rank_latent_routing_amd", "csrc")
-SOURCES = [os.path.join(CSRC, n) for n in ("kernels.hip", "backward.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("kernels.hip", "backward.hip", "project.hip")]
 
 
 @pytest.fixture(scope="module")
