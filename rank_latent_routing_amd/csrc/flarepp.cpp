@@ -205,7 +205,7 @@ int validate_pointers(const void* K, const void* V, const void* S, const void* Q
 struct Saved {
   float* lsyn = nullptr;  // [BH][Mp32] synthesis, per latent
   float* lenc = nullptr;  // [BH][Mp32] encode, per latent
-  bool exact = false;     // split-N partials on the exact (hi/lo, running maximum) path
+  bool hilo = false;      // split-N partials with hi/lo query logits on every pass (the backward's)
   bool no_decode = false; // stop after the encode merge
 };
 
@@ -227,7 +227,7 @@ int enqueue(const void* K, const void* V, const void* S, const void* Qseed, cons
   flarepp::PartialArgs pa{};
   pa.K = S; pa.V = S; pa.Q = Qseed; pa.H = H; pa.Mq = M; pa.Mp = p.Mp16; pa.N = N;
   pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
-  pa.force_exact = (g_force_exact.load() || sv.exact) ? 1 : 0; pa.part_l = pl; pa.part_m = pm;
+  pa.force_exact = g_force_exact.load() ? 1 : 0; pa.hilo = sv.hilo ? 1 : 0; pa.part_l = pl; pa.part_m = pm;
   if (run_kernel(0, st, [&] { return flarepp::launch_partial(pa, dtype, D, true, p.part_plan, gx_part, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
@@ -253,7 +253,7 @@ int enqueue_routing(const void* K, const void* V, int64_t N, int M, int D, int d
   flarepp::PartialArgs pa{};
   pa.K = K; pa.V = V; pa.Q = qbuf; pa.H = p.H; pa.Mq = p.Mp32; pa.Mp = p.Mp16; pa.N = N;
   pa.chunk = p.chunk; pa.nchunk = p.nchunk; pa.nlg = p.nlg; pa.part_acc = acc;
-  pa.force_exact = (g_force_exact.load() || sv.exact) ? 1 : 0; pa.part_l = pl; pa.part_m = pm;
+  pa.force_exact = g_force_exact.load() ? 1 : 0; pa.hilo = sv.hilo ? 1 : 0; pa.part_l = pl; pa.part_m = pm;
   if (run_kernel(2, st, [&] { return flarepp::launch_partial(pa, dtype, D, false, p.part_plan, p.part_gx, p.BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
@@ -393,7 +393,8 @@ int simplified_common(const void* K, const void* V, const void* Sk, const void* 
 
 // ---- Backward pass
 //
-// The synthesis and encode calls are recomputed on the exact path with their normalizers kept, Z
+// The synthesis and encode calls are recomputed with hi/lo query logits (the backward kernels'
+// logits) and their normalizers kept, Z
 // is centered, and the decode kernel forms every token's statistics and the decode call's part of
 // dK; then, per routing call in reverse order (Appendix B.5, Eq. 46-49): the latent-side partials
 // and their reduction for the decode call (dZ, dQ_dec) and the encode call (dQ_enc, then the gate),
@@ -488,7 +489,7 @@ int enqueue_backward(const void* K, const void* V, const void* S, const void* Qs
   Saved sv;
   sv.lsyn = F(p.off_lsyn);
   sv.lenc = F(p.off_lenc);
-  sv.exact = true;
+  sv.hilo = true;
   sv.no_decode = true;
   int rc = enqueue(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, nullptr, F(p.off_qd), nullptr, F(p.off_z32), ws,
                    p.f, st, sv);

@@ -47,6 +47,8 @@ struct PartialArgs {
   int nchunk;      // chunks per (b, h)
   int nlg;         // latent groups per chunk (workgroups sharing one chunk's tokens)
   int force_exact; // skip the zero-shift pass (test hook)
+  int hilo;        // bf16, D = 32: skip the fp16 wide zero-shift pass, so the logits use the hi/lo
+                   // queries on every pass (the zero-shift one first, the exact one if it fails)
   float* part_acc; // [BH][nchunk][Mp][D]
   float* part_l;   // [BH][nchunk][Mp]
   float* part_m;   // [BH][nchunk][Mp]

@@ -263,7 +263,10 @@ __device__ __forceinline__ int perm_row(int r, int half) { return 8 * (r >> 2) +
 // A chunk is first streamed with shift 0 (no running maximum). That is exact whenever no
 // exponential overflowed and every term that matters stayed a normal float, which the kernel checks
 // afterwards on every row: l in [2^-80, 2^100] and a finite accumulator. If any row of the workgroup
-// fails, the whole chunk is streamed again with exact running maxima (online softmax).
+// fails, the whole chunk is streamed again with exact running maxima (online softmax). bf16 runs
+// with D = 32 take that first pass on fp16 score operands; with `hilo` set they take it with the
+// bf16 keys against the hi/lo query pair instead, the logits of the exact pass and of the
+// backward kernels, so that the normalizers they leave match those logits.
 //
 // Grid: x enumerates (chunk, latent group) so that the latent groups of one chunk land on the same
 // XCD (workgroups are dealt to the 8 XCDs round-robin by x) and share its L2; y = b * H + h.
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   }
   const int64_t pbase = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp;
   if constexpr (kWide) {
-    if (!exact) {
+    if (!exact && !a.hilo) {
       run_chunk_wide();
       if constexpr (NB == 1) {
         // Latent j = l % 32 sums to row j % 16, columns 0-7 (j < 16) or 8-15 (j >= 16): lane
