@@ -151,11 +151,6 @@ struct Frag<bf16> {
     for (int e = 0; e < 8; e++) x[e] = (float)o[e];
   }
   __device__ static Op gload(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  // Elements col .. col + 7 of row r of a swizzled tile.
-  template <int D>
-  __device__ static Op row(const bf16* tile, int r, int col) {
-    return *reinterpret_cast<const bf16x8*>(tile + Swz<bf16, D>::off(r, col));
-  }
   // The row operand of 32-row block `blk` (lane offsets o), k block kk.
   template <int D>
   __device__ static Op row_at(const bf16* blk, const LaneOffs<bf16, D>& o, int kk) {
@@ -175,23 +170,6 @@ struct Frag<bf16> {
       r[4 + e] = hi[e];
     }
     return r;
-  }
-  // A operand along the tile's rows: lane l gets rows r0 + row32(e, l / 32) of column l % 32 (D = 16:
-  // column l % 16; the upper 16 result rows then repeat the lower ones and are not used).
-  template <int D>
-  __device__ static Op krows(const bf16* tile, int r0, int lane) {
-    using S = Swz<bf16, D>;
-    const int i = lane & 15, cb = ((lane >> 4) & 1) & (D / 16 - 1), hh = lane >> 5;
-    const int r = r0 + 4 * hh + (i >> 2), col = 16 * cb + 4 * (i & 3);
-    const bf16x4 lo = lds_read_tr4(tile + S::off(r, col));
-    const bf16x4 hi = lds_read_tr4(tile + S::off(r + 8, col));
-    Op o;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      o[e] = lo[e];
-      o[4 + e] = hi[e];
-    }
-    return o;
   }
 };
 
@@ -231,12 +209,6 @@ struct Frag<float> {
     return Op{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   template <int D>
-  __device__ static Op row(const float* tile, int r, int col) {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + Swz<float, D>::off(r, col));
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + Swz<float, D>::off(r, col + 4));
-    return Op{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  template <int D>
   __device__ static Op row_at(const float* blk, const LaneOffs<float, D>& o, int kk) {
     const f32x4 lo = *reinterpret_cast<const f32x4*>(blk + o.row[kk][0]);
     const f32x4 hi = *reinterpret_cast<const f32x4*>(blk + o.row[kk][1]);
@@ -248,14 +220,6 @@ struct Frag<float> {
 #pragma unroll
     for (int e = 0; e < 8; e++) r[e] = blk[o.kr[e]];
     return r;
-  }
-  template <int D>
-  __device__ static Op krows(const float* tile, int r0, int lane) {
-    const int hh = lane >> 5, col = (lane & 31) & (D - 1);
-    Op o;
-#pragma unroll
-    for (int e = 0; e < 8; e++) o[e] = tile[Swz<float, D>::off(r0 + row32(e, hh), col)];
-    return o;
   }
 };
 
@@ -789,7 +753,8 @@ __device__ __forceinline__ void fill_stats(float* sl, float* sc, const float* l,
 // ------------------------------------------------------------------------------------------
 // Decode call, per token (Section 3.2 Eq. 8, the softmax over latents; Appendix B.5 for the
 // cotangent). With l_nm = K_n . c Q_m and dP_nm = dY_n . Zc_m (c*Q and Zc as pairs):
-//   pass 1 (online, running maximum per lane half):  L_n = log2 sum_m 2^(l_nm),
+//   pass 1 (shift 0 with a range check, else online with a running maximum per lane half):
+//                                                     L_n = log2 sum_m 2^(l_nm),
 //                                                     c_n = sum_m 2^(l_nm - L_n) dP_nm;
 //   pass 2:  dK_dec,n = (1/sqrt(D)) sum_m P_nm (dP_nm - c_n) Q_m,  kept in fp32 for the encode kernel.
 // LDS holds c*Q and Zc (pairs).
@@ -879,34 +844,61 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
         body(nlb - 1, std::false_type{});
     };
 
-    float mrun = -INFINITY, l = 0.f, u = 0.f;
-    over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
-      f32x16 E, dP;
-      scores(lb, E, dP, MASKED);
-      float bm = E[0];
+    // The token's other 16 latents of every block are in lane l ^ 32. First pass with shift 0 (no
+    // running maximum), exact whenever no exponential overflowed and the terms that matter stayed
+    // normal floats: every token's sum in [2^-80, 2^100] and a finite u (the check of the forward
+    // passes). A wave with any token outside it takes the pass with running maxima instead.
+    float Ld = 0.f, cd = 0.f;
+    bool done = false;
+    if (!a.force_exact) {
+      float l = 0.f, u = 0.f;
+      over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
+        f32x16 E, dP;
+        scores(lb, E, dP, MASKED);
 #pragma unroll
-      for (int v = 1; v < 16; v++) bm = fmaxf(bm, E[v]);
-      const float mn = fmaxf(mrun, bm);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      const float sc = exp2_fast(mrun - ms);
-      l *= sc;
-      u *= sc;
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const float p = exp2_fast(E[v] - ms);
-        l += p;
-        u += p * dP[v];
+        for (int v = 0; v < 16; v++) {
+          const float p = exp2_fast(E[v]);
+          l += p;
+          u += p * dP[v];
+        }
+      });
+      const float lt = l + shfl_xor(l, 32), ut = u + shfl_xor(u, 32);
+      const bool ok = !valid || (lt >= 0x1p-80f && lt <= 0x1p100f && fabsf(ut) <= 3.0e38f);
+      if (__all(ok)) {
+        Ld = log2f(lt);
+        cd = ut / lt;
+        done = true;
       }
-      mrun = mn;
-    });
-    // The token's other 16 latents of every block are in lane l ^ 32.
-    const float mo = shfl_xor(mrun, 32), lo = shfl_xor(l, 32), uo = shfl_xor(u, 32);
-    const float mt = fmaxf(mrun, mo);
-    const float mts = mt == -INFINITY ? 0.f : mt;
-    const float wa = exp2_fast(mrun - mts), wb = exp2_fast(mo - mts);
-    const float lt = l * wa + lo * wb;
-    const float Ld = mts + log2f(lt);
-    const float cd = (u * wa + uo * wb) / lt;
+    }
+    if (!done) {
+      float mrun = -INFINITY, l = 0.f, u = 0.f;
+      over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
+        f32x16 E, dP;
+        scores(lb, E, dP, MASKED);
+        float bm = E[0];
+#pragma unroll
+        for (int v = 1; v < 16; v++) bm = fmaxf(bm, E[v]);
+        const float mn = fmaxf(mrun, bm);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float sc = exp2_fast(mrun - ms);
+        l *= sc;
+        u *= sc;
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const float p = exp2_fast(E[v] - ms);
+          l += p;
+          u += p * dP[v];
+        }
+        mrun = mn;
+      });
+      const float mo = shfl_xor(mrun, 32), lo = shfl_xor(l, 32), uo = shfl_xor(u, 32);
+      const float mt = fmaxf(mrun, mo);
+      const float mts = mt == -INFINITY ? 0.f : mt;
+      const float wa = exp2_fast(mrun - mts), wb = exp2_fast(mo - mts);
+      const float lt = l * wa + lo * wb;
+      Ld = mts + log2f(lt);
+      cd = (u * wa + uo * wb) / lt;
+    }
     if (valid && hh == 0) {
       a.tl[(int64_t)bh * a.N + tok] = Ld;
       a.tc[(int64_t)bh * a.N + tok] = cd;

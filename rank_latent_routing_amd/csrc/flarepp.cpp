@@ -508,7 +508,7 @@ int enqueue_backward(const void* K, const void* V, const void* S, const void* Qs
   ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
   ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
   ta.lsyn = sv.lsyn; ta.cs = F(p.off_cs); ta.dK = dK; ta.dV = dV; ta.dS = dS; ta.N = N;
-  ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H;
+  ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H; ta.force_exact = g_force_exact.load() ? 1 : 0;
   if (run_kernel(7, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokDecode, p.tok_gx, BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 

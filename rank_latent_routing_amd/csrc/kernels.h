@@ -166,6 +166,7 @@ struct BwdTokenArgs {
   int64_t N;
   int64_t tokens_per_wg;
   int M, Mp, H;
+  int force_exact;         // decode statistics: skip the zero-shift pass (test hook)
 };
 enum BwdTokenKind { kBwdTokDecode = 0, kBwdTokEncode = 1, kBwdTokSynthesis = 2 };
 
