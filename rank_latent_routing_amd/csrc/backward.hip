@@ -312,13 +312,15 @@ __device__ __forceinline__ void load4(const T* src, float* x) {
 }
 
 // Stats of 32 latents (stat_pos order) for lane half hh: the 16 values of its result slots.
-__device__ __forceinline__ void load_stats16(const float* base, int hh, float* out) {
+__device__ __forceinline__ f32x16 load_stats16(const float* base, int hh) {
+  f32x16 out;
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(base + 16 * hh + 4 * q);
 #pragma unroll
     for (int i = 0; i < 4; i++) out[4 * q + i] = v[i];
   }
+  return out;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -475,8 +477,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
     if constexpr (DEC) {
       if (tid < ST) {
         const int p = stat_pos(tid);
-        tst[(2 * buf) * ST + p] = tsl;
-        tst[(2 * buf + 1) * ST + p] = tsc;
+        tst[(2 * buf) * ST + p] = -tsl;  // negated: the decode products start from -L and -c
+        tst[(2 * buf + 1) * ST + p] = -tsc;
       }
     }
   };
@@ -489,7 +491,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
 #pragma unroll
     for (int sub = 0; sub < ST / 32; sub++) {
       const int r0 = 32 * sub;
+      // Decode: the products start from the tokens' -L and -c (negated in LDS), so they come out
+      // as l - L and dP - c; the other calls subtract the latent's scalars below.
       f32x16 s = {}, dp = {};
+      if constexpr (DEC) {
+        s = load_stats16(tst + (2 * buf) * ST + r0, hh);
+        dp = load_stats16(tst + (2 * buf + 1) * ST + r0, hh);
+      }
       if constexpr (SYN) {
         Pair xa[KB];
 #pragma unroll
@@ -518,19 +526,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
           hold(dp, wa[kk]);
         }
       }
-      float Lt[16], Ct[16];
-      if constexpr (DEC) {
-        load_stats16(tst + (2 * buf) * ST + r0, hh, Lt);
-        load_stats16(tst + (2 * buf + 1) * ST + r0, hh, Ct);
-      }
       f32x16 P, dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        float p = exp2_fast(s[v] - (DEC ? Lt[v] : Ll));
+        float p = exp2_fast(DEC ? s[v] : s[v] - Ll);
         if constexpr (decltype(MASKED)::value)
           if (r0 + row32(v, hh) >= nvalid) p = 0.f;
         P[v] = p;
-        dS[v] = p * (dp[v] - (DEC ? Ct[v] : Lc));
+        dS[v] = p * (DEC ? dp[v] : dp[v] - Lc);
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
@@ -743,10 +746,11 @@ __device__ __forceinline__ void fill_blocked(T* lds, int j, const T* src, int st
 }
 template <int NT>
 __device__ __forceinline__ void fill_stats(float* sl, float* sc, const float* l, const float* c, int Mp) {
+  // Negated: the score and dP products start from -L and -c, so they come out as l - L and dP - c.
   for (int m = threadIdx.x; m < Mp; m += NT) {
     const int p = stat_pos(m);
-    sl[p] = l[m];
-    sc[p] = c[m];
+    sl[p] = -l[m];
+    sc[p] = -c[m];
   }
 }
 
@@ -994,7 +998,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
     f32x16 accK = {}, accV = {};
     for (int lb = 0; lb < nlb; lb++) {
       Pair qa[KB], za[KB];
-      f32x16 E = {}, dP = {};
+      // Latents past M: zero rows of c*Q and dZ, L = +inf, c = 0, so P and dS vanish there. The
+      // products start from -L and -c (negated in LDS): E = l - L, dP = dP - c.
+      f32x16 E = load_stats16(sl + 32 * lb, hh), dP = load_stats16(sc + 32 * lb, hh);
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
         qa[kk] = row_pair_at<F, D>(tile(lb, TQH), tile(lb, TQL), lofs, kk);
@@ -1009,16 +1015,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
         hold<F>(dP, za[kk]);
         hold(dP, vb[kk]);
       }
-      // Latents past M: zero rows of c*Q and dZ, L = +inf, c = 0, so P and dS vanish there.
-      float Le[16], Ce[16];
-      load_stats16(sl + 32 * lb, hh, Le);
-      load_stats16(sc + 32 * lb, hh, Ce);
       f32x16 P, dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const float p = exp2_fast(E[v] - Le[v]);
+        const float p = exp2_fast(E[v]);
         P[v] = p;
-        dS[v] = p * (dP[v] - Ce[v]);
+        dS[v] = p * dP[v];
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
@@ -1125,7 +1127,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
     for (int lb = 0; lb < nlb; lb++) {
       Op qa[KB];
       Pair ga[KB];
-      f32x16 A = {}, dP = {};
+      // The products start from -L and -c (negated in LDS): A = l - L, dP = dP - c.
+      f32x16 A = load_stats16(sl + 32 * lb, hh), dP = load_stats16(sc + 32 * lb, hh);
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
         qa[kk] = F::template row_at<D>(tile(lb, TQS), lofs, kk);
@@ -1140,15 +1143,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
         hold<F>(dP, ga[kk]);
         hold<F>(dP, sb[kk]);
       }
-      float Ls[16], Cs[16];
-      load_stats16(sl + 32 * lb, hh, Ls);
-      load_stats16(sc + 32 * lb, hh, Cs);
       f32x16 P, dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const float p = exp2_fast(A[v] - Ls[v]);
+        const float p = exp2_fast(A[v]);
         P[v] = p;
-        dS[v] = p * (dP[v] - Cs[v]);
+        dS[v] = p * dP[v];
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
