@@ -415,6 +415,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
       Lc = a.lc[(int64_t)bh * a.Mp + lrow];
     }
   }
+  // Encode and synthesis: the lane's latent has one L and one c; the products start from them
+  // (negated, in every slot), so they come out as l - L and dP - c.
+  f32x16 negL, negC;
+#pragma unroll
+  for (int v = 0; v < 16; v++) {
+    negL[v] = -Ll;
+    negC[v] = -Lc;
+  }
 
   Chunk rg[PER];
   float tsl = 0.f, tsc = 0.f;
@@ -491,9 +499,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
 #pragma unroll
     for (int sub = 0; sub < ST / 32; sub++) {
       const int r0 = 32 * sub;
-      // Decode: the products start from the tokens' -L and -c (negated in LDS), so they come out
-      // as l - L and dP - c; the other calls subtract the latent's scalars below.
-      f32x16 s = {}, dp = {};
+      // The products start from -L and -c: the tokens' (decode, negated in LDS) or the latent's.
+      f32x16 s = negL, dp = negC;
       if constexpr (DEC) {
         s = load_stats16(tst + (2 * buf) * ST + r0, hh);
         dp = load_stats16(tst + (2 * buf + 1) * ST + r0, hh);
@@ -529,11 +536,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
       f32x16 P, dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        float p = exp2_fast(DEC ? s[v] : s[v] - Ll);
+        float p = exp2_fast(s[v]);
         if constexpr (decltype(MASKED)::value)
           if (r0 + row32(v, hh) >= nvalid) p = 0.f;
         P[v] = p;
-        dS[v] = p * (DEC ? dp[v] : dp[v] - Lc);
+        dS[v] = p * dp[v];
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
