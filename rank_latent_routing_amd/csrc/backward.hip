@@ -822,10 +822,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
     // Logits and dP of latent block lb (C[latent][token], lane = token), masked past M.
     // MASKED: the last block when M is not a multiple of 32 (peeled, so the other blocks carry no
     // mask instructions).
-    auto scores = [&](int lb, f32x16& E, f32x16& dP, auto MASKED) __attribute__((always_inline)) {
+    auto scores = [&](int lb, f32x16& E, f32x16& dP, auto MASKED, const f32x16& e0, const f32x16& d0)
+                      __attribute__((always_inline)) {
       Pair qa[KB], za[KB];
-      E = f32x16{};
-      dP = f32x16{};
+      E = e0;
+      dP = d0;
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
         qa[kk] = row_pair_at<F, D>(tile(lb, TQH), tile(lb, TQL), lofs, kk);
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       float l = 0.f, u = 0.f;
       over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
         f32x16 E, dP;
-        scores(lb, E, dP, MASKED);
+        scores(lb, E, dP, MASKED, f32x16{}, f32x16{});
 #pragma unroll
         for (int v = 0; v < 16; v++) {
           const float p = exp2_fast(E[v]);
@@ -885,7 +886,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       float mrun = -INFINITY, l = 0.f, u = 0.f;
       over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
         f32x16 E, dP;
-        scores(lb, E, dP, MASKED);
+        scores(lb, E, dP, MASKED, f32x16{}, f32x16{});
         float bm = E[0];
 #pragma unroll
         for (int v = 1; v < 16; v++) bm = fmaxf(bm, E[v]);
@@ -915,13 +916,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       a.tc[(int64_t)bh * a.N + tok] = cd;
     }
 
+    // Second pass: the products start from the token's -L and -c (in every slot), so they come
+    // out as l - L and dP - c.
+    f32x16 negL, negC;
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      negL[v] = -Ld;
+      negC[v] = -cd;
+    }
     f32x16 accK = {};
     over_blocks([&](int lb, auto MASKED) __attribute__((always_inline)) {
       f32x16 E, dP;
-      scores(lb, E, dP, MASKED);
+      scores(lb, E, dP, MASKED, negL, negC);
       f32x16 dS;
 #pragma unroll
-      for (int v = 0; v < 16; v++) dS[v] = exp2_fast(E[v] - Ld) * (dP[v] - cd);
+      for (int v = 0; v < 16; v++) dS[v] = exp2_fast(E[v]) * dP[v];
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQL) + 16 * t * D, lofs);
