@@ -12,9 +12,13 @@ and the whole block (flarepp_block: projections of a seeded input X [B, N, H D] 
 near-identity weights, the mixer, the output projection; "block") are timed afterwards, each in a
 region of its own.
 
+Per call the line also gives the median and minimum of the K timed calls; `--cold` adds the same
+for calls that each follow a 1 GiB write (the smaller workloads' inputs otherwise stay in the
+256 MB MALL between calls).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
                       [--cpu-sample-heads H] [--copy-calibration] [--no-backward] [--no-variants]
-                      [--no-block]
+                      [--no-block] [--cold]
 """
 import argparse
 import json
@@ -90,6 +94,8 @@ def _parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true", help="skip plain FLARE and simplified FLARE++")
     ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer + output projection)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time K calls with a 1 GiB write between them (inputs out of the caches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (a reference "
                          "dispatch for scaling the HBM byte counters of a profile)")
@@ -134,9 +140,31 @@ def cpu_baseline(w, heads):
         oracle.mix_head(to_float64(w.K[0, h], w.dtype), to_float64(w.V[0, h], w.dtype), to_float64(w.S[0, h], w.dtype),
                         to_float64(w.Qseed[h], w.dtype), to_float64(w.Qf[h], w.dtype), float(w.g[h]), block=65536)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": heads * w.N / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} (b, h) slices (b=0, h<{heads}), all {w.N} tokens, M={w.M}, D={w.D}, "
-                      f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded"}
+                      f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded",
+            "host_logical_cpus": os.cpu_count(), "cpu_model": model}
+
+
+def _kernel_times(steps, call):
+    """K more calls with the library's event pairs around each kernel: {kernel: ms per launch}."""
+    import torch
+
+    import rank_latent_routing_amd as fl
+    fl.flarepp_timing_enable(True)
+    fl.flarepp_timing_read()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    fl.flarepp_timing_enable(False)
+    return {k: v[0] / max(v[1], 1) for k, v in fl.flarepp_timing_read().items()}
 
 
 def _time_steps(args, call):
@@ -197,25 +225,10 @@ def backward(args, w, dev, dt_code, peak):
                      device="cuda")
     call = lambda: fl.flarepp_mix_backward(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"], dY,
                                            grads=grads, workspace=ws)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    fl.flarepp_timing_enable(True)
-    fl.flarepp_timing_read()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        call()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fl.flarepp_timing_enable(False)
-    per_kernel = fl.flarepp_timing_read()
-    ms = max(ev0.elapsed_time(ev1), wall * 1e3) / args.steps
-    kern = {k: per_kernel[k][0] / max(per_kernel[k][1], 1) for k in BWD_KERNELS}
+    ms = _time_steps(args, call)
+    # Per-kernel durations from K more calls (events between the kernels stay out of the step time).
+    per_kernel = _kernel_times(args.steps, call)
+    kern = {k: per_kernel[k] for k in BWD_KERNELS}
     nmd = float(w.N) * w.M * w.D * w.B * w.H
     dom = max(kern, key=kern.get)
     dom_flops = BWD_FLOPS_PER_NMD.get(dom, 0) * nmd
@@ -260,15 +273,9 @@ def block(args, w, dt_code):
     del bi
     call = lambda: fl.flarepp_block(X, Wk, Wv, Ws, Wo, Qs, Qf, gamma, bk=bk, bv=bv, bs=bs, bo=bo, nq=nq, nk=nk,
                                     out=out, workspace=ws)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    fl.flarepp_timing_enable(True)
-    fl.flarepp_timing_read()
-    ms = _time_steps(argparse.Namespace(warmup=0, steps=args.steps), call)
-    fl.flarepp_timing_enable(False)
-    per_kernel = fl.flarepp_timing_read()
-    kern = {k: per_kernel[k][0] / max(per_kernel[k][1], 1) for k in BLOCK_KERNELS}
+    ms = _time_steps(args, call)
+    per_kernel = _kernel_times(args.steps, call)
+    kern = {k: per_kernel[k] for k in BLOCK_KERNELS}
     es = 2 if w.dtype == "bf16" else 4
     C = w.H * w.D
     big = float(w.B) * w.N * C * es
@@ -326,24 +333,43 @@ def main():
         call()
     torch.cuda.synchronize()
 
-    # Timed region: K steps bracketed by synchronizations, with HIP events on the library's stream
-    # around each kernel (per-kernel durations) and around the whole region.
-    fl.flarepp_timing_enable(True)
-    fl.flarepp_timing_read()
+    # Timed region: K steps bracketed by synchronizations, one HIP event on the library's stream
+    # after each step (the step durations) and the wall clock around the whole region.
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         call()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fl.flarepp_timing_enable(False)
-    per_kernel = fl.flarepp_timing_read()
-    dev_ms = ev0.elapsed_time(ev1)
+    dev_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = max(dev_ms, wall * 1e3) / args.steps
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+
+    # The same K steps again with the library's event pairs around each kernel (per-kernel
+    # durations for the roofline). Kept out of the region above: at the small workloads the
+    # events between kernels would add a visible share of each step.
+    per_kernel = _kernel_times(args.steps, call)
+
+    cold = None
+    if args.cold:
+        # Each timed call follows a 1 GiB write, which evicts the inputs from L2 and the MALL.
+        flush = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+        cms = []
+        for _ in range(args.steps):
+            flush.fill_(1.0)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            call()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            cms.append(a0.elapsed_time(a1))
+        cms.sort()
+        cold = {"ms_median": cms[len(cms) // 2], "ms_min": cms[0], "flush_bytes": 2 ** 30, "calls": len(cms)}
+        del flush
 
     tok_heads = w.B * w.H * w.N
     value = tok_heads / (ms_per_step * 1e-3)
@@ -354,7 +380,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) * 1e-12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
 
-    kern = {k: {"ms_avg": per_kernel[k][0] / max(per_kernel[k][1], 1), "launches": per_kernel[k][1]} for k in KERNELS}
+    kern = {k: {"ms_avg": per_kernel[k]} for k in KERNELS}
     dom = max(KERNELS, key=lambda k: kern[k]["ms_avg"])
     dom_ms = kern[dom]["ms_avg"]
     achieved = kernel_flops(dom, w) / (dom_ms * 1e-3) * 1e-12
@@ -374,6 +400,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_median": step_ms[len(step_ms) // 2],
+        "ms_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -388,6 +416,8 @@ def main():
         "kernels": {k: round(v["ms_avg"], 4) for k, v in kern.items()},
         "roofline": roofline,
     }
+    if cold is not None:
+        res["cold"] = cold
     if not args.no_variants:
         res["variants"] = variants(args, w, dev, dt_code)
     if not args.no_backward:
