@@ -63,6 +63,12 @@ def sdpa_tokens(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int) -> np.n
     ``block`` rows so that the [Nq, Nk] score matrix is never held whole. First pass: the row maxima
     over all keys. Second pass: the exponentials shifted by those maxima, summed and applied to v.
     Equal to ``sdpa`` up to summation order."""
+    return sdpa_tokens_stats(q, k, v, block)[0]
+
+
+def sdpa_tokens_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int):
+    """``sdpa_tokens`` that also returns the softmax's row maxima and shifted row sums, so that
+    P = exp(q k^T / sqrt(D) - max) / sum. Returns (o, row_max, den)."""
     D = q.shape[-1]
     scale = 1.0 / math.sqrt(D)
     n = k.shape[0]
@@ -75,7 +81,7 @@ def sdpa_tokens(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int) -> np.n
         e = np.exp(q @ k[a:a + block].T * scale - row_max[:, None])
         den += e.sum(axis=1)
         num += e @ v[a:a + block]
-    return num / den[:, None]
+    return num / den[:, None], row_max, den
 
 
 def synthesis(Qseed: np.ndarray, S: np.ndarray, block: int | None = None) -> np.ndarray:
@@ -178,6 +184,60 @@ def mix_head_backward(K, V, S, Qseed, Qf, g, dY) -> dict:
     return {"dK": dK_dec + dK_enc, "dV": dV, "dS": rms_normalize_backward(S, dSn_keys + dSn_values),
             "dQseed": dQseed, "dQf": rms_normalize_backward(Qf, dQ), "dg": float(np.sum(dQ * Qd)),
             "dQ": dQ, "dZ": dZ}
+
+
+def sdpa_backward_tokens(q, k, v, fwd, dout, block: int):
+    """``sdpa_backward`` for a short query set against a long key set (softmax over the keys, the
+    tokens), with the keys taken in blocks of ``block`` rows so that no [Nq, Nk] factor is held
+    whole (Appendix B.5, Eq. 46-49). ``fwd`` is the call's forward, (o, row_max, den) from
+    ``sdpa_tokens_stats``: P = exp(q k^T s - row_max) / den, and c = <dout, o>. dq sums over the
+    blocks, while dk and dv are per key row. Equal to ``sdpa_backward`` up to summation order.
+    Returns (dq, dk, dv)."""
+    s = 1.0 / math.sqrt(q.shape[-1])
+    o, row_max, den = fwd
+    dout = np.asarray(dout, dtype=np.float64)
+    c = np.sum(dout * o, axis=-1, keepdims=True)
+    dq = np.zeros(q.shape)
+    dk = np.empty(k.shape)
+    dv = np.empty((k.shape[0], dout.shape[1]))
+    for a in range(0, k.shape[0], block):
+        kb, vb = k[a:a + block], v[a:a + block]
+        P = np.exp(q @ kb.T * s - row_max[:, None]) / den[:, None]
+        dS = P * (dout @ vb.T - c)
+        dq += s * dS @ kb
+        dk[a:a + block] = s * dS.T @ q
+        dv[a:a + block] = P.T @ dout
+    return dq, dk, dv
+
+
+def mix_head_backward_blocked(K, V, S, Qseed, Qf, g, dY, block: int) -> dict:
+    """``mix_head_backward`` with the tokens taken in blocks of ``block`` rows, for token counts
+    whose [N, M] factors would not fit in memory. The same calls in the same order: the decode call
+    (rows independent: ``sdpa_backward`` per token block, its latent cotangents summed over the
+    blocks), then the encode and synthesis calls by ``sdpa_backward_tokens``, the gate and the two
+    N0's. Returns the same fields, and Qd."""
+    K, V, S = (np.asarray(x, dtype=np.float64) for x in (K, V, S))
+    dY = np.asarray(dY, dtype=np.float64)
+    Sn = rms_normalize(S)
+    syn = sdpa_tokens_stats(Qseed, Sn, Sn, block)
+    Qd = syn[0]
+    Q = gate(Qf, Qd, g)
+    enc = sdpa_tokens_stats(Q, K, V, block)
+    Z = enc[0]
+    dK_dec = np.empty(K.shape)
+    dQ_dec = np.zeros(Q.shape)
+    dZ = np.zeros(Z.shape)
+    for a in range(0, K.shape[0], block):
+        dq, dk, dv = sdpa_backward(K[a:a + block], Q, Z, dY[a:a + block])
+        dK_dec[a:a + block] = dq
+        dQ_dec += dk
+        dZ += dv
+    dQ_enc, dK_enc, dV = sdpa_backward_tokens(Q, K, V, enc, dZ, block)
+    dQ = dQ_dec + dQ_enc
+    dQseed, dSn_keys, dSn_values = sdpa_backward_tokens(Qseed, Sn, Sn, syn, float(g) * dQ, block)
+    return {"dK": dK_dec + dK_enc, "dV": dV, "dS": rms_normalize_backward(S, dSn_keys + dSn_values),
+            "dQseed": dQseed, "dQf": rms_normalize_backward(Qf, dQ), "dg": float(np.sum(dQ * Qd)),
+            "dQ": dQ, "dZ": dZ, "Qd": Qd}
 
 
 def mix_backward(K, V, S, Qseed, Qf, g, dY) -> dict:

@@ -160,6 +160,37 @@ def test_bwd_cfg5_shape_one_head():
     _check(make_workload(5, H=1, N=65536), label="cfg5 N=65536 H=1")
 
 
+def test_bwd_full_cfg5_one_head():
+    # The 1M-token workload at its full size (B = 1, H = 8, N = 2^20, M = 512), in the launch
+    # configuration the benchmark times; head 3 against the token-blocked oracle: dK, dV and dS at
+    # every token, dQseed, dQf and dg.
+    import rank_latent_routing_amd as fl
+    from workloads import to_float64
+    w = make_workload(5)
+    dY = make_cotangent(w)
+    h = 3
+    say(f"[bwd] cfg5 full: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}, GPU")
+    dev = to_device(w)
+    out = fl.flarepp_mix_backward(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"],
+                                  _device(dY, w.dtype))
+    torch.cuda.synchronize()
+    for k, v in out.items():
+        assert bool(torch.isfinite(v.float()).all()), k
+    got = {k: out[k][0, h].float().cpu().numpy().astype(np.float64) for k in ("dK", "dV", "dS")}
+    got.update({k: out[k][h].float().cpu().numpy().astype(np.float64) for k in ("dQseed", "dQf")})
+    got["dg"] = float(out["dg"][h])
+    del out, dev
+    say(f"[bwd] cfg5 full: oracle, head {h}")
+    f = lambda a: to_float64(a, w.dtype)
+    ref = oracle.mix_head_backward_blocked(f(w.K[0, h]), f(w.V[0, h]), f(w.S[0, h]), f(w.Qseed[h]), f(w.Qf[h]),
+                                           float(w.g[h]), f(dY[0, h]), 65536)
+    worst = {k: _err(got[k], ref[k], w.dtype) for k in ("dK", "dV", "dS", "dQseed", "dQf")}
+    worst["dg"] = abs(got["dg"] - ref["dg"]) / np.abs(ref["dQ"] * ref["Qd"]).sum()
+    say(f"[bwd] cfg5 full, head {h}: worst {worst} (bar {tol(w.dtype)})")
+    for k, e in worst.items():
+        assert e <= tol(w.dtype), (k, e)
+
+
 def test_bwd_determinism_and_entry_points_agree():
     w = make_workload(4, B=1, H=2, N=5000, M=200, seed=9)
     dY = make_cotangent(w)

@@ -130,3 +130,39 @@ def test_planted_backward_mistake_is_caught(monkeypatch, mutant):
         monkeypatch.setattr(O, "sdpa_backward", bad_sdpa_backward)
     with pytest.raises(AssertionError):
         test_backward_matches_torch_autograd()
+
+
+# ---- The token-blocked backward (for token counts whose [N, M] factors do not fit in memory) ----
+
+@pytest.mark.parametrize("N,block", [(3001, 512), (257, 64), (100, 1000)])
+def test_blocked_backward_equals_whole(N, block):
+    x = _inputs(20 + N, N=N, M=17, D=16)
+    a = oracle.mix_head_backward(**x)
+    b = oracle.mix_head_backward_blocked(**x, block=block)
+    for k in a:
+        ref = np.asarray(a[k])
+        assert np.abs(np.asarray(b[k]) - ref).max() <= 1e-12 * np.abs(ref).max(), k
+
+
+def test_blocked_backward_matches_torch_autograd():
+    # Pinned on its own, not only through the whole-token oracle: autograd through the torch forward.
+    x = _inputs(31, N=300, M=9, D=16)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in x.items() if k not in ("g", "dY")}
+    g = torch.tensor(x["g"], dtype=torch.float64, requires_grad=True)
+    Y = _torch_forward(t["K"], t["V"], t["S"], t["Qseed"], t["Qf"], g)
+    (Y * torch.tensor(x["dY"])).sum().backward()
+    r = oracle.mix_head_backward_blocked(**x, block=64)
+    for k, ref in (("dK", t["K"].grad), ("dV", t["V"].grad), ("dS", t["S"].grad), ("dQseed", t["Qseed"].grad),
+                   ("dQf", t["Qf"].grad)):
+        np.testing.assert_allclose(r[k], ref.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
+    assert abs(r["dg"] - g.grad.item()) <= 1e-10 * max(1.0, abs(g.grad.item()))
+
+
+def test_token_blocked_sdpa_backward_equals_whole():
+    rng = np.random.default_rng(5)
+    q, k, v, do = rng.standard_normal((7, 8)), rng.standard_normal((203, 8)), rng.standard_normal((203, 8)), \
+        rng.standard_normal((7, 8))
+    fwd = oracle.sdpa_tokens_stats(q, k, v, 50)
+    np.testing.assert_allclose(fwd[0], oracle.sdpa(q, k, v), rtol=1e-13)
+    for got, ref in zip(oracle.sdpa_backward_tokens(q, k, v, fwd, do, 50), oracle.sdpa_backward(q, k, v, do)):
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
