@@ -271,9 +271,10 @@ def mixing_matrix(Q: np.ndarray, K: np.ndarray) -> np.ndarray:
     return W_dec @ W_enc
 
 
-def flare(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
-    """Fixed-query FLARE, Section 3.1, Eq. 3: Z = SDPA(Q, K, V), Y = SDPA(K, Q, Z)."""
-    return decode(K, Q, encode(Q, K, V))
+def flare(Q: np.ndarray, K: np.ndarray, V: np.ndarray, block: int | None = None) -> np.ndarray:
+    """Fixed-query FLARE, Section 3.1, Eq. 3: Z = SDPA(Q, K, V), Y = SDPA(K, Q, Z) (tokens in blocks
+    of ``block`` rows when given)."""
+    return decode(K, Q, encode(Q, K, V, block), block)
 
 
 def simplified_mix_head(K, V, Sk, Sv, Qseed, block: int | None = None) -> dict:

@@ -263,6 +263,27 @@ def test_plain_flare(cfg, kw):
     assert worst <= tol(w.dtype)
 
 
+def test_plain_flare_full_cfg5_one_head():
+    # The 1M-token workload at its full size through flarepp_flare; head 5 against the oracle in
+    # token blocks.
+    import oracle
+    import rank_latent_routing_amd as fl
+    w = make_workload(5)
+    say(f"[full] flare {w.name}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D}")
+    dev = to_device(w)
+    Y = fl.flarepp_flare(dev["K"], dev["V"], dev["Qf"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y.float()).all())
+    h = 5
+    got = Y[0, h].float().cpu().numpy().astype(np.float64)
+    from workloads import to_float64
+    ref = oracle.flare(to_float64(w.Qf[h], w.dtype), to_float64(w.K[0, h], w.dtype), to_float64(w.V[0, h], w.dtype),
+                       block=65536)
+    err = slice_err(got, ref, w.dtype)
+    say(f"[full] flare cfg5 head {h}: err {err:.3g} (bar {tol(w.dtype)})")
+    assert err <= tol(w.dtype)
+
+
 def test_plain_flare_equals_mixer_with_gate_zero():
     # g = 0 routes with N0(Qf) alone (Section 3.2), so the mixer equals FLARE on N0(Qf); the two
     # entry points share the encode and decode kernels.

@@ -252,6 +252,7 @@ def test_blocked_evaluation_equals_whole():
     b = orc.mix_head(K, V, S, Qseed, Qf, g, block=77)
     for key in a:
         assert np.abs(a[key] - b[key]).max() < 1e-13
+    assert np.abs(orc.flare(Qf, K, V) - orc.flare(Qf, K, V, block=77)).max() < 1e-13
 
 
 def test_sharded_lse_merge_is_exact():
