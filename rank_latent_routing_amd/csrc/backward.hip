@@ -1319,30 +1319,39 @@ size_t bwd_token_lds_bytes(int dtype, int D, int Mp, int kind) {
   return D == 32 ? bwd_token_lds_t<float, 32>(Mp, kind) : bwd_token_lds_t<float, 16>(Mp, kind);
 }
 
-template <typename T, int D>
+// NW waves per workgroup for the encode and synthesis kernels; the decode kernel always runs 8 (it
+// would spill at 12, which allow at most 168 registers per lane).
+template <typename T, int D, int NW>
 static hipError_t launch_bwd_token_t(const BwdTokenArgs& a, int kind, int gx, int BH, hipStream_t st) {
-  constexpr int NW = kBwdTokenWaves;
   const size_t lds = bwd_token_lds_t<T, D>(a.Mp, kind);
-  auto go = [&](auto* fn) {
+  auto go = [&](auto* fn, int nw) {
     hipError_t e = allow_lds_bwd(fn, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(gx, BH), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL(fn, dim3(gx, BH), dim3(nw * 64), lds, st, a);
     return hipGetLastError();
   };
   switch (kind) {
-    case kBwdTokDecode: return go(bwd_token_decode_kernel<T, D, NW>);
-    case kBwdTokEncode: return go(bwd_token_encode_kernel<T, D, NW>);
-    default: return go(bwd_token_synthesis_kernel<T, D, NW>);
+    case kBwdTokDecode: return go(bwd_token_decode_kernel<T, D, kBwdTokenWaves>, kBwdTokenWaves);
+    case kBwdTokEncode: return go(bwd_token_encode_kernel<T, D, NW>, NW);
+    default: return go(bwd_token_synthesis_kernel<T, D, NW>, NW);
   }
 }
 
-hipError_t launch_bwd_token(const BwdTokenArgs& a, int dtype, int D, int kind, int grid_x, int BH,
-                            hipStream_t st) {
+template <int NW>
+static hipError_t launch_bwd_token_w(const BwdTokenArgs& a, int dtype, int D, int kind, int grid_x, int BH,
+                                     hipStream_t st) {
   if (dtype == 1)
-    return D == 32 ? launch_bwd_token_t<bf16, 32>(a, kind, grid_x, BH, st)
-                   : launch_bwd_token_t<bf16, 16>(a, kind, grid_x, BH, st);
-  return D == 32 ? launch_bwd_token_t<float, 32>(a, kind, grid_x, BH, st)
-                 : launch_bwd_token_t<float, 16>(a, kind, grid_x, BH, st);
+    return D == 32 ? launch_bwd_token_t<bf16, 32, NW>(a, kind, grid_x, BH, st)
+                   : launch_bwd_token_t<bf16, 16, NW>(a, kind, grid_x, BH, st);
+  return D == 32 ? launch_bwd_token_t<float, 32, NW>(a, kind, grid_x, BH, st)
+                 : launch_bwd_token_t<float, 16, NW>(a, kind, grid_x, BH, st);
+}
+
+hipError_t launch_bwd_token(const BwdTokenArgs& a, int dtype, int D, int kind, int nw, int grid_x, int BH,
+                            hipStream_t st) {
+  if (nw == 12) return launch_bwd_token_w<12>(a, dtype, D, kind, grid_x, BH, st);
+  if (nw != 8) return hipErrorInvalidValue;
+  return launch_bwd_token_w<8>(a, dtype, D, kind, grid_x, BH, st);
 }
 
 }  // namespace flarepp

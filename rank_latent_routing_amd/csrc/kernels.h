@@ -181,13 +181,14 @@ struct BwdCenterArgs {
 
 constexpr int kBwdStage = 64;  // tokens per LDS stage of the latent-side kernel
 inline int bwd_latent_waves(int Mp) { return Mp >= 256 ? 8 : 4; }
-constexpr int kBwdTokenWaves = 8;
+constexpr int kBwdTokenWaves = 8;       // token decode kernel
+constexpr int kBwdTokenWavesWide = 12;  // token encode and synthesis kernels (8 also built)
 
 hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, hipStream_t st);
 hipError_t launch_bwd_latent(const BwdLatentArgs& a, int dtype, int D, int call, int nw, int grid_x, int BH,
                              hipStream_t st);
 hipError_t launch_bwd_reduce(const BwdReduceArgs& a, int dtype, int D, int call, int BH, hipStream_t st);
-hipError_t launch_bwd_token(const BwdTokenArgs& a, int dtype, int D, int kind, int grid_x, int BH,
+hipError_t launch_bwd_token(const BwdTokenArgs& a, int dtype, int D, int kind, int nw, int grid_x, int BH,
                             hipStream_t st);
 size_t bwd_token_lds_bytes(int dtype, int D, int Mp, int kind);
 hipError_t launch_bwd_zero(void* p, size_t bytes, hipStream_t st);  // bytes: a multiple of 4
