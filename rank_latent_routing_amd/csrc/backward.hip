@@ -568,6 +568,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
 
   load(0);
   store(0);
+  // Wait here for every global load so far (the latent operands above included). Without it the
+  // compiler carries those loads into the loop as possibly outstanding and waits for them in the
+  // middle of each stage's products, which also waits out the next stage's prefetch there
+  // (vmcnt 0; lgkmcnt and expcnt left at their maxima).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int stage = 0; stage < nstage; stage++) {
     const int buf = stage & 1;
