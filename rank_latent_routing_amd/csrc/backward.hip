@@ -339,7 +339,7 @@ __device__ __forceinline__ f32x16 load_stats16(const float* base, int hh) {
 // LDS in stages of 64 tokens, double-buffered, the next stage's global loads issued before the
 // current stage's compute. Tokens past the chunk's end load as zeros and are masked out of P.
 template <typename T, int D, int CALL, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_latent_kernel(BwdLatentArgs a) {
   using F = Frag<T>;
   using Op = typename F::Op;
   using Pair = typename F::Pair;
@@ -493,11 +493,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
 
   f32x16 acc0 = {}, acc1 = {};
   // MASKED: the chunk's last stage, whose tokens past nvalid are out of the softmax.
+  // The score and dP products of all the stage's 32-token sub-tiles are issued first; the matrix
+  // unit then computes those of the next sub-tile while the vector unit exponentiates and splits
+  // the current one.
+  constexpr int NS = ST / 32;
   auto compute = [&](int buf, auto MASKED, int nvalid) __attribute__((always_inline)) {
     const T* xt = xs + buf * ST * D;
     const T* wt = ws + buf * ST * D;
+    f32x16 s_all[NS], dp_all[NS];
 #pragma unroll
-    for (int sub = 0; sub < ST / 32; sub++) {
+    for (int sub = 0; sub < NS; sub++) {
       const int r0 = 32 * sub;
       // The products start from -L and -c: the tokens' (decode, negated in LDS) or the latent's.
       f32x16 s = negL, dp = negC;
@@ -533,6 +538,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_latent_kernel(BwdLatentArgs a) {
           hold(dp, wa[kk]);
         }
       }
+      s_all[sub] = s;
+      dp_all[sub] = dp;
+    }
+#pragma unroll
+    for (int sub = 0; sub < NS; sub++) {
+      const int r0 = 32 * sub;
+      const f32x16& s = s_all[sub];
+      const f32x16& dp = dp_all[sub];
       f32x16 P, dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
