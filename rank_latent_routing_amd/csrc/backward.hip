@@ -336,15 +336,16 @@ __device__ __forceinline__ f32x16 load_stats16(const float* base, int hh) {
 //
 // Workgroup = NW waves, latent group of 32*NW latents; grid x enumerates (chunk, latent group) with
 // the groups of one chunk on the same XCD, y = b * H + h. The token tiles of a chunk pass through
-// LDS in stages of 64 tokens, double-buffered, the next stage's global loads issued before the
-// current stage's compute. Tokens past the chunk's end load as zeros and are masked out of P.
+// LDS in stages of 128 tokens (fp32: 64), double-buffered, the next stage's global loads issued
+// before the current stage's compute. Tokens past the chunk's end load as zeros and are masked out
+// of P.
 template <typename T, int D, int CALL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_latent_kernel(BwdLatentArgs a) {
   using F = Frag<T>;
   using Op = typename F::Op;
   using Pair = typename F::Pair;
   using Sw = Swz<T, D>;
-  constexpr int ST = kBwdStage;
+  constexpr int ST = sizeof(T) == 2 ? 128 : 64;  // bwd_stage
   constexpr int KB = D / 16;
   constexpr int NT = NW * 64;
   constexpr int CH = 16 / sizeof(T), CPR = D / CH;
@@ -493,16 +494,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   f32x16 acc0 = {}, acc1 = {};
   // MASKED: the chunk's last stage, whose tokens past nvalid are out of the softmax.
-  // The score and dP products of all the stage's 32-token sub-tiles are issued first; the matrix
-  // unit then computes those of the next sub-tile while the vector unit exponentiates and splits
-  // the current one.
-  constexpr int NS = ST / 32;
+  // The 32-token sub-tiles go in pairs: the score and dP products of both are issued first; the
+  // matrix unit then computes the second's while the vector unit exponentiates and splits the first.
+  constexpr int NS = ST / 32;  // sub-tiles per stage
+  constexpr int NPR = 2;       // sub-tiles per pair
   auto compute = [&](int buf, auto MASKED, int nvalid) __attribute__((always_inline)) {
     const T* xt = xs + buf * ST * D;
     const T* wt = ws + buf * ST * D;
-    f32x16 s_all[NS], dp_all[NS];
 #pragma unroll
-    for (int sub = 0; sub < NS; sub++) {
+    for (int g = 0; g < NS; g += NPR) {
+    if (decltype(MASKED)::value && 32 * g >= nvalid) break;  // the rest of the last stage is empty
+    f32x16 s_all[NPR], dp_all[NPR];
+#pragma unroll
+    for (int j = 0; j < NPR; j++) {
+      const int sub = g + j;
       const int r0 = 32 * sub;
       // The products start from -L and -c: the tokens' (decode, negated in LDS) or the latent's.
       f32x16 s = negL, dp = negC;
@@ -538,14 +543,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           hold(dp, wa[kk]);
         }
       }
-      s_all[sub] = s;
-      dp_all[sub] = dp;
+      s_all[j] = s;
+      dp_all[j] = dp;
     }
 #pragma unroll
-    for (int sub = 0; sub < NS; sub++) {
-      const int r0 = 32 * sub;
-      const f32x16& s = s_all[sub];
-      const f32x16& dp = dp_all[sub];
+    for (int j = 0; j < NPR; j++) {
+      const int r0 = 32 * (g + j);
+      const f32x16& s = s_all[j];
+      const f32x16& dp = dp_all[j];
       f32x16 P, dS;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
@@ -576,6 +581,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           hold<F>(acc0, pp);
         }
       }
+    }
     }
   };
 
@@ -1271,7 +1277,8 @@ hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, h
 
 template <typename T, int D, int CALL, int NW>
 static hipError_t launch_bwd_latent_t(const BwdLatentArgs& a, int gx, int BH, hipStream_t st) {
-  const size_t lds = (size_t)4 * kBwdStage * D * sizeof(T) + (CALL == kBwdDecode ? 4 * kBwdStage * sizeof(float) : 0);
+  const size_t stage = (size_t)bwd_stage(sizeof(T) == 2 ? 1 : 0);
+  const size_t lds = 4 * stage * D * sizeof(T) + (CALL == kBwdDecode ? 4 * stage * sizeof(float) : 0);
   hipError_t e = allow_lds_bwd(bwd_latent_kernel<T, D, CALL, NW>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_latent_kernel<T, D, CALL, NW>), dim3(gx, BH), dim3(NW * 64), lds, st, a);

@@ -179,7 +179,9 @@ struct BwdCenterArgs {
   int M, Mp;
 };
 
-constexpr int kBwdStage = 64;  // tokens per LDS stage of the latent-side kernel
+// Tokens per LDS stage of the latent-side kernel: 128 for bf16 runs, 64 for fp32 runs (whose
+// operands take twice the registers).
+inline int bwd_stage(int dtype) { return dtype == 1 ? 128 : 64; }
 inline int bwd_latent_waves(int Mp) { return Mp >= 256 ? 8 : 4; }
 constexpr int kBwdTokenWaves = 8;       // token decode kernel
 constexpr int kBwdTokenWavesWide = 12;  // token encode and synthesis kernels (8 also built)
