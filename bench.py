@@ -297,8 +297,9 @@ def block(args, w, dt_code):
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (the mixer shards over "
-              "(b, h) or over tokens, see DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (the mixer would shard "
+              "over (b, h) or over token ranges with a log-sum-exp merge of the latent partials); run with "
+              "--gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
