@@ -306,7 +306,7 @@ def main():
     import torch
 
     import rank_latent_routing_amd as fl
-    from workloads import make_workload
+    from workloads import DESCRIPTIONS, FAMILIES, make_workload
 
     fl.lib()
     w = make_workload(args.config)
@@ -408,8 +408,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"FLARE++ mixer forward, {w.name}", "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D,
-                   "inputs": "points on a random closed surface, sinusoidal-feature K/V/S" if args.config == 5 else "see workloads/gen.py"},
+        "config": {"workload": f"FLARE++ mixer forward: {DESCRIPTIONS[args.config]}", "B": w.B, "H": w.H, "N": w.N,
+                   "M": w.M, "D": w.D, "inputs": FAMILIES[w.kind]},
         "tflops": tflops,
         "mfma_frac": tflops / peak,
         "hbm_frac": hbm_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),

@@ -38,6 +38,22 @@ CONFIGS = {
     5: dict(B=1, H=8, N=1048576, M=512, D=32, dtype="bf16", kind="surface"),
 }
 
+#: What each workload stands for (its sizes are in CONFIGS).
+DESCRIPTIONS = {
+    1: "small fp32 case, Gaussian inputs",
+    2: "mesh-like fields on points in the unit cube",
+    3: "sequence-classification batch, Gaussian inputs, one head with gate 0",
+    4: "mesh-like fields on 65536 points in the unit cube",
+    5: "a million points on a random closed surface with mesh-like fields",
+}
+
+#: Input families as written in a benchmark record.
+FAMILIES = {
+    "gauss": "K, V, S i.i.d. N(0, 1)",
+    "cube": "points uniform in the unit cube, sinusoidal-feature K/V/S",
+    "surface": "points on a random closed surface, sinusoidal-feature K/V/S",
+}
+
 _SEED_BASE = 2608_11519
 
 
