@@ -237,3 +237,33 @@ def test_full_size_projection_sampled_rows():
             worst = max(worst, _err(gs[0, h], r[0, h], d, 1e-4))
     say(f"[project] full size: worst {worst:.3g}")
     assert worst <= 1e-4
+
+
+def test_full_size_block_constant_values():
+    # The whole block at the 1M-token shape (B = 1, H = 8, N = 2^20, M = 512, D = 32), in the launch
+    # configuration the benchmark times, against a closed form: with a value projection that ignores
+    # X (Wv = 0), V is the bias bv in every token; a row-stochastic operator maps a constant field to
+    # itself (Section 3.1, Eq. 4), whatever the keys and routing queries, so every output row is
+    # concat_h(bv_h) Wo^T + bo (Section 2). Every output element is checked.
+    import rank_latent_routing_amd as fl
+    from workloads.gen import _store
+    w = make_workload(5, N=64)  # only its seeds Qseed and Qf are used
+    shape = types.SimpleNamespace(B=1, H=8, N=1 << 20, D=32, dtype="bf16", kind="gauss")
+    bi = make_block_inputs(shape, seed=71)
+    bi.Wv = _store(np.zeros_like(bi.f64("Wv")), "bf16")
+    say(f"[block] full size, constant values: N={shape.N} C={shape.H * shape.D}")
+    d = "bf16"
+    out = fl.flarepp_block(_dev(bi.X, d), _wdev(bi.Wk, d), _wdev(bi.Wv, d), _wdev(bi.Ws, d), _wdev(bi.Wo, d),
+                           _dev(w.Qseed, d), _dev(w.Qf, d), torch.from_numpy(bi.gamma).cuda(), bk=_dev(bi.bk, d),
+                           bv=_dev(bi.bv, d), bs=_dev(bi.bs, d), bo=_dev(bi.bo, d), nq=_dev(bi.nq, d),
+                           nk=_dev(bi.nk, d))
+    torch.cuda.synchronize()
+    f = bi.f64
+    Y1 = f("bv").reshape(1, shape.H, 1, shape.D)
+    ref = oracle.out_project(Y1, f("Wo"), f("bo"))[0, 0]  # [C]
+    r = torch.from_numpy(ref).cuda()
+    excess = ((out[0].double() - r).abs() - 2.0 ** -8 * r.abs()).max().item()
+    err = max(excess, 0.0) / float(np.sqrt(np.mean(ref * ref)))
+    say(f"[block] full size, constant values: err {err:.3g}")
+    assert bool(torch.isfinite(out.float()).all())
+    assert err <= 2e-2
