@@ -76,10 +76,12 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   if (plan_env >= 0 && plan_env <= 3 && !(plan_env == 3 && dtype == FLAREPP_FP32)) p.part_plan = plan_env;
   const flarepp::PartialShape ps = flarepp::partial_plan_shape(p.part_plan);
   p.nlg = (int)ceil_div(p.Mp16, (int64_t)ps.lpw * ps.nw);
-  // 16-wave groups (1 per CU): one round over the 256 CUs, since fewer chunks also make the merge
-  // cheaper (256 against 512 workgroups: same partials, merges 0.016 -> 0.010 ms at the 1M-token
-  // workload). 8- and 4-wave groups (2 and 4 per CU): about two rounds.
-  const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", ps.nw == 16 ? 256 : ps.nw == 8 ? 1024 : 2048);
+  // Workgroups over the token chunks: 256 for 16-wave groups (1 per CU: one round), 512 for 8- and
+  // 4-wave groups (2 and 4 per CU). Fewer chunks make the merges cheaper, which outweighs the
+  // partials' lower occupancy. Measured per call: 1M-token workload 2.04 -> 2.02 ms (against 512),
+  // M = 256 (8-wave) 0.219 -> 0.200 ms and M = 128 (4-wave) 0.174 -> 0.161 ms (against 1024 and
+  // 2048), M = 64 (4-wave) 0.068 -> 0.059 ms.
+  const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", ps.nw == 16 ? 256 : 512);
   int64_t nchunk = ceil_div(target, (int64_t)p.BH * p.nlg);
   nchunk = nchunk < 1 ? 1 : nchunk;
   // At most 2048 chunks: the merge keeps a row block's chunk weights in LDS (16 rows x 2048 x 4 B).
