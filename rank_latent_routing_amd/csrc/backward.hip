@@ -336,7 +336,7 @@ __device__ __forceinline__ f32x16 load_stats16(const float* base, int hh) {
 //
 // Workgroup = NW waves, latent group of 32*NW latents; grid x enumerates (chunk, latent group) with
 // the groups of one chunk on the same XCD, y = b * H + h. The token tiles of a chunk pass through
-// LDS in stages of 128 tokens (fp32: 64), double-buffered, the next stage's global loads issued
+// LDS in stages of bwd_stage_t tokens, double-buffered, the next stage's global loads issued
 // before the current stage's compute. Tokens past the chunk's end load as zeros and are masked out
 // of P.
 template <typename T, int D, int CALL, int NW>
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   using Op = typename F::Op;
   using Pair = typename F::Pair;
   using Sw = Swz<T, D>;
-  constexpr int ST = sizeof(T) == 2 ? 128 : 64;  // bwd_stage
+  constexpr int ST = bwd_stage_t(sizeof(T) == 2, NW);
   constexpr int KB = D / 16;
   constexpr int NT = NW * 64;
   constexpr int CH = 16 / sizeof(T), CPR = D / CH;
@@ -1277,7 +1277,7 @@ hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, h
 
 template <typename T, int D, int CALL, int NW>
 static hipError_t launch_bwd_latent_t(const BwdLatentArgs& a, int gx, int BH, hipStream_t st) {
-  const size_t stage = (size_t)bwd_stage(sizeof(T) == 2 ? 1 : 0);
+  const size_t stage = (size_t)bwd_stage_t(sizeof(T) == 2, NW);
   const size_t lds = 4 * stage * D * sizeof(T) + (CALL == kBwdDecode ? 4 * stage * sizeof(float) : 0);
   hipError_t e = allow_lds_bwd(bwd_latent_kernel<T, D, CALL, NW>, lds);
   if (e != hipSuccess) return e;

@@ -428,7 +428,7 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.lat_nlg = (int)ceil_div(p.Mp, 32 * p.lat_nw);
   const int64_t target = env_int("FLAREPP_BWD_LATENT_WORKGROUPS", p.lat_nw == 8 ? 1024 : 2048);
   int64_t nchunk = ceil_div(target, (int64_t)BH * p.lat_nlg);
-  const int64_t stage = flarepp::bwd_stage(dtype);
+  const int64_t stage = flarepp::bwd_stage(dtype, p.lat_nw);
   const int64_t max_chunks = ceil_div(N, stage);
   if (nchunk > max_chunks) nchunk = max_chunks;
   if (nchunk < 1) nchunk = 1;

@@ -179,9 +179,10 @@ struct BwdCenterArgs {
   int M, Mp;
 };
 
-// Tokens per LDS stage of the latent-side kernel: 128 for bf16 runs, 64 for fp32 runs (whose
-// operands take twice the registers).
-inline int bwd_stage(int dtype) { return dtype == 1 ? 128 : 64; }
+// Tokens per LDS stage of the latent-side kernel: bf16 runs 256 with 8-wave workgroups and 128
+// with 4-wave ones, fp32 runs 64 (their operands take twice the registers).
+constexpr int bwd_stage_t(bool bf16, int nw) { return bf16 ? (nw == 8 ? 256 : 128) : 64; }
+inline int bwd_stage(int dtype, int nw) { return bwd_stage_t(dtype == 1, nw); }
 inline int bwd_latent_waves(int Mp) { return Mp >= 256 ? 8 : 4; }
 constexpr int kBwdTokenWaves = 8;       // token decode kernel
 constexpr int kBwdTokenWavesWide = 12;  // token encode and synthesis kernels (8 also built)
