@@ -12,13 +12,15 @@ and the whole block (flarepp_block: projections of a seeded input X [B, N, H D] 
 near-identity weights, the mixer, the output projection; "block") are timed afterwards, each in a
 region of its own.
 
-Per call the line also gives the median and minimum of the K timed calls; `--cold` adds the same
-for calls that each follow a 1 GiB write (the smaller workloads' inputs otherwise stay in the
-256 MB MALL between calls).
+Per call the line also gives the median and minimum of the K timed calls; `graph_replay` the time
+per call when the call, captured once in a HIP graph, is replayed K times (the host out of the
+launch chain; `value` stays the eager call); `--cold` adds the median and minimum for calls that
+each follow a 1 GiB write (the smaller workloads' inputs otherwise stay in the 256 MB MALL between
+calls).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
                       [--cpu-sample-heads H] [--copy-calibration] [--no-backward] [--no-variants]
-                      [--no-block] [--cold]
+                      [--no-block] [--no-graph] [--cold]
 """
 import argparse
 import json
@@ -94,6 +96,7 @@ def _parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true", help="skip plain FLARE and simplified FLARE++")
     ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer + output projection)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the mixer call")
     ap.add_argument("--cold", action="store_true",
                     help="also time K calls with a 1 GiB write between them (inputs out of the caches)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -355,6 +358,31 @@ def main():
     # events between kernels would add a visible share of each step.
     per_kernel = _kernel_times(args.steps, call)
 
+    # The same call captured once in a HIP graph and replayed K times (the workspace entry point
+    # enqueues kernels only): what remains of the launch chain's gaps when the host is out of it.
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            call()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"ms_per_step": g0.elapsed_time(g1) / args.steps, "calls": args.steps}
+        del g
+
     cold = None
     if args.cold:
         # Each timed call follows a 1 GiB write, which evicts the inputs from L2 and the MALL.
@@ -419,6 +447,8 @@ def main():
     }
     if cold is not None:
         res["cold"] = cold
+    if graph is not None:
+        res["graph_replay"] = graph
     if not args.no_variants:
         res["variants"] = variants(args, w, dev, dt_code)
     if not args.no_backward:
