@@ -188,6 +188,32 @@ def _time_steps(args, call):
     return max(ev0.elapsed_time(ev1), (time.perf_counter() - t0) * 1e3) / args.steps
 
 
+def _graph_replay(args, call, stream):
+    """The call captured once in a HIP graph and replayed K times: ms per replay."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        call()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph = {"ms_per_step": g0.elapsed_time(g1) / args.steps, "calls": args.steps}
+    del g
+    return graph
+
+
 def variants(args, w, dev, dt_code):
     """Plain FLARE (Eq. 3, the fixed queries Qf used as given) and simplified FLARE++ (Eq. 20, S as
     the synthesis keys and seeded separate synthesis values) on the same workload."""
@@ -362,26 +388,12 @@ def main():
     # enqueues kernels only): what remains of the launch chain's gaps when the host is out of it.
     graph = None
     if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            call()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            call()
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(args.steps):
-            g.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph = {"ms_per_step": g0.elapsed_time(g1) / args.steps, "calls": args.steps}
-        del g
+        try:
+            graph = _graph_replay(args, call, stream)
+        except Exception as e:  # noqa: BLE001
+            import traceback
+            traceback.print_exc()
+            graph = {"error": f"{type(e).__name__}: {e}"[:300]}
 
     cold = None
     if args.cold:
@@ -449,14 +461,25 @@ def main():
         res["cold"] = cold
     if graph is not None:
         res["graph_replay"] = graph
+
+    def leg(name, fn, *a):
+        # An extra leg that fails is reported in its field (traceback on stderr) and does not take
+        # the headline measurement above with it.
+        try:
+            res[name] = fn(*a)
+        except Exception as e:  # noqa: BLE001
+            import traceback
+            traceback.print_exc()
+            res[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
+
     if not args.no_variants:
-        res["variants"] = variants(args, w, dev, dt_code)
+        leg("variants", variants, args, w, dev, dt_code)
     if not args.no_backward:
-        res["backward"] = backward(args, w, dev, dt_code, peak)
+        leg("backward", backward, args, w, dev, dt_code, peak)
     if not args.no_block:
-        res["block"] = block(args, w, dt_code)
+        leg("block", block, args, w, dt_code)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+        leg("cpu_baseline", cpu_baseline, w, args.cpu_sample_heads)
     print(json.dumps(res), flush=True)
 
 
