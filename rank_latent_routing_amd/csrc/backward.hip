@@ -1036,7 +1036,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
       vb[kk] = valid ? F::gload(vbase + o) : F::zero();
     }
     f32x16 accK = {}, accV = {};
-    for (int lb = 0; lb < nlb; lb++) {
+    // One latent block; the loop below runs four per iteration (bf16), so that the LDS reads of the
+    // second to fourth address their tiles by the instructions' immediate offsets.
+    auto block = [&](int lb) __attribute__((always_inline)) {
       Pair qa[KB], za[KB];
       // Latents past M: zero rows of c*Q and dZ, L = +inf, c = 0, so P and dS vanish there. The
       // products start from -L and -c (negated in LDS): E = l - L, dP = dP - c.
@@ -1075,6 +1077,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
         hold<F>(accV, zk);
         hold<F>(accV, pk);
       }
+    };
+    constexpr int UF = sizeof(T) == 2 ? 4 : 1;  // fp32 operands leave no registers for it
+    if constexpr (UF > 1) {
+      int lb = 0;
+      for (; lb + UF <= nlb; lb += UF) {
+#pragma unroll
+        for (int u = 0; u < UF; u++) block(lb + u);
+      }
+      for (; lb < nlb; lb++) block(lb);
+    } else {
+      for (int lb = 0; lb < nlb; lb++) block(lb);
     }
     if (valid) {
       // dK = dK_dec + (1/sqrt(D)) dS Q = dK_dec + ln 2 * dS (c*Q).
@@ -1164,7 +1177,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
       sb[kk] = F::split8(y);
     }
     f32x16 accA = {}, accB = {};
-    for (int lb = 0; lb < nlb; lb++) {
+    // One latent block; four per loop iteration for bf16, as in the encode kernel.
+    auto block = [&](int lb) __attribute__((always_inline)) {
       Op qa[KB];
       Pair ga[KB];
       // The products start from -L and -c (negated in LDS): A = l - L, dP = dP - c.
@@ -1203,6 +1217,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
         hold<F>(accB, gk);
         hold<F>(accB, pk);
       }
+    };
+    constexpr int UF = sizeof(T) == 2 ? 4 : 1;
+    if constexpr (UF > 1) {
+      int lb = 0;
+      for (; lb + UF <= nlb; lb += UF) {
+#pragma unroll
+        for (int u = 0; u < UF; u++) block(lb + u);
+      }
+      for (; lb < nlb; lb++) block(lb);
+    } else {
+      for (int lb = 0; lb < nlb; lb++) block(lb);
     }
     // dSn in slot v: dim row32(v, l / 32) of the lane's token; with S at the same dims, the N0
     // backward needs one sum over the token's D dims (this lane's and lane l ^ 32's).
