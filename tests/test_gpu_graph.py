@@ -1,8 +1,9 @@
-"""The workspace entry points inside HIP graphs: flarepp_mix_ws, flarepp_mix_backward_ws and
+"""Streams and HIP graphs. The workspace entry points inside HIP graphs: flarepp_mix_ws, flarepp_mix_backward_ws and
 flarepp_block_ws enqueue kernels only (no allocation, no memset, no host synchronization), so a
 caller can capture them once and replay them. Each graph is replayed several times with eager calls
 of the library and synchronizations in between, and every replay must equal the eager result bit
-for bit (the kernels are deterministic)."""
+for bit (the kernels are deterministic). Calls on a stream the caller created match the default
+stream's results."""
 import numpy as np
 import pytest
 
@@ -112,3 +113,28 @@ def test_block_graph_replays():
     g = _capture(lambda: call(out))
     other = lambda: fl.flarepp_out_project(torch.ones((w.B, w.H, w.N, w.D), dtype=torch.bfloat16, device="cuda"), W[3])
     _replays_match(g, [out], [ref], other)
+
+
+def test_calls_on_a_caller_stream_match_the_default_stream():
+    # The stream argument: the mixer and its backward enqueued on a stream the caller created (with
+    # other work queued ahead of them there) give the default stream's results bit for bit.
+    import rank_latent_routing_amd as fl
+    w = make_workload(4, B=1, H=2, N=4000, M=96, seed=13)
+    say(f"[stream] {w.name} N={w.N}")
+    dev = to_device(w)
+    args = (dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"])
+    dY = _t(make_cotangent(w), w.dtype)
+    ref = fl.flarepp_mix_ws(*args).clone()
+    gref = {k: v.clone() for k, v in fl.flarepp_mix_backward(*args, dY).items()}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    busy = torch.empty(2 ** 24, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        busy.fill_(1.0)  # queued ahead of the library's kernels on the same stream
+        out = torch.empty_like(ref)
+        fl.flarepp_mix_ws(*args, out=out, stream=s)
+        grads = fl.flarepp_mix_backward(*args, dY, stream=s)
+    s.synchronize()
+    assert torch.equal(out, ref)
+    for k in gref:
+        assert torch.equal(grads[k], gref[k]), k
