@@ -41,6 +41,12 @@
  * run surface at the caller's next synchronization of `stream`, as in HIP. No C++ exception or
  * abort crosses this interface. Inputs holding NaN or Inf give NaN outputs; finite inputs whose
  * values exceed about 1e22 in magnitude may overflow the fp32 accumulators.
+ *
+ * The entry points that take a caller's workspace (the *_ws ones, flarepp_mix_backward_ws,
+ * flarepp_block_ws) enqueue kernel launches only: no allocation, memset, copy or synchronization.
+ * A caller may capture them in a HIP graph and replay it; every replay recomputes everything from
+ * the inputs, so the workspace needs no clearing between replays. The entry points without a
+ * workspace argument allocate theirs stream-ordered (hipMallocAsync / hipFreeAsync on `stream`).
  */
 #ifndef FLAREPP_H
 #define FLAREPP_H
