@@ -300,3 +300,23 @@ def test_plain_flare_equals_mixer_with_gate_zero():
     got = Y2.float().cpu().numpy().astype(np.float64)
     for h in range(w.H):
         assert slice_err(got[0, h], ref[0, h], w.dtype) <= tol(w.dtype)
+
+
+# ---- seeded random shapes (D, M, N, B, H, dtype and the gate drawn together) ---------------------
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.6 else "fp32"
+        D = int(rng.choice([16, 32]))
+        M = int(rng.choice([1, 2, 31, 32, 33, 64, 100, 127, 128, 129, 255, 256, 257, 300, 480, 512]))
+        N = int(rng.choice([1, 2, 17, 63, 64, 65, 255, 256, 257, 999, 1024, 2500, 4097]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        cases.append((i, dtype, D, M, N, B, H))
+    return cases
+
+
+@pytest.mark.parametrize("i,dtype,D,M,N,B,H", _random_cases(16, 2024))
+def test_random_shapes_forward(i, dtype, D, M, N, B, H):
+    w = make_workload(1, B=B, H=H, N=N, M=M, D=D, dtype=dtype, kind="gauss", seed=7000 + i)
+    _check(w, label=f"random {i}: {dtype} D={D} M={M} N={N} B={B} H={H}")
