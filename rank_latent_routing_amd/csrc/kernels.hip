@@ -268,10 +268,18 @@ __device__ __forceinline__ int perm_row(int r, int half) { return 8 * (r >> 2) +
 // bf16 keys against the hi/lo query pair instead, the logits of the exact pass and of the
 // backward kernels, so that the normalizers they leave match those logits.
 //
+// HILO (bf16, the backward's recompute): the P.V product and the row sums take each probability as
+// a pair hi + lo (hi = bf16(p), lo = bf16(p - hi)), and the synthesis call's values N0(s) likewise
+// (a second value tile holds their lo parts): P.V = Phi.Vhi + Plo.Vhi + Phi.Vlo. The backward forms
+// the row terms of the encode and synthesis calls from these Z and Qd against products that take
+// every operand as a pair; single-bf16 P and N0(s) would leave those terms about 2^-8 off, which
+// dominates the cotangents when a softmax row spans only a few tokens.
+//
 // Grid: x enumerates (chunk, latent group) so that the latent groups of one chunk land on the same
 // XCD (workgroups are dealt to the 8 XCDs round-robin by x) and share its L2; y = b * H + h.
-template <typename T, int D, int LPW, int NW, bool SYNTH, int STG>
+template <typename T, int D, int LPW, int NW, bool SYNTH, int STG, bool HILO>
 __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
+  static_assert(!HILO || sizeof(T) == 2, "hi/lo probabilities are for bf16 operands");
   constexpr int kStage = STG;  // tokens per LDS stage
   using O = Ops<T, D>;
   using Slice = typename O::Slice;
@@ -293,7 +301,8 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);                   // [2][kStage][RS]
   T* vt = ks + 2 * kStage * RS;                          // [2][VE]
-  int* fail_s = reinterpret_cast<int*>(vt + 2 * VE);     // one flag
+  T* vtl = vt + 2 * VE;                                  // HILO synthesis: value lo parts, [2][VE]
+  int* fail_s = reinterpret_cast<int*>(vt + (HILO && SYNTH ? 4 : 2) * VE);  // one flag
 
   // (chunk, latent group) of this workgroup.
   int chunk_id, lg;
@@ -426,6 +435,12 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
             *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = float_to_chunk<T>(kx);
           }
           rowtile_store<T, D>(vdst, kStage, t, part * CH, float_to_chunk<T>(x));
+          if constexpr (HILO) {
+            float xl[CH];
+#pragma unroll
+            for (int j = 0; j < CH; j++) xl[j] = x[j] - (float)(T)x[j];
+            rowtile_store<T, D>(vtl + buf * VE, kStage, t, part * CH, float_to_chunk<T>(xl));
+          }
         } else {
           if constexpr (f16keys)
             *reinterpret_cast<f16x8*>(kdst + t * RS + part * CH) =
@@ -443,6 +458,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     constexpr bool exact = decltype(EXACT)::value;
     const T* kt = ks + buf * kStage * RS;
     const T* vtt = vt + buf * VE;
+    const T* vtlt = vtl + buf * VE;
     const int nsub = (nvalid + 31) / 32;
     for (int st = 0; st < nsub; st++) {
       const Slice ka0 = O::load_slice(kt + (32 * st + perm_row(c, 0)) * RS, g);
@@ -511,12 +527,32 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       Oct vb[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; db++) vb[db] = O::load_oct_rows(vtt, VSTR, 32 * st, 16 * db, c, g);
+      Oct vbl[HILO && SYNTH ? NDB : 1];
+      if constexpr (HILO && SYNTH) {
+#pragma unroll
+        for (int db = 0; db < NDB; db++) vbl[db] = O::load_oct_rows(vtlt, VSTR, 32 * st, 16 * db, c, g);
+      }
 #pragma unroll
       for (int lb = 0; lb < NLB; lb++) {
         const Oct pa = O::pack(s0v[lb], s1v[lb]);
         lsum[lb] = O::osum(pa, lsum[lb]);
 #pragma unroll
         for (int db = 0; db < NDB; db++) zacc[lb][db] = O::pv(pa, vb[db], zacc[lb][db]);
+        if constexpr (HILO) {
+          f32x4 r0, r1;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            r0[i] = s0v[lb][i] - (float)pa[i];
+            r1[i] = s1v[lb][i] - (float)pa[4 + i];
+          }
+          const Oct pl = O::pack(r0, r1);
+          lsum[lb] = O::osum(pl, lsum[lb]);
+#pragma unroll
+          for (int db = 0; db < NDB; db++) {
+            zacc[lb][db] = O::pv(pl, vb[db], zacc[lb][db]);
+            if constexpr (SYNTH) zacc[lb][db] = O::pv(pa, vbl[db], zacc[lb][db]);
+          }
+        }
       }
     }
   };
@@ -743,7 +779,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   }
   const int64_t pbase = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp;
   if constexpr (kWide) {
-    if (!exact && !a.hilo) {
+    if (!HILO && !exact && !a.hilo) {
       run_chunk_wide();
       if constexpr (NB == 1) {
         // Latent j = l % 32 sums to row j % 16, columns 0-7 (j < 16) or 8-15 (j >= 16): lane
@@ -1477,19 +1513,27 @@ static hipError_t allow_lds(F* fn, size_t lds) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <typename T, int D, int STG>
+template <typename T, int D, int STG, bool VLO>
 static size_t partial_lds_t() {
   constexpr int CH = 16 / sizeof(T);
-  return (size_t)(2 * STG * (D + CH) + 2 * RowTile<T, D>::elems(STG)) * sizeof(T) + 16;
+  return (size_t)(2 * STG * (D + CH) + (VLO ? 4 : 2) * RowTile<T, D>::elems(STG)) * sizeof(T) + 16;
 }
 
-template <typename T, int D, int LPW, int NW, bool SYNTH, int STG>
+template <typename T, int D, int LPW, int NW, bool SYNTH, int STG, bool HILO>
 static hipError_t launch_partial_t(const PartialArgs& a, int grid_x, int grid_y, hipStream_t st) {
-  const size_t lds = partial_lds_t<T, D, STG>();
-  hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH, STG>, lds);
+  const size_t lds = partial_lds_t<T, D, STG, HILO && SYNTH>();
+  hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH, STG, HILO>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH, STG>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH, STG, HILO>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
+}
+
+// bf16 calls with `hilo` set (the backward's recompute) take the hi/lo P.V instance.
+template <typename T, int D, int LPW, int NW, bool SYNTH, int STG>
+static hipError_t launch_partial_h(const PartialArgs& a, int grid_x, int grid_y, hipStream_t st) {
+  if constexpr (sizeof(T) == 2)
+    if (a.hilo) return launch_partial_t<T, D, LPW, NW, SYNTH, STG, true>(a, grid_x, grid_y, st);
+  return launch_partial_t<T, D, LPW, NW, SYNTH, STG, false>(a, grid_x, grid_y, st);
 }
 
 // Partial-kernel variants (latents per wave, waves per workgroup, tokens per stage); see
@@ -1498,11 +1542,11 @@ static hipError_t launch_partial_t(const PartialArgs& a, int grid_x, int grid_y,
 template <typename T, int D, bool SYNTH>
 static hipError_t launch_partial_d(const PartialArgs& a, int plan, int gx, int gy, hipStream_t st) {
   switch (plan) {
-    case 0: return launch_partial_t<T, D, 16, 4, SYNTH, 128>(a, gx, gy, st);
-    case 1: return launch_partial_t<T, D, 32, 4, SYNTH, 128>(a, gx, gy, st);
-    case 2: return launch_partial_t<T, D, 32, 8, SYNTH, 128>(a, gx, gy, st);
+    case 0: return launch_partial_h<T, D, 16, 4, SYNTH, 128>(a, gx, gy, st);
+    case 1: return launch_partial_h<T, D, 32, 4, SYNTH, 128>(a, gx, gy, st);
+    case 2: return launch_partial_h<T, D, 32, 8, SYNTH, 128>(a, gx, gy, st);
     case 3:
-      if constexpr (sizeof(T) == 2) return launch_partial_t<T, D, 32, 16, SYNTH, 256>(a, gx, gy, st);
+      if constexpr (sizeof(T) == 2) return launch_partial_h<T, D, 32, 16, SYNTH, 256>(a, gx, gy, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -1610,14 +1654,18 @@ size_t decode_lds_bytes(int dtype, int D, int Mp, int nw) {
   return D == 32 ? decode_lds_t<float, 32>(Mp, nw) : decode_lds_t<float, 16>(Mp, nw);
 }
 
-size_t partial_lds_bytes(int dtype, int D, int plan) {
+size_t partial_lds_bytes(int dtype, int D, int plan, bool value_lo) {
   const bool big = plan == 3;
   if (dtype == 1) {
-    if (D == 32) return big ? partial_lds_t<bf16, 32, 256>() : partial_lds_t<bf16, 32, 128>();
-    return big ? partial_lds_t<bf16, 16, 256>() : partial_lds_t<bf16, 16, 128>();
+    if (value_lo) {
+      if (D == 32) return big ? partial_lds_t<bf16, 32, 256, true>() : partial_lds_t<bf16, 32, 128, true>();
+      return big ? partial_lds_t<bf16, 16, 256, true>() : partial_lds_t<bf16, 16, 128, true>();
+    }
+    if (D == 32) return big ? partial_lds_t<bf16, 32, 256, false>() : partial_lds_t<bf16, 32, 128, false>();
+    return big ? partial_lds_t<bf16, 16, 256, false>() : partial_lds_t<bf16, 16, 128, false>();
   }
-  if (D == 32) return big ? partial_lds_t<float, 32, 256>() : partial_lds_t<float, 32, 128>();
-  return big ? partial_lds_t<float, 16, 256>() : partial_lds_t<float, 16, 128>();
+  if (D == 32) return big ? partial_lds_t<float, 32, 256, false>() : partial_lds_t<float, 32, 128, false>();
+  return big ? partial_lds_t<float, 16, 256, false>() : partial_lds_t<float, 16, 128, false>();
 }
 
 }  // namespace flarepp
