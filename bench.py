@@ -12,6 +12,9 @@ and the whole block (flarepp_block: projections of a seeded input X [B, N, H D] 
 near-identity weights, the mixer, the output projection; "block") are timed afterwards, each in a
 region of its own.
 
+"shard" times one GPU's share of the same workload split over 8 GPUs by token ranges (the pages'
+context parallelism): the first N/8 tokens of every (b, h) slice through the same call.
+
 Per call the line also gives the median and minimum of the K timed calls; `graph_replay` the time
 per call when the call, captured once in a HIP graph, is replayed K times (the host out of the
 launch chain; `value` stays the eager call); `--cold` adds the median and minimum for calls that
@@ -20,7 +23,7 @@ calls).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
                       [--cpu-sample-heads H] [--copy-calibration] [--no-backward] [--no-variants]
-                      [--no-block] [--no-graph] [--cold]
+                      [--no-block] [--no-shard] [--no-graph] [--cold]
 """
 import argparse
 import json
@@ -96,6 +99,7 @@ def _parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true", help="skip plain FLARE and simplified FLARE++")
     ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer + output projection)")
+    ap.add_argument("--no-shard", action="store_true", help="skip one GPU's share of an 8-way token split")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the mixer call")
     ap.add_argument("--cold", action="store_true",
                     help="also time K calls with a 1 GiB write between them (inputs out of the caches)")
@@ -235,6 +239,26 @@ def variants(args, w, dev, dt_code):
         ms = _time_steps(args, call)
         res[name] = {"ms_per_step": ms, "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "tokens*heads/s"}
     return res
+
+
+def shard(args, w, dev, dt_code, ranks=8):
+    """One GPU's share of the workload split over `ranks` GPUs by token ranges (context parallelism,
+    Appendix B): the first N / ranks tokens of every (b, h) slice through the same mixer call. Under
+    that split each GPU runs the partial kernels and the decode on its own tokens; what this figure
+    leaves out is the exchange of the latent partials between GPUs (one all-gather of M (D + 2)
+    values per head and routing call) and the merge of the gathered sets."""
+    import torch
+
+    import rank_latent_routing_amd as fl
+    n = w.N // ranks
+    K, V, S = (dev[k][:, :, :n].contiguous() for k in ("K", "V", "S"))
+    out = torch.empty_like(K)
+    ws = torch.empty(fl.flarepp_workspace_bytes(w.B, w.H, n, w.M, w.D, dt_code), dtype=torch.uint8, device="cuda")
+    call = lambda: fl.flarepp_mix_ws(K, V, S, dev["Qseed"], dev["Qf"], dev["g"], out=out, workspace=ws)
+    ms = _time_steps(args, call)
+    kern = _kernel_times(args.steps, call)
+    return {"ranks": ranks, "N": n, "ms_per_step": ms, "value": w.B * w.H * n / (ms * 1e-3),
+            "unit": "tokens*heads/s", "kernels": {k: round(v, 4) for k, v in kern.items() if v > 0}}
 
 
 def backward(args, w, dev, dt_code, peak):
@@ -474,6 +498,8 @@ def main():
 
     if not args.no_variants:
         leg("variants", variants, args, w, dev, dt_code)
+    if not args.no_shard:
+        leg("shard", shard, args, w, dev, dt_code)
     if not args.no_backward:
         leg("backward", backward, args, w, dev, dt_code, peak)
     if not args.no_block:
