@@ -33,7 +33,9 @@
 // K, V, S, dY and the seeds are exact bf16. Each c is formed from the operands its dP products see
 // (the decode call's from its own P and dP, the encode call's as <dZ, Z> with dZ as carried, the
 // synthesis call's as <G, Qd> likewise), and the recomputed forward takes the exact hi/lo path, so
-// that its normalizers match the logits computed here.
+// that its normalizers match the logits computed here; its P.V products take P (and the synthesis
+// values N0(S)) as pairs too, so that Z and Qd, and with them those c, are as exact as the products
+// here.
 //
 // Layout of the 32x32x16 MFMA C[i][j] += sum_k A[i][k] B[k][j]: lane l supplies row l % 32 of A and
 // column l % 32 of B with k = 8 (l / 32) + e (e = 0..7) and receives column l % 32, rows

@@ -397,7 +397,7 @@ int simplified_common(const void* K, const void* V, const void* Sk, const void* 
 // ---- Backward pass
 //
 // The synthesis and encode calls are recomputed with hi/lo query logits (the backward kernels'
-// logits) and their normalizers kept, Z is centered, and the decode kernel forms every token's
+// logits) and hi/lo P.V products (the partial kernel's HILO instance) and their normalizers kept, Z is centered, and the decode kernel forms every token's
 // statistics and the decode call's part of dK; then, per routing call in reverse order (Appendix
 // B.5, Eq. 46-49): the latent-side partials and their reduction for the decode call (dZ, dQ_dec)
 // and the encode call (dQ_enc, then the gate), the synthesis call (dQseed and the batch sums), and
