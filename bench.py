@@ -103,6 +103,9 @@ def _parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the mixer call")
     ap.add_argument("--cold", action="store_true",
                     help="also time K calls with a 1 GiB write between them (inputs out of the caches)")
+    ap.add_argument("--microbench", action="store_true",
+                    help="also run the roofline microbenchmarks (exp, fp32 FMA and bf16 MFMA issue rates, their "
+                         "mixes, the partial kernels' tile loop in isolation, HBM read and copy rates) into a 'microbench' field")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy before the timed region (a reference "
                          "dispatch for scaling the HBM byte counters of a profile)")
@@ -157,6 +160,82 @@ def cpu_baseline(w, heads):
             "sample": f"{heads} of {w.B * w.H} (b, h) slices (b=0, h<{heads}), all {w.N} tokens, M={w.M}, D={w.D}, "
                       f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded",
             "host_logical_cpus": os.cpu_count(), "cpu_model": model}
+
+
+def microbench():
+    """The denominators of the rooflines, measured: the issue rate of v_exp_f32, of fp32 FMAs and of
+    32x32x16 bf16 MFMAs, alone and mixed (a mix that takes about as long as its slower part alone
+    shows that the two pipes overlap), at 4 waves per SIMD on every SIMD of the chip; the partial
+    kernels' tile loop in isolation (register forms, LDS operands, 16-wave workgroups, a barrier
+    every 8 tiles); and HBM read and copy bandwidth over 2 GiB. Rates are per second over the whole
+    device; times per wave instruction are per SIMD."""
+    import ctypes
+
+    import torch
+
+    from rank_latent_routing_amd.build import MB_LIB
+    if not os.path.exists(MB_LIB):
+        raise RuntimeError(f"{MB_LIB} is missing: build it with `python -m rank_latent_routing_amd.build`")
+    L = ctypes.CDLL(MB_LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.flarepp_mb_compute.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
+    L.flarepp_mb_compute.restype = i32
+    L.flarepp_mb_stream.argtypes = [vp, vp, i64, i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
+    L.flarepp_mb_stream.restype = i32
+    L.flarepp_mb_kind_name.argtypes = [i32]
+    L.flarepp_mb_kind_name.restype = ctypes.c_char_p
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    wps = 4
+    grid = cus * 4 * wps // 4
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    iters = 4096
+    # Per loop iteration and lane: (exps, fmas, MFMAs) of each kind, in the library's order.
+    work = {"exp": (8, 0, 0), "fma": (0, 8, 0), "exp+fma": (8, 8, 0), "mfma": (0, 0, 4), "mfma+fma": (0, 32, 4),
+            "mfma+exp": (16, 0, 4), "mfma+exp+fma": (16, 16, 4), "tile": (16, 0, 0), "tile_agpr_acc": (16, 0, 0),
+            "tile_lds": (16, 0, 0), "tile_lds_wg16": (16, 0, 0), "tile_lds_wg16_sync8": (16, 0, 0),
+            "tile_lds_wg16_sync8_random": (16, 0, 0), "exp_f16": (8, 0, 0), "tile_random_no_row_sums": (16, 0, 0),
+            "tile_random_dot2_row_sums": (16, 0, 0), "mfma_random": (0, 0, 4)}
+    res = {"cus": cus, "waves_per_simd": wps, "iters": iters, "kinds": {}}
+    lanes = grid * 256
+    waves = grid * 4
+    for k in range(len(work)):
+        name = L.flarepp_mb_kind_name(k).decode()
+        ms = ctypes.c_double()
+        rc = L.flarepp_mb_compute(k, grid, iters, 5, ctypes.c_void_p(out.data_ptr()), stream, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"microbenchmark {name}: HIP error {rc}")
+        t = ms.value * 1e-3
+        ne, nf, nm = work[name]
+        # Time per wave instruction on one SIMD: launch time over the instructions each SIMD issues.
+        rec = {"ms": round(ms.value, 4)}
+        if ne:
+            rec["exp_per_s"] = lanes * iters * ne / t
+            rec["ns_per_wave_exp"] = round(t * 1e9 / (iters * ne * wps), 3)
+        if nf:
+            rec["fma_per_s"] = lanes * iters * nf / t
+            rec["ns_per_wave_fma"] = round(t * 1e9 / (iters * nf * wps), 3)
+        if nm:
+            rec["mfma_tflops"] = round(waves * iters * nm * 32 * 32 * 16 * 2 / t * 1e-12, 1)
+        if name.startswith("tile"):
+            # One 32x32 score tile per wave and iteration: time per tile on one SIMD.
+            rec["ns_per_tile_per_simd"] = round(t * 1e9 / (iters * wps), 2)
+        res["kinds"][name] = rec
+    del out
+    nbytes = 2 ** 31
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    sgrid = cus * 8
+    red = torch.empty(sgrid * 256, dtype=torch.float32, device="cuda")
+    for name, d, moved in (("hbm_read", None, nbytes), ("hbm_copy", dst, 2 * nbytes)):
+        ms = ctypes.c_double()
+        rc = L.flarepp_mb_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(0 if d is None else d.data_ptr()),
+                                 nbytes, sgrid, 5, ctypes.c_void_p(red.data_ptr()), stream, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"microbenchmark {name}: HIP error {rc}")
+        res[name + "_gbs"] = round(moved / (ms.value * 1e-3) * 1e-9, 1)
+    return res
 
 
 def _kernel_times(steps, call):
@@ -504,6 +583,8 @@ def main():
         leg("backward", backward, args, w, dev, dt_code, peak)
     if not args.no_block:
         leg("block", block, args, w, dt_code)
+    if args.microbench:
+        leg("microbench", microbench)
     if not args.no_cpu_baseline:
         leg("cpu_baseline", cpu_baseline, w, args.cpu_sample_heads)
     print(json.dumps(res), flush=True)

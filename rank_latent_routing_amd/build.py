@@ -1,5 +1,7 @@
 """Build step of the FLARE++ mixer library: compiles the HIP sources for gfx950 into
-``rank_latent_routing_amd/libflarepp.so`` with hipcc.
+``rank_latent_routing_amd/libflarepp.so`` with hipcc, and the roofline microbenchmarks into
+``rank_latent_routing_amd/libflarepp_microbench.so`` (a library of their own, used only by the
+benchmark script).
 
 Usage: ``python -m rank_latent_routing_amd.build`` (or ``__graft_entry__.build()``).
 """
@@ -13,6 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflarepp.so")
 SOURCES = [os.path.join(PKG, "csrc", n) for n in ("kernels.hip", "backward.hip", "project.hip", "flarepp.cpp")]
+MB_LIB = os.path.join(PKG, "libflarepp_microbench.so")
+MB_SOURCES = [os.path.join(PKG, "csrc", "microbench.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
@@ -21,12 +25,11 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always, even when a built copy exists) and return its path."""
+def _compile(sources, lib, verbose):
     hipcc = os.environ.get("HIPCC", "hipcc")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(PKG, "csrc")]
-    for src in SOURCES:
+    for src in sources:
         cmd += ["-x", "hip", src]
     cmd += ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,8 +39,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library and the microbenchmarks (always, even when built copies exist) and return
+    the library's path."""
+    _compile(MB_SOURCES, MB_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -249,3 +249,20 @@ def test_block_validation_and_workspace(L):
         # The mixer's workspace plus K, V, S and the mixer output, the seeds and the gates.
         assert ws >= fl.flarepp_workspace_bytes(B, H, N, M, D, dt) + 4 * B * H * N * D * es + H * M * D * es
         assert ws < fl.flarepp_workspace_bytes(B, H, N, M, D, dt) + 4 * B * H * N * D * es + H * M * D * es + 2048
+
+
+def test_microbenchmark_library_loads_and_validates():
+    # The roofline microbenchmarks live in a library of their own; invalid sizes are refused before
+    # any launch (no GPU needed).
+    from rank_latent_routing_amd.build import MB_LIB
+    M = ctypes.CDLL(MB_LIB)
+    for n in ("flarepp_mb_compute", "flarepp_mb_stream", "flarepp_mb_kind_name", "flarepp_mb_num_kinds"):
+        assert hasattr(M, n), n
+    M.flarepp_mb_kind_name.restype = ctypes.c_char_p
+    kinds = [M.flarepp_mb_kind_name(i).decode() for i in range(M.flarepp_mb_num_kinds())]
+    assert kinds[:4] == ["exp", "fma", "exp+fma", "mfma"] and "tile_lds_wg16_sync8_random" in kinds
+    assert M.flarepp_mb_kind_name(len(kinds)) is None
+    ms = ctypes.c_double()
+    vp = ctypes.c_void_p
+    assert M.flarepp_mb_compute(0, 0, 16, 1, vp(0x1000), vp(0), ctypes.byref(ms)) != 0
+    assert M.flarepp_mb_stream(vp(0x1000), vp(0x2000), ctypes.c_int64(15), 1, 1, vp(0), vp(0), ctypes.byref(ms)) != 0
