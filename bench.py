@@ -60,13 +60,23 @@ PROJECT_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n i
 BLOCK_PROFILE = os.path.join(ROOT, "profiles", "flarepp_block_1M_tokens.md")
 
 
+def _code_only(text):
+    """Source text with // and /* */ comments and trailing blanks removed: a comment edit leaves the
+    compiled kernels, and so a profile taken on them, unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash(srcs=None):
-    """sha256 over kernel sources (default: the forward's, kernels.hip then device.h)."""
+    """sha256 over the code of kernel sources, comments removed (default: the forward's, kernels.hip
+    then device.h)."""
     import hashlib
     h = hashlib.sha256()
     for src in srcs or KERNEL_SRCS:
-        with open(src, "rb") as f:
-            h.update(f.read())
+        with open(src, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -177,7 +177,8 @@ int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const v
  * The block around the mixer: the feature projections in front of it, the per-head normalizations
  * and the output projection (Section 3.2: the synthesis keys of Eq. 5, the routing keys and values
  * before Eq. 8, the seeds and the gate of Eq. 6-7; Appendix C.2 for which tensors carry the learned-
- * scale normalization N_a; Section 2 for the head split and the output projection).
+ * scale normalization N_a; Section 3.1, "Full self-attention", for the head split and the output
+ * projection).
  *
  * Layouts (row-major, contiguous, element type `dtype` unless stated):
  *   X, out         : [B, N, C] with C = H * D; head h owns channels h*D .. h*D + D - 1

@@ -329,11 +329,6 @@ def encode_sharded(Q: np.ndarray, K: np.ndarray, V: np.ndarray, bounds) -> tuple
     return U / d[:, None], L_max + np.log(d)
 
 
-def decode_rows(K_rows: np.ndarray, Q: np.ndarray, Z: np.ndarray) -> np.ndarray:
-    """Decode (Eq. 8, second call) for a chosen subset of token rows only."""
-    return sdpa(K_rows, Q, Z)
-
-
 # ---- The block around the mixer: feature projections, per-head normalizations, output projection --
 
 def rms_normalize_scaled(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
@@ -345,14 +340,14 @@ def rms_normalize_scaled(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 
 def split_heads(T: np.ndarray, H: int) -> np.ndarray:
-    """[B, N, C] -> [B, H, N, D], D = C / H: head h owns channels h D .. h D + D - 1 (Section 2, the
-    projections split into H heads of width D = C / H)."""
+    """[B, N, C] -> [B, H, N, D], D = C / H: head h owns channels h D .. h D + D - 1 (Section 3.1,
+    "Full self-attention": the projections split into H heads of width D = C / H)."""
     B, N, C = T.shape
     return np.ascontiguousarray(T.reshape(B, N, H, C // H).transpose(0, 2, 1, 3))
 
 
 def merge_heads(Y: np.ndarray) -> np.ndarray:
-    """[B, H, N, D] -> [B, N, H D]: the head outputs concatenated along the channels (Section 2)."""
+    """[B, H, N, D] -> [B, N, H D]: the head outputs concatenated along the channels (Section 3.1, "Full self-attention")."""
     B, H, N, D = Y.shape
     return np.ascontiguousarray(Y.transpose(0, 2, 1, 3).reshape(B, N, H * D))
 
@@ -374,7 +369,8 @@ def project(X, Wk, Wv, Ws, H, nk, bk=None, bv=None, bs=None):
 
 
 def out_project(Y, Wo, bo=None):
-    """The output projection: heads concatenated, then W_O (Section 2). Y [B, H, N, D] -> [B, N, C]."""
+    """The output projection: heads concatenated, then W_O (Section 3.1, "Full self-attention").
+    Y [B, H, N, D] -> [B, N, C]."""
     return linear(merge_heads(Y), Wo, bo)
 
 

@@ -1,8 +1,8 @@
 // Projections around the FLARE++ mixer ("FLARE++: Low-rank attention with attention-synthesized
 // routing"): the synthesis keys of Section 3.2 Eq. 5, the routing keys and values before Eq. 8 with
 // the learned-scale normalization N_a on the keys (Appendix C.2 lists where N_a and N0 apply), the
-// head split and the output projection of Section 2, and the per-head seed normalization and gate
-// logistic of Eq. 6-7.
+// head split and the output projection of Section 3.1 ("Full self-attention"), and the per-head seed
+// normalization and gate logistic of Eq. 6-7.
 //
 // A projection is Out = X W^T with C <= 512 input channels (W in torch's Linear layout: row o holds
 // output channel o). One wave owns one output group of 32 channels. The group's weight rows (32

@@ -1,6 +1,7 @@
 """GPU parity of the projections around the mixer and of the whole block (flarepp_project,
 flarepp_out_project, flarepp_block, through the C ABI) against the float64 oracle (``project``,
-``out_project``, ``mixer_block``): Section 3.2 Eq. 5-8, Appendix A.6-A.7 and C.2, Section 2.
+``out_project``, ``mixer_block``): Section 3.2 Eq. 5-8, Appendix A.6-A.7 and C.2, Section 3.1
+("Full self-attention") for the head split and the output projection.
 
 Bars:
 * projections, fp32: max |x - x_ref| / max |x_ref| <= 1e-5 per (b, h) slice (per b for the output
@@ -244,7 +245,7 @@ def test_full_size_block_constant_values():
     # configuration the benchmark times, against a closed form: with a value projection that ignores
     # X (Wv = 0), V is the bias bv in every token; a row-stochastic operator maps a constant field to
     # itself (Section 3.1, Eq. 4), whatever the keys and routing queries, so every output row is
-    # concat_h(bv_h) Wo^T + bo (Section 2). Every output element is checked.
+    # concat_h(bv_h) Wo^T + bo (Section 3.1, "Full self-attention"). Every output element is checked.
     import rank_latent_routing_amd as fl
     from workloads.gen import _store
     w = make_workload(5, N=64)  # only its seeds Qseed and Qf are used

@@ -33,16 +33,22 @@ def _case(seed=0, N=64, M=8, D=16, g=None):
 # ---------------------------------------------------------------- library cross-checks
 
 def _torch_mixer(K, V, S, Qseed, Qf, g):
-    """The three-SDPA composition of the mixer, evaluated with torch's CPU SDPA in float64
-    (the author's blog sketch: normalized shared synthesis keys, gated sum, encode, decode)."""
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)[None, None]
-    D = K.shape[-1]
-    Ks = F.rms_norm(t(S), (D,), eps=orc.RMS_EPS)
-    Qd = F.scaled_dot_product_attention(t(Qseed), Ks, Ks)
-    Q = F.rms_norm(t(Qf), (D,), eps=orc.RMS_EPS) + g * Qd
-    Z = F.scaled_dot_product_attention(Q, t(K), t(V))
-    Y = F.scaled_dot_product_attention(t(K), Q, Z)
-    return {k: v[0, 0].numpy() for k, v in dict(Qd=Qd, Q=Q, Z=Z, Y=Y).items()}
+    """One head of the mixer from torch float64 library calls, in the routing-factor form of
+    Section 3.1 (Eq. 3-4) rather than the oracle's: the synthesis call (Eq. 5-6) through torch's
+    scaled_dot_product_attention on the rms_norm-ed synthesis rows (keys and values at once), the
+    gate blend of Eq. 7, then the encode and decode factors W_enc = softmax over tokens and
+    W_dec = softmax over latents of one score matrix (Eq. 8), applied as Y = W_dec (W_enc V)."""
+    as_t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
+    width = K.shape[-1]
+    unit_rms = lambda x: F.rms_norm(x, (width,), eps=orc.RMS_EPS)
+    syn_rows = unit_rms(as_t(S))
+    correction = F.scaled_dot_product_attention(as_t(Qseed)[None], syn_rows[None], syn_rows[None])[0]
+    routing = unit_rms(as_t(Qf)) + g * correction
+    scores = routing @ as_t(K).T / math.sqrt(width)  # [M, N]
+    w_enc = torch.softmax(scores, dim=1)
+    w_dec = torch.softmax(scores.T, dim=1)
+    latents = w_enc @ as_t(V)
+    return {"Qd": correction.numpy(), "Q": routing.numpy(), "Z": latents.numpy(), "Y": (w_dec @ latents).numpy()}
 
 
 def check_library(seed=1, N=200, M=12, D=16):

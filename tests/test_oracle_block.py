@@ -1,10 +1,10 @@
 """Pins of the oracle's mixer block: the projections in front of the mixer, the per-head
 normalizations, the gate logit and the output projection (Section 3.2, Eq. 5-8; Appendix A.5-A.7,
-C.2; Section 2 for the head split and the output projection). CPU only.
+C.2; Section 3.1, "Full self-attention", for the head split and the output projection). CPU only.
 
 The pins:
-* torch's own primitives (linear, rms_norm with and without weight, sigmoid, SDPA, unflatten and
-  transpose for the head split) composed as the pages' mixer sketch composes them, in float64;
+* torch's own primitives (matmul, rms_norm with and without weight, sigmoid, SDPA), one (batch,
+  head) at a time over the heads' channel ranges, in float64;
 * the near-identity initialization of Appendix A.5 at Delta W = 0 (W = I, no bias): the keys are the
   input's head slices, RMS-normalized, written out with explicit loops;
 * every routing-key row has the RMS of the key scale (N_a), whatever the input;
@@ -43,22 +43,37 @@ def _run(impl, c):
 
 
 def _torch_block(c):
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
-    X = t(c["X"])
-    H, M, D = c["Qseed"].shape
-    split = lambda T: T.unflatten(-1, (H, D)).transpose(1, 2)
-    n0 = lambda T: F.rms_norm(T, (D,), eps=orc.RMS_EPS)
-    na = lambda T, w: F.rms_norm(T, (D,), weight=t(w), eps=orc.RMS_EPS)
-    lin = lambda W, b: F.linear(X, t(W).T, t(b))  # torch's linear takes W as [out, in]
-    Ks = n0(split(lin(c["Ws"], c["bs"])))
-    Qd = F.scaled_dot_product_attention(na(t(c["Qseed"]), c["nq"]).unsqueeze(0), Ks, Ks)
-    g = torch.sigmoid(t(c["gamma"])).view(1, H, 1, 1)
-    Q = n0(t(c["Qf"])).unsqueeze(0) + g * Qd
-    K = na(split(lin(c["Wk"], c["bk"])), c["nk"])
-    V = split(lin(c["Wv"], c["bv"]))
-    Z = F.scaled_dot_product_attention(Q, K, V)
-    Y = F.scaled_dot_product_attention(K, Q, Z)
-    out = F.linear(Y.transpose(1, 2).flatten(2), t(c["Wo"]).T, t(c["bo"]))
+    """The block from torch float64 library calls, one (batch, head) at a time: the projections as
+    X W + b (torch.matmul), head h as the channel range h D .. h D + D - 1 (Section 3.1, "Full
+    self-attention"), N_a and N0 by torch's rms_norm (Section 3.2; Appendix C.2), the gate
+    g_h = sigmoid(gamma_h) (Eq. 7), the mixer of Eq. 5-8 with torch's scaled_dot_product_attention
+    per call, and the outputs of all heads written back into their channel ranges before W_O."""
+    as_t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
+    X = as_t(c["X"])
+    n_heads, _, width = c["Qseed"].shape
+    unit_rms = lambda x: F.rms_norm(x, (width,), eps=orc.RMS_EPS)
+    scaled_rms = lambda x, w: F.rms_norm(x, (width,), weight=as_t(w), eps=orc.RMS_EPS)
+    attend = lambda q, k, v: F.scaled_dot_product_attention(q[None], k[None], v[None])[0]
+    keys_all = X @ as_t(c["Wk"]) + as_t(c["bk"])
+    values_all = X @ as_t(c["Wv"]) + as_t(c["bv"])
+    syn_all = X @ as_t(c["Ws"]) + as_t(c["bs"])
+    K = torch.empty(X.shape[0], n_heads, X.shape[1], width, dtype=torch.float64)
+    V = torch.empty_like(K)
+    Y = torch.empty_like(K)
+    merged = torch.empty_like(X)
+    for b in range(X.shape[0]):
+        for h in range(n_heads):
+            cols = slice(h * width, (h + 1) * width)
+            K[b, h] = scaled_rms(keys_all[b, :, cols], c["nk"])
+            V[b, h] = values_all[b, :, cols]
+            syn = unit_rms(syn_all[b, :, cols])
+            correction = attend(scaled_rms(as_t(c["Qseed"][h]), c["nq"]), syn, syn)
+            gate_h = torch.sigmoid(as_t(c["gamma"][h]))
+            routing = unit_rms(as_t(c["Qf"][h])) + gate_h * correction
+            latents = attend(routing, K[b, h], V[b, h])
+            Y[b, h] = attend(K[b, h], routing, latents)
+            merged[b, :, cols] = Y[b, h]
+    out = merged @ as_t(c["Wo"]) + as_t(c["bo"])
     return {"K": K.numpy(), "V": V.numpy(), "Y": Y.numpy(), "out": out.numpy()}
 
 
@@ -118,7 +133,7 @@ def _pins(impl):
             and check_head_permutation(impl) < 1e-12)
 
 
-def test_matches_torch_composition_of_the_sketch():
+def test_matches_torch_per_head_composition():
     assert check_torch_composition(oracle.mixer_block) < 1e-12
     assert check_torch_composition(oracle.mixer_block, seed=5, H=4, D=32, N=33) < 1e-12
 
