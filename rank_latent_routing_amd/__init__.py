@@ -153,6 +153,34 @@ def _check(status: int, what: str):
         raise FlareppError(status, what)
 
 
+def _require_like(name, t, shape, dtype):
+    """A caller-supplied output: a contiguous tensor of the given shape and dtype."""
+    import torch
+    if not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def _require_device(ref, **tensors):
+    """Every tensor (None entries skipped) lives on ref's GPU: the kernels read and write them
+    there, so a host tensor or another GPU's memory would be a fault, not an error."""
+    import torch
+    if not isinstance(ref, torch.Tensor) or ref.device.type != "cuda":
+        raise ValueError("the mixer's tensors must be on a GPU (device 'cuda')")
+    for name, t in tensors.items():
+        if t is not None and (not isinstance(t, torch.Tensor) or t.device != ref.device):
+            raise ValueError(f"{name} must be on {ref.device}, the device of the other tensors")
+
+
+def _require_workspace(workspace, device):
+    """A caller-owned workspace: a contiguous uint8 tensor on the mixer's GPU (its numel() is the
+    byte count the library checks against the size it needs)."""
+    import torch
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}")
+
+
 def flarepp_workspace_bytes(B: int, H: int, N: int, M: int, D: int, dtype: int) -> int:
     return int(lib().flarepp_workspace_bytes(B, H, N, M, D, dtype))
 
@@ -163,6 +191,9 @@ def flarepp_mix(K, V, S, Qseed, Qf, g, out=None, stream=None):
     allocates its workspace stream-ordered."""
     import torch
     B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, S=S, Qseed=Qseed, Qf=Qf, g=g, out=out)
     if out is None:
         out = torch.empty_like(K)
     st = lib().flarepp_mix(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D,
@@ -176,6 +207,8 @@ def _workspace(B, H, N, M, D, dt, device, workspace):
     need = flarepp_workspace_bytes(B, H, N, M, D, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    else:
+        _require_workspace(workspace, device)
     return workspace, need
 
 
@@ -185,6 +218,9 @@ def flarepp_mix_ws(K, V, S, Qseed, Qf, g, out=None, workspace=None, stream=None)
     import torch
     B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
     dt = _dtype_code(K)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, S=S, Qseed=Qseed, Qf=Qf, g=g, out=out)
     if out is None:
         out = torch.empty_like(K)
     workspace, _ = _workspace(B, H, N, M, D, dt, K.device, workspace)
@@ -199,6 +235,9 @@ def flarepp_mix_debug(K, V, S, Qseed, Qf, g, out=None, workspace=None, stream=No
     import torch
     B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
     dt = _dtype_code(K)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, S=S, Qseed=Qseed, Qf=Qf, g=g, out=out)
     if out is None:
         out = torch.empty_like(K)
     workspace, _ = _workspace(B, H, N, M, D, dt, K.device, workspace)
@@ -231,6 +270,11 @@ def flarepp_flare(K, V, Q, out=None, workspace=None, stream=None):
     import torch
     B, H, N, M, D = _flare_shapes(K, V, Q)
     dt = _dtype_code(K)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, Q=Q, out=out)
+    if workspace is not None:
+        _require_workspace(workspace, K.device)
     if out is None:
         out = torch.empty_like(K)
     if workspace is None:
@@ -257,6 +301,16 @@ def flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=None, workspace=None, 
     if dY.shape != K.shape or dY.dtype != K.dtype or not dY.is_contiguous():
         raise ValueError("dY must be a contiguous tensor of K's shape and dtype")
     dt = _dtype_code(K)
+    if grads is not None:
+        expect = {"dK": K, "dV": K, "dS": K, "dQseed": Qseed, "dQf": Qf, "dg": g}
+        for name, like in expect.items():
+            if name not in grads:
+                raise ValueError(f"grads must hold {name}")
+            _require_like(f"grads[{name!r}]", grads[name], like.shape, like.dtype)
+    _require_device(K, V=V, S=S, Qseed=Qseed, Qf=Qf, g=g, dY=dY,
+                    **({f"grads[{k!r}]": v for k, v in grads.items()} if grads is not None else {}))
+    if workspace is not None:
+        _require_workspace(workspace, K.device)
     if grads is None:
         grads = {"dK": torch.empty_like(K), "dV": torch.empty_like(K), "dS": torch.empty_like(K),
                  "dQseed": torch.empty_like(Qseed), "dQf": torch.empty_like(Qf), "dg": torch.empty_like(g)}
@@ -286,6 +340,11 @@ def flarepp_mix_simplified(K, V, Sk, Sv, Qseed, out=None, workspace=None, stream
             raise ValueError("all tensors must be contiguous and share one dtype")
     M = Qseed.shape[1]
     dt = _dtype_code(K)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, Sk=Sk, Sv=Sv, Qseed=Qseed, out=out)
+    if workspace is not None:
+        _require_workspace(workspace, K.device)
     if out is None:
         out = torch.empty_like(K)
     args = [_ptr(K), _ptr(V), _ptr(Sk), _ptr(Sv), _ptr(Qseed), B, H, N, M, D, dt, _ptr(out)]
@@ -326,6 +385,13 @@ def flarepp_project(X, Wk, Wv, Ws, H, bk=None, bv=None, bs=None, nk=None, out=No
     nk [D] optional. Returns (K, V, S); `out` may supply them."""
     import torch
     B, N, C, D = _linear_args(X, (Wk, Wv, Ws), (bk, bv, bs), (nk,), H)
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be a tuple (K, V, S)")
+        for name, t in zip("KVS", out):
+            _require_like(f"out {name}", t, (B, H, N, D), X.dtype)
+    _require_device(X, Wk=Wk, Wv=Wv, Ws=Ws, bk=bk, bv=bv, bs=bs, nk=nk,
+                    **({f"out {n}": t for n, t in zip("KVS", out)} if out is not None else {}))
     if out is None:
         out = tuple(torch.empty((B, H, N, D), dtype=X.dtype, device=X.device) for _ in range(3))
     K, V, S = out
@@ -348,6 +414,9 @@ def flarepp_out_project(Y, Wo, bo=None, out=None, stream=None):
     for t in (Y, Wo, bo):
         if t is not None and (not t.is_contiguous() or t.dtype != Y.dtype):
             raise ValueError("all tensors must be contiguous and share Y's dtype")
+    if out is not None:
+        _require_like("out", out, (B, N, C), Y.dtype)
+    _require_device(Y, Wo=Wo, bo=bo, out=out)
     if out is None:
         out = torch.empty((B, N, C), dtype=Y.dtype, device=Y.device)
     st = lib().flarepp_out_project(_ptr(Y), _ptr(Wo), _ptr(bo), B, H, N, D, _dtype_code(Y), _ptr(out),
@@ -379,6 +448,12 @@ def flarepp_block(X, Wk, Wv, Ws, Wo, Qseed, Qf, gamma, bk=None, bv=None, bs=None
             raise ValueError("Qseed and Qf must be contiguous and share X's dtype")
     if gamma.shape != (H,) or gamma.dtype != torch.float32 or not gamma.is_contiguous():
         raise ValueError("gamma must be a contiguous float32 tensor of shape [H]")
+    if out is not None:
+        _require_like("out", out, (B, N, C), X.dtype)
+    _require_device(X, Wk=Wk, Wv=Wv, Ws=Ws, Wo=Wo, bk=bk, bv=bv, bs=bs, bo=bo, Qseed=Qseed, Qf=Qf, gamma=gamma,
+                    nq=nq, nk=nk, out=out)
+    if workspace is not None:
+        _require_workspace(workspace, X.device)
     if out is None:
         out = torch.empty((B, N, C), dtype=X.dtype, device=X.device)
     args = [_ptr(t) for t in (X, Wk, Wv, Ws, Wo, bk, bv, bs, bo, Qseed, Qf, gamma, nq, nk)]

@@ -266,3 +266,79 @@ def test_microbenchmark_library_loads_and_validates():
     vp = ctypes.c_void_p
     assert M.flarepp_mb_compute(0, 0, 16, 1, vp(0x1000), vp(0), ctypes.byref(ms)) != 0
     assert M.flarepp_mb_stream(vp(0x1000), vp(0x2000), ctypes.c_int64(15), 1, 1, vp(0), vp(0), ctypes.byref(ms)) != 0
+
+
+def _host_inputs(B=1, H=2, N=40, M=8, D=16, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    big = lambda: torch.zeros((B, H, N, D), dtype=dtype)
+    return dict(K=big(), V=big(), S=big(), Qseed=torch.zeros((H, M, D), dtype=dtype),
+                Qf=torch.zeros((H, M, D), dtype=dtype), g=torch.zeros(H, dtype=torch.float32))
+
+
+def test_binding_checks_outputs_before_any_launch():
+    # Caller-supplied outputs of the wrong shape, dtype or layout are refused by the binding; every
+    # case here raises before the library is asked to launch anything (host tensors, no GPU).
+    import torch
+    x = _host_inputs()
+    bad_out = (torch.zeros((1, 2, 39, 16), dtype=torch.bfloat16), torch.zeros((1, 2, 40, 16), dtype=torch.float32),
+               torch.zeros((1, 2, 16, 40), dtype=torch.bfloat16).transpose(2, 3))
+    for out in bad_out:
+        for fn in (fl.flarepp_mix, fl.flarepp_mix_ws, fl.flarepp_mix_debug):
+            with pytest.raises(ValueError, match="out must be"):
+                fn(x["K"], x["V"], x["S"], x["Qseed"], x["Qf"], x["g"], out=out)
+        with pytest.raises(ValueError, match="out must be"):
+            fl.flarepp_flare(x["K"], x["V"], x["Qf"], out=out)
+        with pytest.raises(ValueError, match="out must be"):
+            fl.flarepp_mix_simplified(x["K"], x["V"], x["S"], x["S"], x["Qseed"], out=out)
+    grads = {"dK": torch.zeros_like(x["K"]), "dV": torch.zeros_like(x["K"]), "dS": torch.zeros_like(x["K"]),
+             "dQseed": torch.zeros_like(x["Qseed"]), "dQf": torch.zeros_like(x["Qf"]), "dg": torch.zeros(2)}
+    dY = torch.zeros_like(x["K"])
+    for name, bad in (("dK", torch.zeros((1, 2, 40, 8), dtype=torch.bfloat16)), ("dQf", torch.zeros((2, 8, 16))),
+                      ("dg", torch.zeros(3))):
+        g2 = dict(grads, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            fl.flarepp_mix_backward(x["K"], x["V"], x["S"], x["Qseed"], x["Qf"], x["g"], dY, grads=g2)
+    with pytest.raises(ValueError, match="dS"):
+        fl.flarepp_mix_backward(x["K"], x["V"], x["S"], x["Qseed"], x["Qf"], x["g"], dY,
+                                grads={k: v for k, v in grads.items() if k != "dS"})
+    # Projections and the block: outputs of the wrong shape.
+    X = torch.zeros((1, 40, 32), dtype=torch.bfloat16)
+    W = torch.zeros((32, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out K"):
+        fl.flarepp_project(X, W, W, W, 2, out=(torch.zeros((1, 2, 40, 8), dtype=torch.bfloat16),) * 3)
+    with pytest.raises(ValueError, match="out must be"):
+        fl.flarepp_out_project(x["K"], W, out=torch.zeros((1, 40, 16), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        fl.flarepp_block(X, W, W, W, W, x["Qseed"], x["Qf"], torch.zeros(2), out=torch.zeros((1, 41, 32),
+                                                                                            dtype=torch.bfloat16))
+
+
+def test_binding_requires_gpu_tensors_and_a_byte_workspace():
+    import torch
+    x = _host_inputs()
+    args = (x["K"], x["V"], x["S"], x["Qseed"], x["Qf"], x["g"])
+    # Host tensors with correct shapes: refused as not on a GPU.
+    for fn in (fl.flarepp_mix, fl.flarepp_mix_ws, fl.flarepp_mix_debug):
+        with pytest.raises(ValueError, match="GPU"):
+            fn(*args)
+    with pytest.raises(ValueError, match="GPU"):
+        fl.flarepp_flare(x["K"], x["V"], x["Qf"])
+    with pytest.raises(ValueError, match="GPU"):
+        fl.flarepp_mix_backward(*args, torch.zeros_like(x["K"]))
+    with pytest.raises(ValueError, match="GPU"):
+        fl.flarepp_mix_simplified(x["K"], x["V"], x["S"], x["S"], x["Qseed"])
+    X = torch.zeros((1, 40, 32), dtype=torch.bfloat16)
+    W = torch.zeros((32, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fl.flarepp_project(X, W, W, W, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        fl.flarepp_out_project(x["K"], W)
+    with pytest.raises(ValueError, match="GPU"):
+        fl.flarepp_block(X, W, W, W, W, x["Qseed"], x["Qf"], torch.zeros(2))
+    # A workspace that is not bytes, or not contiguous.
+    for ws in (torch.zeros(100, dtype=torch.float32), torch.zeros(200, dtype=torch.uint8)[::2]):
+        with pytest.raises(ValueError, match="workspace"):
+            fl._require_workspace(ws, torch.device("cpu"))
+    with pytest.raises(ValueError, match="workspace must be on"):
+        fl._require_workspace(torch.zeros(100, dtype=torch.uint8), torch.device("cuda", 0))
