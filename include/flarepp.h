@@ -68,7 +68,9 @@ enum flarepp_status {
   FLAREPP_MISALIGNED = 3,       /* a tensor pointer that is not 16-byte aligned */
   FLAREPP_OUT_OF_MEMORY = 4,    /* workspace allocation failed */
   FLAREPP_LAUNCH_FAILED = 5,    /* a kernel launch was rejected by the runtime */
-  FLAREPP_DEVICE_ERROR = 6      /* the HIP runtime reported an error while querying the device */
+  FLAREPP_DEVICE_ERROR = 6,     /* the HIP runtime reported an error while querying the device */
+  FLAREPP_SCRATCH_TOO_SMALL = 7 /* flarepp_mix_noalloc: the problem needs more workspace than the
+                                   static scratch holds (FLAREPP_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* Element types of K, V, S, Qseed, Qf and out. */
@@ -97,6 +99,22 @@ size_t flarepp_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype)
 int flarepp_mix_ws(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
                    const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): flarepp_mix with its workspace in a static device array of
+ * FLAREPP_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs on until the
+ * process ends. The call allocates nothing (no hipMalloc, hipFree or allocating library routine) and
+ * otherwise behaves as flarepp_mix_ws. A problem whose workspace, flarepp_workspace_bytes(...),
+ * exceeds the scratch returns FLAREPP_SCRATCH_TOO_SMALL and enqueues nothing; 32 MiB holds every
+ * shape up to the 1M-token one (B=1, H=8, N=2^20, M=512, D=32: about 18 MiB). All calls on one GPU
+ * share that GPU's scratch: calls that overlap on one GPU (other streams, other threads) race, so a
+ * caller serializes them, for instance on one stream.
+ */
+#define FLAREPP_NOALLOC_SCRATCH_BYTES (32u << 20)
+int flarepp_mix_noalloc(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                        const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
+                        hipStream_t stream);
 
 /*
  * flarepp_mix_ws that also exports the per-(b,h) latent stages as fp32 device arrays of shape

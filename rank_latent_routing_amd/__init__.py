@@ -20,6 +20,9 @@ FLAREPP_MISALIGNED = 3
 FLAREPP_OUT_OF_MEMORY = 4
 FLAREPP_LAUNCH_FAILED = 5
 FLAREPP_DEVICE_ERROR = 6
+FLAREPP_SCRATCH_TOO_SMALL = 7
+# Bytes of the static device scratch of flarepp_mix_noalloc (FLAREPP_NOALLOC_SCRATCH_BYTES).
+FLAREPP_NOALLOC_SCRATCH_BYTES = 32 << 20
 FLAREPP_FP32 = 0
 FLAREPP_BF16 = 1
 
@@ -45,6 +48,8 @@ def lib() -> ctypes.CDLL:
     mix_args = [vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp]
     L.flarepp_mix.argtypes = mix_args + [vp]
     L.flarepp_mix.restype = i32
+    L.flarepp_mix_noalloc.argtypes = mix_args + [vp]
+    L.flarepp_mix_noalloc.restype = i32
     L.flarepp_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.flarepp_workspace_bytes.restype = sz
     L.flarepp_mix_ws.argtypes = mix_args + [vp, sz, vp]
@@ -199,6 +204,24 @@ def flarepp_mix(K, V, S, Qseed, Qf, g, out=None, stream=None):
     st = lib().flarepp_mix(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D,
                            _dtype_code(K), _ptr(out), _stream_ptr(stream, K.device))
     _check(st, "flarepp_mix")
+    return out
+
+
+def flarepp_mix_noalloc(K, V, S, Qseed, Qf, g, out=None, stream=None):
+    """flarepp_mix with its workspace in the library's static device scratch: the C call allocates
+    nothing (for callers that cannot allocate). Calls that overlap on one GPU race; problems whose
+    workspace exceeds FLAREPP_NOALLOC_SCRATCH_BYTES raise (status FLAREPP_SCRATCH_TOO_SMALL). `out`
+    should be supplied by a caller that cannot allocate (torch allocates it otherwise)."""
+    import torch
+    B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, S=S, Qseed=Qseed, Qf=Qf, g=g, out=out)
+    if out is None:
+        out = torch.empty_like(K)
+    st = lib().flarepp_mix_noalloc(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D,
+                                   _dtype_code(K), _ptr(out), _stream_ptr(stream, K.device))
+    _check(st, "flarepp_mix_noalloc")
     return out
 
 
@@ -488,7 +511,7 @@ def flarepp_timing_read() -> dict:
     return {flarepp_kernel_name(i): (ms[i], cnt[i]) for i in range(k)}
 
 
-__all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_debug", "flarepp_workspace_bytes",
+__all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_noalloc", "FLAREPP_NOALLOC_SCRATCH_BYTES", "flarepp_mix_debug", "flarepp_workspace_bytes",
            "flarepp_flare", "flarepp_mix_simplified", "flarepp_mix_backward", "flarepp_backward_workspace_bytes",
            "flarepp_project", "flarepp_out_project", "flarepp_block", "flarepp_block_workspace_bytes",
            "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",

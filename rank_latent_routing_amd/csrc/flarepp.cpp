@@ -302,6 +302,57 @@ int mix_common(const void* K, const void* V, const void* S, const void* Qseed, c
   return rc;
 }
 
+// ---- The mixer without allocation (flarepp_mix_noalloc)
+//
+// Its workspace is this file-scope device array: every GPU the library runs on holds one copy of it
+// from the module's load until the process ends, at an address of its own. The host never uses the
+// array's name as a device address; it looks the address up once per device and passes that
+// pointer to the kernels, as the other entry points pass their workspace. The workspace needs no
+// clearing: the kernels write every entry they later read. Calls that overlap on one GPU share the
+// array and race.
+__device__ __align__(256) unsigned char scratch[FLAREPP_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up on the first call per device (with
+// that device current) and kept.
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FLAREPP_DEVICE_ERROR;
+  }
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FLAREPP_DEVICE_ERROR;
+    }
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return FLAREPP_OK;
+}
+
+int mix_noalloc_common(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                       const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  rc = validate_pointers(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out);
+  if (rc != FLAREPP_OK) return rc;
+  const Plan p = make_plan(B, H, N, M, D, dtype);
+  if (p.total > (size_t)FLAREPP_NOALLOC_SCRATCH_BYTES) return FLAREPP_SCRATCH_TOO_SMALL;
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  void* ws = nullptr;
+  rc = noalloc_scratch(&ws);
+  if (rc != FLAREPP_OK) return rc;
+  return enqueue(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, nullptr, nullptr, nullptr, ws, p, st);
+}
+
 int flare_common(const void* K, const void* V, const void* Q, int B, int H, int64_t N, int M, int D, int dtype,
                  void* out, void* ws, size_t ws_bytes, bool own_ws, hipStream_t st) {
   bool empty = false;
@@ -840,6 +891,12 @@ int flarepp_mix(const void* K, const void* V, const void* S, const void* Qseed, 
                     true, stream);
 }
 
+int flarepp_mix_noalloc(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                        const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
+                        hipStream_t stream) {
+  return mix_noalloc_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, stream);
+}
+
 size_t flarepp_workspace_bytes(int B, int H, int64_t N, int M, int D, int dtype) {
   bool empty = false;
   if (validate_sizes(B, H, N, M, D, dtype, &empty) != FLAREPP_OK || empty) return 0;
@@ -968,6 +1025,9 @@ const char* flarepp_strerror(int status) {
     case FLAREPP_OUT_OF_MEMORY: return "workspace allocation failed";
     case FLAREPP_LAUNCH_FAILED: return "kernel launch failed";
     case FLAREPP_DEVICE_ERROR: return "HIP runtime error while querying the device";
+    case FLAREPP_SCRATCH_TOO_SMALL:
+      return "the problem's workspace exceeds the static scratch of flarepp_mix_noalloc "
+             "(FLAREPP_NOALLOC_SCRATCH_BYTES); use flarepp_mix_ws";
     default: return "unknown status";
   }
 }

@@ -342,3 +342,25 @@ def test_binding_requires_gpu_tensors_and_a_byte_workspace():
             fl._require_workspace(ws, torch.device("cpu"))
     with pytest.raises(ValueError, match="workspace must be on"):
         fl._require_workspace(torch.zeros(100, dtype=torch.uint8), torch.device("cuda", 0))
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(L):
+    # The no-allocation entry point refuses, before touching any device, a problem whose workspace
+    # exceeds the static scratch; every benchmark workload fits.
+    assert fl.FLAREPP_NOALLOC_SCRATCH_BYTES == 32 << 20
+    for shape in ((1, 2, 1024, 32, 16, 0), (4, 8, 16384, 64, 16, 1), (32, 8, 4096, 128, 32, 1),
+                  (2, 8, 65536, 256, 32, 1), (1, 8, 1 << 20, 512, 32, 1)):
+        assert 0 < fl.flarepp_workspace_bytes(*shape) <= fl.FLAREPP_NOALLOC_SCRATCH_BYTES
+    big = (64, 8, 65536, 512, 32, 1)
+    assert fl.flarepp_workspace_bytes(*big) > fl.FLAREPP_NOALLOC_SCRATCH_BYTES
+    vp = ctypes.c_void_p
+    B, H, N, M, D, dt = big
+    rc = L.flarepp_mix_noalloc(vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), B, H,
+                               ctypes.c_int64(N), M, D, dt, vp(0x70000000000), vp(0))
+    assert rc == fl.FLAREPP_SCRATCH_TOO_SMALL
+    assert "scratch" in fl.flarepp_strerror(rc)
+    # Validation comes first, as for flarepp_mix.
+    assert L.flarepp_mix_noalloc(vp(0), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), 1, 1,
+                                 ctypes.c_int64(64), 8, 16, 1, vp(0x7000000), vp(0)) == fl.FLAREPP_INVALID_ARGUMENT
+    assert L.flarepp_mix_noalloc(vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), vp(0x5000), vp(0x6000), 1, 1,
+                                 ctypes.c_int64(0), 8, 16, 1, vp(0x7000000), vp(0)) == fl.FLAREPP_OK
