@@ -203,7 +203,6 @@ hipError_t launch_merge(const MergeArgs& a, int dtype, int D, bool gate, int BH,
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int D, int nw, int grid_x, int grid_y,
                          hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int D, int Mp, int nw);
-size_t partial_lds_bytes(int dtype, int D, int plan, bool value_lo);
 
 // ---- Projections around the mixer (project.hip) ----------------------------------------------
 // Out = X W^T per 32-token tile; each wave keeps the weight rows of its 32-channel output group in

@@ -47,8 +47,54 @@
 namespace flarepp {
 namespace {
 
-// Synthesis seeds whose logit bound (log2 units) exceeds this go straight to the exact pass.
-constexpr float kFastBound = 90.0f;
+// A priori bounds on the logits (log2 units) of the zero-shift passes with fp16 score operands. The
+// fp16 rounding of a computed score operand (the synthesis keys c N0(s), the routing queries c Q)
+// moves a logit by at most 2^-11 of the bound, and the output's sensitivity to that error grows
+// with the keys' and seeds' scales, so larger bounds take the exact passes, whose logits are
+// exact up to fp32 accumulation. Synthesis: ||Qseed_m|| log2(e) (the keys have unit RMS); the
+// benchmark workloads reach about 12. Encode and decode: ||c Q_m|| ||K_n||; the workloads reach
+// about 14 (39 with the keys scaled by 4).
+constexpr float kFastBound = 24.0f;
+constexpr float kRouteBound = 20.0f;
+
+__device__ __forceinline__ float sumsq_bf16x8(bf16x8 x) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const bf16x2 p = {x[2 * i], x[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
+  }
+  return s;
+}
+// Maximum over the wave with DPP moves within each row of 16 lanes and reads of the four rows'
+// results: no lane-address registers (which the compiler would otherwise keep live across the
+// partial kernel's stage loop, between a reduction before it and one after it).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));   // lane ^ 1
+  v = fmaxf(v, dpp_move<0x4E>(v));   // lane ^ 2
+  v = fmaxf(v, dpp_move<0x141>(v));  // the other quad of 8 lanes
+  v = fmaxf(v, dpp_move<0x140>(v));  // the other half of 16 lanes
+  const auto rd = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  return fmaxf(fmaxf(rd(0), rd(16)), fmaxf(rd(32), rd(48)));
+}
+
+// The 16-bit operand of a P.V MFMA read as fp16 (the tile holds fp16 values); unused for fp32 tiles.
+template <typename OctT>
+__device__ __forceinline__ f16x8 as_f16x8(const OctT& o) {
+  if constexpr (sizeof(OctT) == sizeof(f16x8)) return __builtin_bit_cast(f16x8, o);
+  else return f16x8{};
+}
+
+__device__ __forceinline__ float sumsq_f16x8(f16x8 x) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const f16x2 p = {x[2 * i], x[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2(p, p, s, false);
+  }
+  return s;
+}
 
 // ------------------------------------------------------------------------------------------
 // Per-dtype operand helpers. A "slice" is the D/4 consecutive elements of a row that one lane
@@ -302,7 +348,21 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   T* ks = reinterpret_cast<T*>(smem);                   // [2][kStage][RS]
   T* vt = ks + 2 * kStage * RS;                          // [2][VE]
   T* vtl = vt + 2 * VE;                                  // HILO synthesis: value lo parts, [2][VE]
-  int* fail_s = reinterpret_cast<int*>(vt + (HILO && SYNTH ? 4 : 2) * VE);  // one flag
+  // bf16 synthesis on the 16x16x32 path: the key tile holds the raw synthesis keys s (exact bf16)
+  // and this array each token's factor c / rms(s), applied to the scores in fp32 (see store_set).
+  constexpr bool kFactorKeys = SYNTH && sizeof(T) == 2;
+  // bf16 synthesis (not the backward's HILO instance): the exact pass takes its probabilities and
+  // values N0(s) in fp16. Both fit its range there (P <= 1 under the running maximum,
+  // |N0(s)| <= sqrt(D)), and fp16 keeps 11 significant bits to bf16's 8: at large seed scales the
+  // routing queries, and through them the routing logits, inherit the synthesis call's rounding.
+  constexpr bool kF16Exact = SYNTH && sizeof(T) == 2 && !HILO;
+  float* tf = reinterpret_cast<float*>(vt + (HILO && SYNTH ? 4 : 2) * VE);  // [2][kStage]
+  int* fail_s = reinterpret_cast<int*>(tf + (kFactorKeys ? 2 * kStage : 0));  // one flag
+  // Encode's zero-shift pass (the routing bound of kRouteBound): each wave's largest ||c Q_m||^2, and
+  // per token row of a stage the largest ||K_n||^2 staged through it (kept in LDS, so no register
+  // stays live across the pass).
+  float* qred = reinterpret_cast<float*>(fail_s + 4);  // [NW]
+  float* knmax = qred + NW;                            // [kStage]
 
   // (chunk, latent group) of this workgroup.
   int chunk_id, lg;
@@ -326,6 +386,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   const int lat0 = (lg * NW + wave) * LPW;
   const bool active = lat0 < a.Mp;
   if (tid == 0) *fail_s = 0;
+  for (int t = tid; t < kStage; t += NT) knmax[t] = 0.f;
   __syncthreads();
 
   const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
@@ -371,6 +432,25 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
         }
       }
     }
+    if constexpr (!SYNTH) {
+      // The largest ||c Q_m||^2 of this wave's latents, for the routing bound of the zero-shift
+      // pass: each lane reads a whole fp16 row (no lane exchange, whose address registers the
+      // compiler would keep live across the stage loop).
+      float q2 = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) {
+        const int row = lat0 + 32 * nb + (lane & 31);
+        if (row < a.Mq) {
+          const f16x8* qr = reinterpret_cast<const f16x8*>(reinterpret_cast<const bf16*>(qbase) + (int64_t)row * QRS + 2 * D);
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < D / 8; k++) ss += sumsq_f16x8(qr[k]);
+          q2 = fmaxf(q2, ss);
+        }
+      }
+      q2 = wave_max_dpp(q2);
+      if (lane == 0) qred[wave] = q2;
+    }
   } else {
     load_queries();
   }
@@ -400,9 +480,11 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     }
   };
   // Store a register set into LDS buffer `buf`. F16 (bf16 runs of the wide zero-shift pass): the
-  // key tile holds fp16 keys.
-  auto store_set = [&](auto P, int buf, auto F16) {
+  // key tile holds fp16 keys. F16V (bf16 synthesis, exact pass): the value tile holds N0(s) in fp16.
+  // The encode's wide zero-shift pass also keeps the largest ||K_n||^2 per row (knmax).
+  auto store_set = [&](auto P, int buf, auto F16, auto F16V) {
     constexpr bool f16keys = decltype(F16)::value && sizeof(T) == 2;
+    constexpr bool f16vals = decltype(F16V)::value && sizeof(T) == 2;
     T* kdst = ks + buf * kStage * RS;
     T* vdst = vt + buf * VE;
 #pragma unroll
@@ -431,10 +513,23 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; j++) hk[j] = (f16)kx[j];
             *reinterpret_cast<f16x8*>(kdst + t * RS + part * CH) = hk;
+          } else if constexpr (kFactorKeys) {
+            // c N0(s) = (c / rms(s)) s: the raw keys are exact bf16 MFMA operands and the factor
+            // scales each token's scores in fp32. A bf16 copy of c N0(s) would carry a relative
+            // error of 2^-9 into logits that grow with the seeds' scale (Appendix A.3, Eq. 14).
+            *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kr[decltype(P)::value][i];
+            if (part == 0) tf[buf * kStage + t] = inv * c_scale;
           } else {
             *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = float_to_chunk<T>(kx);
           }
-          rowtile_store<T, D>(vdst, kStage, t, part * CH, float_to_chunk<T>(x));
+          if constexpr (f16vals) {
+            f16x8 hv;
+#pragma unroll
+            for (int j = 0; j < 8; j++) hv[j] = (f16)x[j];
+            rowtile_store<T, D>(vdst, kStage, t, part * CH, __builtin_bit_cast(Chunk, hv));
+          } else {
+            rowtile_store<T, D>(vdst, kStage, t, part * CH, float_to_chunk<T>(x));
+          }
           if constexpr (HILO) {
             float xl[CH];
 #pragma unroll
@@ -442,10 +537,14 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
             rowtile_store<T, D>(vtl + buf * VE, kStage, t, part * CH, float_to_chunk<T>(xl));
           }
         } else {
-          if constexpr (f16keys)
-            *reinterpret_cast<f16x8*>(kdst + t * RS + part * CH) =
-                to_f16x8(__builtin_bit_cast(bf16x8, kr[decltype(P)::value][i]));
-          else
+          if constexpr (f16keys) {
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, kr[decltype(P)::value][i]);
+            *reinterpret_cast<f16x8*>(kdst + t * RS + part * CH) = to_f16x8(kb);
+            // An LDS max without a returned value (non-negative floats order as their bits), so
+            // no register waits for it in this loop, where every register is in use.
+            const float k2 = group_sum<CPR>(sumsq_bf16x8(kb));
+            if (part == 0) atomicMax(reinterpret_cast<unsigned*>(knmax) + t, __float_as_uint(k2));
+          } else
             *reinterpret_cast<Chunk*>(kdst + t * RS + part * CH) = kr[decltype(P)::value][i];
           rowtile_store<T, D>(vdst, kStage, t, part * CH, vr[decltype(P)::value][i]);
         }
@@ -476,6 +575,18 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       __builtin_amdgcn_sched_barrier(kAllButMfma);
       keep_live(ka0);
       keep_live(ka1);
+      if constexpr (kFactorKeys) {
+        // Lane group g holds tokens 32 st + 8 g + i (s0v[.][i]) and + 4 + i (s1v[.][i]).
+        const f32x4* fp = reinterpret_cast<const f32x4*>(tf + buf * kStage + 32 * st + 8 * g);
+        const f32x4 f0 = fp[0], f1 = fp[1];
+#pragma unroll
+        for (int lb = 0; lb < NLB; lb++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            s0v[lb][i] *= f0[i];
+            s1v[lb][i] *= f1[i];
+          }
+      }
       // Tokens past the end of the chunk do not enter the softmax.
       if (32 * st + 32 > nvalid) {
 #pragma unroll
@@ -523,6 +634,29 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
             s0v[lb][i] = exp2_fast(s0v[lb][i]);
             s1v[lb][i] = exp2_fast(s1v[lb][i]);
           }
+      }
+      if constexpr (kF16Exact && exact) {
+        f16x8 vh[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; db++)
+          vh[db] = as_f16x8(O::load_oct_rows(vtt, VSTR, 32 * st, 16 * db, c, g));
+#pragma unroll
+        for (int lb = 0; lb < NLB; lb++) {
+          f16x8 ph;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            ph[i] = (f16)s0v[lb][i];
+            ph[4 + i] = (f16)s1v[lb][i];
+          }
+          typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+          const f16x2 one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+          for (int i = 0; i < 4; i++) lsum[lb] = __builtin_amdgcn_fdot2(f16x2{ph[2 * i], ph[2 * i + 1]}, one, lsum[lb], false);
+#pragma unroll
+          for (int db = 0; db < NDB; db++)
+            zacc[lb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vh[db], zacc[lb][db], 0, 0, 0);
+        }
+        continue;
       }
       Oct vb[NDB];
 #pragma unroll
@@ -696,11 +830,11 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
     load_set(I0{}, 0);
     if (nstage > 1) load_set(I1{}, 1);
-    store_set(I0{}, 0, std::true_type{});
+    store_set(I0{}, 0, std::true_type{}, std::false_type{});
     if (nstage > 2) load_set(I0{}, 2);
     __syncthreads();
     auto wstep = [&](auto P, int s) {
-      if (s + 1 < nstage) store_set(P, (s + 1) & 1, std::true_type{});
+      if (s + 1 < nstage) store_set(P, (s + 1) & 1, std::true_type{}, std::false_type{});
       if (s + 3 < nstage) load_set(P, s + 3);
       if (active) {
         const int64_t left = n_end - (n_begin + (int64_t)s * kStage);
@@ -720,7 +854,8 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   // Stage s: store stage s+1 (register set P = (s+1) % 2) into its buffer, refill set P with stage
   // s+3, compute stage s, barrier.
   auto step = [&](auto P, auto EXACT, int s) {
-    if (s + 1 < nstage) store_set(P, (s + 1) & 1, std::false_type{});
+    if (s + 1 < nstage)
+      store_set(P, (s + 1) & 1, std::false_type{}, std::integral_constant<bool, decltype(EXACT)::value && kF16Exact>{});
     if (s + 3 < nstage) load_set(P, s + 3);
     if (active) {
       const int64_t left = n_end - (n_begin + (int64_t)s * kStage);
@@ -739,7 +874,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
     }
     load_set(I0{}, 0);
     if (nstage > 1) load_set(I1{}, 1);
-    store_set(I0{}, 0, std::false_type{});
+    store_set(I0{}, 0, std::false_type{}, std::integral_constant<bool, decltype(EXACT)::value && kF16Exact>{});
     if (nstage > 2) load_set(I0{}, 2);
     __syncthreads();
     for (int s = 0; s < nstage; s += 2) {
@@ -803,7 +938,17 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       }
       if (!__all(ok) && lane == 0) atomicOr(fail_s, 1);
       __syncthreads();
-      if (*fail_s == 0) {
+      // Routing bound (kRouteBound) over every latent and token of the chunk: beyond it the chunk
+      // takes the exact pass, whose logits use the hi/lo query pair.
+      bool in_bound = true;
+      if constexpr (!SYNTH) {
+        float qm = 0.f, km = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) qm = fmaxf(qm, qred[w]);
+        for (int t = lane; t < kStage; t += 64) km = fmaxf(km, knmax[t]);
+        in_bound = qm * wave_max_dpp(km) <= kRouteBound * kRouteBound;
+      }
+      if (*fail_s == 0 && in_bound) {
         if (!active) return;
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
@@ -1208,14 +1353,24 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
   const bf16* qsrc = reinterpret_cast<const bf16*>(a.Q) + (int64_t)bh * Mp * kQRow<bf16> * D;
   const bf16* zsrc = reinterpret_cast<const bf16*>(a.Z) + (int64_t)bh * Mp * D;
 
+  // Stage the queries and Z; keep the largest ||c Q_m||^2 (a row's four chunks sit in four
+  // consecutive lanes) for the routing bound of the zero-shift pass.
+  float q2 = 0.f;
   for (int q = tid; q < Mp * 4; q += NT) {
     const int row = q >> 2, part = q & 3;
-    *reinterpret_cast<Chunk*>(qh + row * QHS + part * 8) =
-        *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<bf16> * D + 2 * D + part * 8);
+    const Chunk qc = *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<bf16> * D + 2 * D + part * 8);
+    *reinterpret_cast<Chunk*>(qh + row * QHS + part * 8) = qc;
+    q2 = fmaxf(q2, group_sum<4>(sumsq_f16x8(__builtin_bit_cast(f16x8, qc))));
     rowtile_store<bf16, D>(zs, Mp, row, part * 8, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * 8));
   }
   for (int q = tid; q < 32 * 4; q += NT) *reinterpret_cast<Chunk*>(qh + (Mp + (q >> 2)) * QHS + (q & 3) * 8) = Chunk{0u, 0u, 0u, 0u};
+  float* qred = reinterpret_cast<float*>(zs + ZT::elems(Mp));  // [NW]
+  q2 = wave_max_dpp(q2);
+  if (lane == 0) qred[wave] = q2;
   __syncthreads();
+  float qmax2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; w++) qmax2 = fmaxf(qmax2, qred[w]);
 
   const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
   const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
@@ -1242,11 +1397,15 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
   for (int64_t base = t_begin + (int64_t)wave * TG; base < t_end; base += gstride) {
     auto load_keys = [&](int tb, int kh) __attribute__((always_inline)) { return load_keys_at(base, tb, kh); };
     f16x8 kf[TB][2];
+    // ||K_n||^2 of this lane's tokens (lanes l and l ^ 32 hold the two halves of a key).
+    float k2[TB];
     if constexpr (PREF) {
 #pragma unroll
-      for (int tb = 0; tb < TB; tb++)
+      for (int tb = 0; tb < TB; tb++) {
+        k2[tb] = sumsq_bf16x8(knext[tb][0]) + sumsq_bf16x8(knext[tb][1]);
 #pragma unroll
         for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(knext[tb][kh]);
+      }
       if (base + gstride < t_end) {
 #pragma unroll
         for (int tb = 0; tb < TB; tb++)
@@ -1255,9 +1414,12 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
       }
     } else {
 #pragma unroll
-      for (int tb = 0; tb < TB; tb++)
-#pragma unroll
-        for (int kh = 0; kh < 2; kh++) kf[tb][kh] = to_f16x8(load_keys_at(base, tb, kh));
+      for (int tb = 0; tb < TB; tb++) {
+        const bf16x8 k0 = load_keys_at(base, tb, 0), k1 = load_keys_at(base, tb, 1);
+        k2[tb] = sumsq_bf16x8(k0) + sumsq_bf16x8(k1);
+        kf[tb][0] = to_f16x8(k0);
+        kf[tb][1] = to_f16x8(k1);
+      }
     }
 
     f32x16 yacc[TB];
@@ -1443,6 +1605,10 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
 
     clear();
     bool ok = a.force_exact == 0;
+    // Routing bound (kRouteBound): a group holding a token beyond it takes the exact pass at once.
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++) ok = ok && qmax2 * (k2[tb] + shfl_xor(k2[tb], 32)) <= kRouteBound * kRouteBound;
+    ok = __all(ok);
     if (ok) {
       if constexpr (TB == 1)
         accumulate_fast_pipelined();
@@ -1513,15 +1679,19 @@ static hipError_t allow_lds(F* fn, size_t lds) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <typename T, int D, int STG, bool VLO>
+// LDS of the partial kernel: key tiles, value tiles (VLO: and their lo parts), the per-token key
+// factors of bf16 synthesis (FK), one flag (in 16 bytes), a per-wave maximum (up to 16 waves) and a
+// per-row maximum of a stage.
+template <typename T, int D, int STG, bool VLO, bool FK>
 static size_t partial_lds_t() {
   constexpr int CH = 16 / sizeof(T);
-  return (size_t)(2 * STG * (D + CH) + (VLO ? 4 : 2) * RowTile<T, D>::elems(STG)) * sizeof(T) + 16;
+  return (size_t)(2 * STG * (D + CH) + (VLO ? 4 : 2) * RowTile<T, D>::elems(STG)) * sizeof(T) +
+         (FK ? 2 * STG * sizeof(float) : 0) + 16 + (16 + STG) * sizeof(float);
 }
 
 template <typename T, int D, int LPW, int NW, bool SYNTH, int STG, bool HILO>
 static hipError_t launch_partial_t(const PartialArgs& a, int grid_x, int grid_y, hipStream_t st) {
-  const size_t lds = partial_lds_t<T, D, STG, HILO && SYNTH>();
+  const size_t lds = partial_lds_t<T, D, STG, HILO && SYNTH, SYNTH && sizeof(T) == 2>();
   hipError_t e = allow_lds(partial_kernel<T, D, LPW, NW, SYNTH, STG, HILO>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((partial_kernel<T, D, LPW, NW, SYNTH, STG, HILO>), dim3(grid_x, grid_y), dim3(NW * 64), lds, st, a);
@@ -1621,7 +1791,9 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int nw, int gx, int gy, h
 }
 
 static size_t decode_wide_lds(int Mp) {
-  return (size_t)(Mp + 32) * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16);
+  // fp16 query rows (and a zero block), the Z tile, and one float per wave (up to 16).
+  return (size_t)(Mp + 32) * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16) +
+         16 * sizeof(float);
 }
 
 template <int NW, int TB, bool PREF = true>
@@ -1654,18 +1826,5 @@ size_t decode_lds_bytes(int dtype, int D, int Mp, int nw) {
   return D == 32 ? decode_lds_t<float, 32>(Mp, nw) : decode_lds_t<float, 16>(Mp, nw);
 }
 
-size_t partial_lds_bytes(int dtype, int D, int plan, bool value_lo) {
-  const bool big = plan == 3;
-  if (dtype == 1) {
-    if (value_lo) {
-      if (D == 32) return big ? partial_lds_t<bf16, 32, 256, true>() : partial_lds_t<bf16, 32, 128, true>();
-      return big ? partial_lds_t<bf16, 16, 256, true>() : partial_lds_t<bf16, 16, 128, true>();
-    }
-    if (D == 32) return big ? partial_lds_t<bf16, 32, 256, false>() : partial_lds_t<bf16, 32, 128, false>();
-    return big ? partial_lds_t<bf16, 16, 256, false>() : partial_lds_t<bf16, 16, 128, false>();
-  }
-  if (D == 32) return big ? partial_lds_t<float, 32, 256, false>() : partial_lds_t<float, 32, 128, false>();
-  return big ? partial_lds_t<float, 16, 256, false>() : partial_lds_t<float, 16, 128, false>();
-}
 
 }  // namespace flarepp

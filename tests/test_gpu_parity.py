@@ -150,6 +150,53 @@ def test_wide_logits_take_the_exact_path():
     _check(w, label="wide logits")
 
 
+# Seed and key scales: the seeds' learned scale sets the temperature of the synthesis logits
+# (Appendix A.3, Eq. 14) and the routing keys' scale that of the routing logits (Appendix A.4), so
+# logits of several tens (log2 units) are ordinary operating points. The grid covers the zero-shift
+# window and, with the exact path forced, the running-maximum passes. The latent stages Qd, Q, Z
+# (fp32 exports) keep the plain bar. In bf16 the outputs become one-hot picks of single latent rows
+# as the scales grow, up to 15 times RMS(Y), and storing Y and Z in bf16 alone then costs more than
+# 2% of RMS (tests/test_oracle.py::test_bf16_storage_of_heavy_tailed_outputs_exceeds_the_plain_bar),
+# so Y takes the plain bar plus that storage rounding, 2^-8 |Y_ref| per element.
+SCALE_GRID = [(1, 1), (2, 1), (3, 1), (4, 1), (5, 1), (6, 1), (1, 2), (1, 4), (1, 8), (1, 12), (3, 6), (4, 9),
+              (6, 12)]
+
+
+def _scaled(w, seeds, keys):
+    from workloads.gen import _store
+    w.Qseed = _store(w.f64("Qseed") * seeds, w.dtype)
+    w.K = _store(w.f64("K") * keys, w.dtype)
+    return w
+
+
+@pytest.mark.parametrize("exact", [False, True], ids=["default", "exact"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("seeds,keys", SCALE_GRID)
+def test_seed_and_key_scale_sweep(seeds, keys, dtype, exact):
+    import rank_latent_routing_amd as fl
+    w = _scaled(make_workload(3, B=1, H=2, N=3000, M=64, dtype=dtype, seed=41 + 7 * seeds + keys), seeds, keys)
+    prev = fl.flarepp_debug_force_exact(exact)
+    try:
+        _check(w, label=f"seeds x{seeds} keys x{keys} {dtype} {'exact' if exact else 'default'}",
+               bf16_storage=(dtype == "bf16"))
+    finally:
+        fl.flarepp_debug_force_exact(prev)
+
+
+@pytest.mark.parametrize("exact", [False, True], ids=["default", "exact"])
+@pytest.mark.parametrize("seeds,keys", [(4, 1), (6, 1), (1, 8), (6, 12)])
+def test_seed_and_key_scales_d16(seeds, keys, exact):
+    # bf16 with D = 16 runs both passes on the 16x16x32 path (raw synthesis keys with a per-token
+    # factor on the zero-shift pass too).
+    import rank_latent_routing_amd as fl
+    w = _scaled(make_workload(2, B=1, H=2, N=3000, M=48, seed=17 * seeds + keys), seeds, keys)
+    prev = fl.flarepp_debug_force_exact(exact)
+    try:
+        _check(w, label=f"D=16 seeds x{seeds} keys x{keys} {'exact' if exact else 'default'}", bf16_storage=True)
+    finally:
+        fl.flarepp_debug_force_exact(prev)
+
+
 @pytest.mark.parametrize("dtype,big", [("fp32", 36.0), ("bf16", 40.0)])
 def test_zero_shift_and_exact_chunks_mixed(dtype, big):
     # Large keys in two token ranges: the chunks and decode token groups that hold them fall back

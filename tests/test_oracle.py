@@ -369,3 +369,23 @@ def test_planted_mistake_is_caught(monkeypatch, target, mutant):
     assert _all_pins_pass()
     monkeypatch.setattr(orc, target, mutant)
     assert not _all_pins_pass()
+
+
+def test_bf16_storage_of_heavy_tailed_outputs_exceeds_the_plain_bar():
+    # The bar of the bf16 parity tests at large key scales, derived: with the routing keys scaled x2
+    # (Gaussian inputs, M = 64; the sweep's seeds x1, keys x2 case, head 1) the decode rows become
+    # near one-hot picks of single latent rows and max|Y| reaches 15 RMS(Y). Rounding the oracle's
+    # own exact Y to bf16 (the output dtype) then moves it by more than the plain bar of 2e-2 RMS(Y),
+    # so no bf16-output implementation can meet that bar there. Round to nearest moves each element
+    # by at most the unit roundoff of bf16's 8-bit significand, 2^-8 |Y|, which is the per-element
+    # allowance the tests add for such outputs.
+    from workloads.gen import _store, to_float64
+    w = make_workload(3, B=1, H=2, N=3000, M=64, dtype="bf16", seed=50)
+    K = to_float64(_store(w.f64("K")[0, 1] * 2.0, "bf16"), "bf16")
+    r = orc.mix_head(K, w.f64("V")[0, 1], w.f64("S")[0, 1], w.f64("Qseed")[1], w.f64("Qf")[1], float(w.g[1]))
+    Y = r["Y"]
+    rms = np.sqrt(np.mean(Y * Y))
+    Yb = to_float64(_store(Y, "bf16"), "bf16")
+    assert np.abs(Y).max() > 10 * rms
+    assert np.abs(Yb - Y).max() > 3e-2 * rms
+    assert (np.abs(Yb - Y) <= 2.0 ** -8 * np.abs(Y) * (1 + 1e-12)).all()
