@@ -271,6 +271,23 @@ def test_bwd_zero_shift_and_running_maximum_mixed(dtype, big):
     _check(w, label=f"bwd mixed {dtype}", bar=bar)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("scale", [8.0, 24.0])
+def test_bwd_saturated_softmaxes(dtype, scale):
+    # Keys scaled on every token (Appendix B.5, Eq. 46-49 in the saturated regime): at x24 the
+    # routing logits reach about 200 (log2 units), every softmax row is nearly one-hot, and each
+    # score cotangent P (dP - c) is a difference of nearly equal terms. The bf16 bars hold as they
+    # stand; fp32 adds the logits' accumulation error, as in the mixed case above.
+    w = make_workload(3, B=1, H=2, N=3000, M=64, dtype=dtype, seed=11)
+    from workloads.gen import _store
+    w.K = _store(w.f64("K") * scale, dtype)
+    bar = None
+    if dtype == "fp32":
+        big_sum = max(float(_routing_logits(w, 0, h)[1].max()) for h in range(w.H))
+        bar = 1e-5 + np.log(2.0) * 2.0 ** -24 * np.sqrt(w.D) * big_sum
+    _check(w, label=f"bwd saturated x{scale:g} {dtype}", bar=bar)
+
+
 # ---- seeded random shapes (D, M, N, B, H and dtype drawn together) ------------------------------
 def _random_cases(n, seed):
     rng = np.random.default_rng(seed)
