@@ -244,38 +244,59 @@ def test_empty_problem():
 # ---------------------------------------------------------------- full sizes, sampled
 
 def _full(cfg, heads, ntok=None, **kw):
+    """The workload at its full size in the launch configuration the benchmark times, checked on the
+    (b, h) slices `heads` ("all": every slice; the oracle runs them on a pool of host threads)."""
     w = make_workload(cfg, **kw)
     say(f"[full] {w.name}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D}")
     Y = run_gpu(w, debug=False)
     assert np.isfinite(Y).all()
+    if heads == "all":
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     rng = np.random.default_rng(cfg)
-    for b, h in heads:
-        ref = oracle_head(w, b, h, block=65536)
-        if ntok is None:
-            e = slice_err(Y[b, h], ref["Y"], w.dtype)
-        else:
-            idx = rng.choice(w.N, size=ntok, replace=False)
-            e = np.abs(Y[b, h][idx] - ref["Y"][idx]).max() / np.sqrt(np.mean(ref["Y"] ** 2))
-        say(f"[full] {w.name} (b={b}, h={h}) err {e:.3g}")
-        assert e <= tol(w.dtype)
+    picks = {bh: (None if ntok is None else rng.choice(w.N, size=ntok, replace=False)) for bh in heads}
+
+    def err(bh):
+        # (plain metric, bf16: the same beyond the storage rounding 2^-8 |Y_ref| of each element)
+        b, h = bh
+        ref = oracle_head(w, b, h, block=65536)["Y"]
+        idx = picks[bh]
+        got, want = (Y[b, h], ref) if idx is None else (Y[b, h][idx], ref[idx])
+        if w.dtype == "fp32":
+            e = slice_err(got, want, w.dtype)
+            return e, e
+        rms = np.sqrt(np.mean(ref ** 2))
+        d = np.abs(got - want)
+        return d.max() / rms, max(float((d - 2.0 ** -8 * np.abs(want)).max()), 0.0) / rms
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        errs = dict(zip(heads, pool.map(err, heads)))
+    worst = max(errs, key=lambda k: errs[k][0])
+    plain_ok = sum(e[0] <= tol(w.dtype) for e in errs.values())
+    say(f"[full] {w.name}: {len(errs)} slices, worst {errs[worst][0]:.3g} at (b, h) = {worst} "
+        f"({errs[worst][1]:.3g} beyond storage); {plain_ok} of {len(errs)} within the plain bar")
+    # bf16 outputs are held to the plain bar beyond their storage rounding: in heavy-tailed slices
+    # (max|Y| several times RMS(Y)) rounding Y to bf16 alone moves an element by up to 2^-8 |Y|.
+    for bh, e in errs.items():
+        assert e[1] <= tol(w.dtype), (bh, e)
     return w, Y
 
 
 def test_full_cfg2():
-    _full(2, [(0, 0), (1, 5), (3, 7)])
+    _full(2, "all")
 
 
 def test_full_cfg3():
-    _full(3, [(0, 0), (17, 3), (31, 7)])
+    _full(3, "all")
 
 
 def test_full_cfg4_and_peaked():
-    _full(4, [(0, 1), (1, 6)])
-    _full(4, [(1, 2)], peaked=True)
+    _full(4, "all")
+    _full(4, [(0, 0), (1, 2), (1, 7)], peaked=True)
 
 
-def test_full_cfg5_one_head():
-    _full(5, [(0, 3)])
+def test_full_cfg5_two_heads():
+    _full(5, [(0, 3), (0, 6)])
 
 
 def test_full_cfg5_constant_values_pass_through():
