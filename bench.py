@@ -38,8 +38,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-# Measured v_exp_f32 issue rate on gfx950: 32 per clock per CU (quarter of the fp32 FMA rate).
-PEAK_EXP_PER_S = 256 * 2.4e9 * 32
+# v_exp_f32 rate of the whole chip, measured by the exp microbenchmark (bench.py --microbench, summary
+# in profiles/roofline_microbenchmarks.md): 1.46e13 exponentials per second, 4.49 ns per wave
+# instruction on a SIMD.
+PEAK_EXP_PER_S = 1.46e13
 
 KERNELS = ["synthesis_partial", "merge_gate", "encode_partial", "merge", "decode"]
 # Backward kernels (flarepp_mix_backward) and the recomputed forward kernels it launches.
@@ -98,6 +100,23 @@ def profiled_traffic(kernel, profile=PROFILE, key="forward_sources_sha256", srcs
     return None if k is None else float(k)
 
 
+def profiled_kernel_us(kernel, profile=PROFILE, key="forward_sources_sha256", srcs=None):
+    """Average dispatch duration (us) of `kernel` in a committed rocprofv3 kernel trace, or None when
+    the summary is missing or was taken on a different kernel source."""
+    try:
+        lines = open(profile).read().splitlines()
+    except OSError:
+        return None
+    rec = None
+    for ln in lines:
+        if ln.startswith("traffic-json: "):
+            rec = json.loads(ln[len("traffic-json: "):])
+    if not rec or rec.get(key) != kernel_source_hash(srcs):
+        return None
+    v = rec.get("kernel_avg_us", {}).get(kernel)
+    return None if v is None else float(v)
+
+
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,7 +124,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-heads", type=int, default=2)
+    ap.add_argument("--cpu-sample-heads", type=int, default=8,
+                    help="(b, h) slices of the workload the CPU baseline runs (default 8: all of the 1M-token one)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-variants", action="store_true", help="skip plain FLARE and simplified FLARE++")
     ap.add_argument("--no-block", action="store_true", help="skip the block (projections + mixer + output projection)")
@@ -146,29 +166,49 @@ def kernel_bytes(name, w):
 
 
 def cpu_baseline(w, heads):
-    """The float64 oracle on the first `heads` heads (b = 0) of the same workload, all N tokens."""
+    """The float64 oracle, as it stands, on the first `heads` (b, h) slices of the same workload (all N
+    tokens each), one slice per worker thread over the host's cores: numpy releases the interpreter
+    lock in its BLAS products and elementwise exponentials, and the BLAS threads are divided among
+    the workers so that the threads in use match the cores."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     from workloads import to_float64
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    heads = max(1, min(heads, w.H))
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    slices = [(b, h) for b in range(w.B) for h in range(w.H)][:max(1, heads)]
+    workers = min(len(slices), cores)
+    blas = max(1, cores // workers)
+
+    def run(bh):
+        b, h = bh
+        oracle.mix_head(to_float64(w.K[b, h], w.dtype), to_float64(w.V[b, h], w.dtype),
+                        to_float64(w.S[b, h], w.dtype), to_float64(w.Qseed[h], w.dtype),
+                        to_float64(w.Qf[h], w.dtype), float(w.g[h]), block=65536)
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=blas)
+    except Exception:  # noqa: BLE001
+        limit, blas = None, 1
     t0 = time.perf_counter()
-    for h in range(heads):
-        oracle.mix_head(to_float64(w.K[0, h], w.dtype), to_float64(w.V[0, h], w.dtype), to_float64(w.S[0, h], w.dtype),
-                        to_float64(w.Qseed[h], w.dtype), to_float64(w.Qf[h], w.dtype), float(w.g[h]), block=65536)
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(run, slices))
     dt = time.perf_counter() - t0
+    if limit is not None:
+        limit.restore_original_limits()
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": heads * w.N / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} (b, h) slices (b=0, h<{heads}), all {w.N} tokens, M={w.M}, D={w.D}, "
-                      f"float64 numpy oracle; {dt:.2f} s; BLAS threads {threads}, elementwise exp single-threaded",
+    return {"value": len(slices) * w.N / dt, "unit": "tokens*heads/s", "cores": workers * blas, "kind": "oracle",
+            "sample": f"{len(slices)} of {w.B * w.H} (b, h) slices, all {w.N} tokens each, M={w.M}, D={w.D}, "
+                      f"float64 numpy oracle; {dt:.2f} s wall; {workers} worker threads (one slice each) x "
+                      f"{blas} BLAS threads",
             "host_logical_cpus": os.cpu_count(), "cpu_model": model}
 
 
@@ -539,8 +579,14 @@ def main():
     dom_ms = kern[dom]["ms_avg"]
     achieved = kernel_flops(dom, w) / (dom_ms * 1e-3) * 1e-12
     traffic = profiled_traffic(dom) if args.config == 5 else None
+    # The same kernel's average duration in the committed kernel trace (same sources), for a fraction
+    # that can be recomputed from the profile alone.
+    prof_us = profiled_kernel_us(dom) if args.config == 5 else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
+                "profile_kernel_us": prof_us,
+                "frac_profile": (round(kernel_flops(dom, w) / (prof_us * 1e-6) * 1e-12 / peak, 4)
+                                 if prof_us else None),
                 "kernel_ms": round(dom_ms, 4), "flops_per_launch": kernel_flops(dom, w),
                 "algorithmic_bytes_per_launch": kernel_bytes(dom, w),
                 "hbm_gbs": round(kernel_bytes(dom, w) / (dom_ms * 1e-3) * 1e-9, 1),
