@@ -57,6 +57,10 @@ BWD_FLOPS_PER_NMD = {"synthesis_partial": 4, "encode_partial": 4, "bwd_token_dec
 # The forward kernels' sources, in the order their bytes enter the profile's fingerprint.
 KERNEL_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n in ("kernels.hip", "device.h")]
 PROFILE = os.path.join(ROOT, "profiles", "flarepp_mixer_1M_tokens.md")
+# The backward kernels' sources (with the forward's, whose hi/lo instance the recompute runs) and the
+# backward's kernel-trace summary.
+BWD_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n in ("backward.hip", "kernels.hip", "device.h")]
+BWD_PROFILE = os.path.join(ROOT, "profiles", "flarepp_mixer_backward_1M_tokens.md")
 # The projection kernel's sources and the block's counter summary.
 PROJECT_SRCS = [os.path.join(ROOT, "rank_latent_routing_amd", "csrc", n) for n in ("project.hip", "device.h")]
 BLOCK_PROFILE = os.path.join(ROOT, "profiles", "flarepp_block_1M_tokens.md")
@@ -392,7 +396,9 @@ def shard(args, w, dev, dt_code, ranks=8):
 
 def backward(args, w, dev, dt_code, peak):
     """The mixer's backward pass (flarepp_mix_backward, forward recomputed inside) on the same inputs
-    with a seeded cotangent dY, timed like the forward in a region of its own."""
+    with a seeded cotangent dY, timed like the forward in a region of its own; then a training step's
+    two calls, flarepp_mix_forward_saved and flarepp_mix_backward_saved (no recompute), each timed on
+    its own ("saved")."""
     import numpy as np
     import torch
 
@@ -415,12 +421,28 @@ def backward(args, w, dev, dt_code, peak):
     dom = max(kern, key=kern.get)
     dom_flops = BWD_FLOPS_PER_NMD.get(dom, 0) * nmd
     achieved = dom_flops / (kern[dom] * 1e-3) * 1e-12
+    prof_us = profiled_kernel_us(dom, BWD_PROFILE, "backward_sources_sha256", BWD_SRCS) if args.config == 5 else None
+    # A training step's two calls: the forward that keeps the backward's starting state, then the
+    # backward from it (no recompute).
+    out = torch.empty_like(dev["K"])
+    ws_saved = torch.empty_like(ws)
+    fwd_saved = lambda: fl.flarepp_mix_forward_saved(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"],
+                                                     workspace=ws_saved, out=out)
+    bwd_saved = lambda: fl.flarepp_mix_backward_saved(dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"],
+                                                      dev["g"], dY, workspace=ws_saved, grads=grads)
+    ms_fs = _time_steps(args, fwd_saved)
+    ms_bs = _time_steps(args, bwd_saved)
+    saved_kern = _kernel_times(args.steps, bwd_saved)
     return {"ms_per_step": ms, "value": w.B * w.H * w.N / (ms * 1e-3), "unit": "tokens*heads/s",
             "algorithmic_tflops": sum(BWD_FLOPS_PER_NMD.values()) * nmd / (ms * 1e-3) * 1e-12,
             "kernels": {k: round(v, 4) for k, v in kern.items()},
             "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "kernel_ms": round(kern[dom], 4),
-                         "flops_per_launch": dom_flops}}
+                         "flops_per_launch": dom_flops, "profile_kernel_us": prof_us,
+                         "frac_profile": (round(dom_flops / (prof_us * 1e-6) * 1e-12 / peak, 4) if prof_us else None)},
+            "saved": {"forward_ms": ms_fs, "backward_ms": ms_bs, "training_step_ms": ms_fs + ms_bs,
+                      "backward_value": w.B * w.H * w.N / (ms_bs * 1e-3),
+                      "kernels": {k: round(v, 4) for k, v in saved_kern.items() if v > 0}}}
 
 
 BLOCK_KERNELS = ["block_params", "project", "synthesis_partial", "merge_gate", "encode_partial", "merge", "decode",

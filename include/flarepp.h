@@ -192,6 +192,32 @@ int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const v
                             hipStream_t stream);
 
 /*
+ * The same backward in two calls, the way a training step runs it (the pages' backward takes the
+ * log-normalizers and outputs its forward kept, Appendix B.3 and B.5):
+ *
+ * flarepp_mix_forward_saved runs the mixer forward and keeps, in the caller's workspace, the state
+ * the backward starts from: both token-axis calls computed with hi/lo query logits and hi/lo P.V
+ * products (as the backward's own recompute computes them), the routing-query rows, Z and Qd in
+ * fp32, and the synthesis and encode calls' per-latent log2 normalizers. It writes `out` like
+ * flarepp_mix (the same bars; its latent stages carry more bits). The workspace is at least
+ * flarepp_backward_workspace_bytes(B, H, N, M, D, dtype) bytes, 256-byte aligned.
+ *
+ * flarepp_mix_backward_saved then writes the cotangents as flarepp_mix_backward_ws does, bit for
+ * bit, without recomputing that state: the workspace must hold what flarepp_mix_forward_saved left
+ * for the same inputs and sizes, untouched since (the library cannot check this; other contents
+ * give wrong cotangents, not a fault). It only reads that state, so several cotangents dY can follow
+ * one forward_saved. Both calls only enqueue kernels (no allocation) and may be captured in a HIP
+ * graph. Arguments, support and errors as for flarepp_mix and flarepp_mix_backward_ws.
+ */
+int flarepp_mix_forward_saved(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                              const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+int flarepp_mix_backward_saved(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                               const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype,
+                               void* dK, void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The block around the mixer: the feature projections in front of it, the per-head normalizations
  * and the output projection (Section 3.2: the synthesis keys of Eq. 5, the routing keys and values
  * before Eq. 8, the seeds and the gate of Eq. 6-7; Appendix C.2 for which tensors carry the learned-

@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.flarepp_mix_backward.restype = i32
     L.flarepp_mix_backward_ws.argtypes = bwd_args + [vp, sz, vp]
     L.flarepp_mix_backward_ws.restype = i32
+    L.flarepp_mix_forward_saved.argtypes = mix_args + [vp, sz, vp]
+    L.flarepp_mix_forward_saved.restype = i32
+    L.flarepp_mix_backward_saved.argtypes = bwd_args + [vp, sz, vp]
+    L.flarepp_mix_backward_saved.restype = i32
     L.flarepp_backward_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.flarepp_backward_workspace_bytes.restype = sz
     L.flarepp_project.argtypes = [vp] * 8 + [i32, i32, i64, i32, i32, vp, vp, vp, vp]
@@ -314,7 +318,7 @@ def flarepp_backward_workspace_bytes(B: int, H: int, N: int, M: int, D: int, dty
     return int(lib().flarepp_backward_workspace_bytes(B, H, N, M, D, dtype))
 
 
-def flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=None, workspace=None, stream=None):
+def flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=None, workspace=None, stream=None, _saved=False):
     """Backward pass of flarepp_mix given the output cotangent dY [B, H, N, D] (the input dtype).
     Returns {dK, dV, dS: [B, H, N, D], dQseed, dQf: [H, M, D] in the input dtype, dg: [H] float32};
     `grads` may supply those tensors. With `workspace` (a uint8 tensor of
@@ -339,13 +343,44 @@ def flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=None, workspace=None, 
                  "dQseed": torch.empty_like(Qseed), "dQf": torch.empty_like(Qf), "dg": torch.empty_like(g)}
     outs = [_ptr(grads[k]) for k in ("dK", "dV", "dS", "dQseed", "dQf", "dg")]
     args = [_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), _ptr(dY), B, H, N, M, D, dt] + outs
-    if workspace is None:
+    if _saved:
+        if workspace is None:
+            raise ValueError("flarepp_mix_backward_saved needs the workspace of flarepp_mix_forward_saved")
+        st = lib().flarepp_mix_backward_saved(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream, K.device))
+        _check(st, "flarepp_mix_backward_saved")
+    elif workspace is None:
         st = lib().flarepp_mix_backward(*args, _stream_ptr(stream, K.device))
         _check(st, "flarepp_mix_backward")
     else:
         st = lib().flarepp_mix_backward_ws(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream, K.device))
         _check(st, "flarepp_mix_backward_ws")
     return grads
+
+
+def flarepp_mix_forward_saved(K, V, S, Qseed, Qf, g, workspace, out=None, stream=None):
+    """The mixer forward of a training step: writes out [B, H, N, D] and keeps in `workspace` (a uint8
+    tensor of at least flarepp_backward_workspace_bytes bytes, kept by the caller) the state
+    flarepp_mix_backward_saved starts from. Returns out."""
+    import torch
+    B, H, N, M, D = _shapes(K, V, S, Qseed, Qf, g)
+    if out is not None:
+        _require_like("out", out, K.shape, K.dtype)
+    _require_device(K, V=V, S=S, Qseed=Qseed, Qf=Qf, g=g, out=out)
+    _require_workspace(workspace, K.device)
+    if out is None:
+        out = torch.empty_like(K)
+    st = lib().flarepp_mix_forward_saved(_ptr(K), _ptr(V), _ptr(S), _ptr(Qseed), _ptr(Qf), _ptr(g), B, H, N, M, D,
+                                         _dtype_code(K), _ptr(out), _ptr(workspace), workspace.numel(),
+                                         _stream_ptr(stream, K.device))
+    _check(st, "flarepp_mix_forward_saved")
+    return out
+
+
+def flarepp_mix_backward_saved(K, V, S, Qseed, Qf, g, dY, workspace, grads=None, stream=None):
+    """flarepp_mix_backward from the state flarepp_mix_forward_saved left in `workspace` for the same
+    inputs (no recompute). Returns the cotangents as flarepp_mix_backward does."""
+    return flarepp_mix_backward(K, V, S, Qseed, Qf, g, dY, grads=grads, workspace=workspace, stream=stream,
+                                _saved=True)
 
 
 def flarepp_mix_simplified(K, V, Sk, Sv, Qseed, out=None, workspace=None, stream=None):
@@ -513,6 +548,7 @@ def flarepp_timing_read() -> dict:
 
 __all__ = ["FlareppError", "flarepp_mix", "flarepp_mix_ws", "flarepp_mix_noalloc", "FLAREPP_NOALLOC_SCRATCH_BYTES", "flarepp_mix_debug", "flarepp_workspace_bytes",
            "flarepp_flare", "flarepp_mix_simplified", "flarepp_mix_backward", "flarepp_backward_workspace_bytes",
+           "flarepp_mix_forward_saved", "flarepp_mix_backward_saved",
            "flarepp_project", "flarepp_out_project", "flarepp_block", "flarepp_block_workspace_bytes",
            "flarepp_debug_force_exact", "flarepp_timing_enable", "flarepp_timing_read", "flarepp_kernel_name", "flarepp_strerror",
            "flarepp_version", "lib", "FLAREPP_FP32", "FLAREPP_BF16"]

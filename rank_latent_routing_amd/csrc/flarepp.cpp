@@ -538,21 +538,36 @@ int validate_bwd_sizes(int B, int H, int64_t N, int M, int D, int dtype, bool* e
   return FLAREPP_OK;
 }
 
-int enqueue_backward(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
-                     const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype, void* dK,
-                     void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* ws, const BwdPlan& p,
-                     hipStream_t st) {
+// The forward state the backward starts from (Appendix B.3 and B.5: the forward keeps each routing
+// call's log-normalizer and output): the synthesis and encode partials with hi/lo query logits and
+// hi/lo P.V products, merged into the routing-query rows, Z and Qd in fp32 and both calls'
+// per-latent log2 normalizers, all in the backward workspace. With `out` the decode runs too and
+// writes the mixer's output.
+int enqueue_saved_forward(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                          const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out, void* ws,
+                          const BwdPlan& p, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  Saved sv;
+  sv.lsyn = F(p.off_lsyn);
+  sv.lenc = F(p.off_lenc);
+  sv.hilo = true;
+  sv.no_decode = out == nullptr;
+  return enqueue(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, F(p.off_qd), nullptr, F(p.off_z32), ws, p.f, st,
+                 sv);
+}
+
+// The backward proper, from the state enqueue_saved_forward left in the workspace.
+int enqueue_backward_from_saved(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                                const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype,
+                                void* dK, void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* ws,
+                                const BwdPlan& p, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
   const int BH = p.f.BH;
   Saved sv;
   sv.lsyn = F(p.off_lsyn);
   sv.lenc = F(p.off_lenc);
-  sv.hilo = true;
-  sv.no_decode = true;
-  int rc = enqueue(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, nullptr, F(p.off_qd), nullptr, F(p.off_z32), ws,
-                   p.f, st, sv);
-  if (rc != FLAREPP_OK) return rc;
   void* qrows = w + p.f.off_q;
   float* ldec = F(p.off_ldec);
   float* cd = F(p.off_cd);
@@ -611,9 +626,22 @@ int enqueue_backward(const void* K, const void* V, const void* S, const void* Qs
   return FLAREPP_OK;
 }
 
+int enqueue_backward(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                     const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype, void* dK,
+                     void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* ws, const BwdPlan& p,
+                     hipStream_t st) {
+  const int rc = enqueue_saved_forward(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, nullptr, ws, p, st);
+  if (rc != FLAREPP_OK) return rc;
+  return enqueue_backward_from_saved(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg,
+                                     ws, p, st);
+}
+
+// from_saved: the workspace holds the state of flarepp_mix_forward_saved for the same inputs, and the
+// backward starts from it instead of recomputing it.
 int backward_common(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf, const float* g,
                     const void* dY, int B, int H, int64_t N, int M, int D, int dtype, void* dK, void* dV, void* dS,
-                    void* dQseed, void* dQf, float* dg, void* ws, size_t ws_bytes, bool own_ws, hipStream_t st) {
+                    void* dQseed, void* dQf, float* dg, void* ws, size_t ws_bytes, bool own_ws, hipStream_t st,
+                    bool from_saved = false) {
   bool empty = false;
   int rc = validate_bwd_sizes(B, H, N, M, D, dtype, &empty);
   if (rc != FLAREPP_OK) return rc;
@@ -654,9 +682,29 @@ int backward_common(const void* K, const void* V, const void* S, const void* Qse
       return FLAREPP_OUT_OF_MEMORY;
     }
   }
-  rc = enqueue_backward(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, ws, p, st);
+  rc = from_saved ? enqueue_backward_from_saved(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed,
+                                                dQf, dg, ws, p, st)
+                  : enqueue_backward(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg,
+                                     ws, p, st);
   if (own_ws) (void)hipFreeAsync(ws, st);
   return rc;
+}
+
+// The forward that keeps the state the backward starts from (flarepp_mix_forward_saved).
+int forward_saved_common(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                         const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out, void* ws,
+                         size_t ws_bytes, hipStream_t st) {
+  bool empty = false;
+  int rc = validate_bwd_sizes(B, H, N, M, D, dtype, &empty);
+  if (rc != FLAREPP_OK || empty) return rc;
+  rc = validate_pointers(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out);
+  if (rc != FLAREPP_OK) return rc;
+  const BwdPlan p = make_bwd_plan(B, H, N, M, D, dtype);
+  if (!ws || ws_bytes < p.total) return FLAREPP_INVALID_ARGUMENT;
+  if ((uintptr_t)ws & 255) return FLAREPP_MISALIGNED;
+  rc = check_device();
+  if (rc != FLAREPP_OK) return rc;
+  return enqueue_saved_forward(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, ws, p, st);
 }
 
 // ---- Projections around the mixer and the whole block --------------------------------------
@@ -951,6 +999,20 @@ int flarepp_mix_backward_ws(const void* K, const void* V, const void* S, const v
                             size_t workspace_bytes, hipStream_t stream) {
   return backward_common(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, workspace,
                          workspace_bytes, false, stream);
+}
+
+int flarepp_mix_forward_saved(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                              const float* g, int B, int H, int64_t N, int M, int D, int dtype, void* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_saved_common(K, V, S, Qseed, Qf, g, B, H, N, M, D, dtype, out, workspace, workspace_bytes, stream);
+}
+
+int flarepp_mix_backward_saved(const void* K, const void* V, const void* S, const void* Qseed, const void* Qf,
+                               const float* g, const void* dY, int B, int H, int64_t N, int M, int D, int dtype,
+                               void* dK, void* dV, void* dS, void* dQseed, void* dQf, float* dg, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return backward_common(K, V, S, Qseed, Qf, g, dY, B, H, N, M, D, dtype, dK, dV, dS, dQseed, dQf, dg, workspace,
+                         workspace_bytes, false, stream, true);
 }
 
 int flarepp_project(const void* X, const void* Wk, const void* Wv, const void* Ws, const void* bk, const void* bv,

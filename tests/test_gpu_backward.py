@@ -317,3 +317,40 @@ def test_bwd_tiny_token_counts(dtype, N):
     in the recompute, c was about 2^-8 off and these two tensors reached 3.6% of their RMS."""
     w = make_workload(1, B=1, H=1, N=N, M=257, D=16, dtype=dtype, kind="gauss", seed=8003)
     _check(w, label=f"bwd tiny N={N} {dtype}")
+
+
+# ---- the backward from the forward's saved state (flarepp_mix_forward_saved, _backward_saved) ----
+@pytest.mark.parametrize("cfg,kw", [(1, {}), (3, dict(B=2, H=2, N=3000)), (4, dict(B=1, H=2, N=20000)),
+                                    (4, dict(B=1, H=2, N=3001, M=300, seed=9)), (5, dict(H=2, N=65536))])
+def test_saved_forward_and_backward(cfg, kw):
+    """flarepp_mix_forward_saved's output meets the forward's bar against the oracle, and
+    flarepp_mix_backward_saved from its workspace equals flarepp_mix_backward_ws bit for bit, for two
+    cotangents in a row (the backward only reads the saved state)."""
+    import rank_latent_routing_amd as fl
+    from gpu_util import oracle_head
+    w = make_workload(cfg, **kw)
+    dt = 1 if w.dtype == "bf16" else 0
+    say(f"[saved] {w.name} {kw}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    dev = to_device(w)
+    args = (dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"])
+    need = fl.flarepp_backward_workspace_bytes(w.B, w.H, w.N, w.M, w.D, dt)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws_ref = torch.empty(need, dtype=torch.uint8, device="cuda")
+    Y = fl.flarepp_mix_forward_saved(*args, workspace=ws)
+    torch.cuda.synchronize()
+    Yn = Y.float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            worst = max(worst, slice_err(Yn[b, h], oracle_head(w, b, h)["Y"], w.dtype))
+    say(f"[saved] forward: worst {worst:.3g} (bar {tol(w.dtype)})")
+    assert worst <= tol(w.dtype)
+    for k, seed in enumerate((None, 77)):
+        dy = _device(make_cotangent(w, seed=seed), w.dtype)
+        a = fl.flarepp_mix_backward_saved(*args, dy, workspace=ws)
+        b = fl.flarepp_mix_backward(*args, dy, workspace=ws_ref)
+        torch.cuda.synchronize()
+        for name in a:
+            same = torch.equal(a[name].view(torch.int16) if a[name].dtype == torch.bfloat16 else a[name],
+                               b[name].view(torch.int16) if b[name].dtype == torch.bfloat16 else b[name])
+            assert same, (k, name)
