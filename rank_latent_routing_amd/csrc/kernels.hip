@@ -47,6 +47,19 @@
 namespace flarepp {
 namespace {
 
+// v on lanes l and l ^ 32 combined, on every lane, through one swap of the wave's halves
+// (v_permlane32_swap: the first result holds lanes 0-31 of v in both halves, the second lanes
+// 32-63): no LDS permute and no lane-index arithmetic. Sums and maxima are commutative, so every
+// lane gets exactly v_l + v_(l^32) (or the max), as a shfl_xor by 32 would give.
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A priori bounds on the logits (log2 units) of the zero-shift passes with fp16 score operands. The
 // fp16 rounding of a computed score operand (the synthesis keys c N0(s), the routing queries c Q)
 // moves a logit by at most 2^-11 of the bound, and the output's sensitivity to that error grows
@@ -606,7 +619,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
           float tm = fmaxf(fmaxf(fmaxf(s0v[lb][0], s0v[lb][1]), fmaxf(s0v[lb][2], s0v[lb][3])),
                            fmaxf(fmaxf(s1v[lb][0], s1v[lb][1]), fmaxf(s1v[lb][2], s1v[lb][3])));
           tm = fmaxf(tm, shfl_xor(tm, 16));
-          tm = fmaxf(tm, shfl_xor(tm, 32));
+          tm = max_xor32(tm);
           const float mold = mrow[lb];
           const float mnew = fmaxf(mold, tm);
           const float alpha = (mnew == mold) ? 1.0f : exp2_fast(mold - mnew);
@@ -896,7 +909,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
         for (int kh = 0; kh < 2; kh++)
 #pragma unroll
           for (int e = 0; e < 8; e++) ss += (float)qw[nb][kh][e] * (float)qw[nb][kh][e];
-        ss += shfl_xor(ss, 32);
+        ss = sum_xor32(ss);
         qss = fmaxf(qss, ss);
       }
     } else {
@@ -904,7 +917,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       for (int lb = 0; lb < NLB; lb++) {
         float ss = O::sumsq(qb[lb]);
         ss += shfl_xor(ss, 16);
-        ss += shfl_xor(ss, 32);
+        ss = sum_xor32(ss);
         qss = fmaxf(qss, ss);
       }
     }
@@ -930,7 +943,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       if (active) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
-          const float l = lw[nb] + shfl_xor(lw[nb], 32);
+          const float l = sum_xor32(lw[nb]);
           ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
 #pragma unroll
           for (int v = 0; v < 16; v++) ok = ok && fabsf(zw[nb][v]) <= 3.0e38f;
@@ -952,7 +965,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
         if (!active) return;
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
-          const float l = lw[nb] + shfl_xor(lw[nb], 32);
+          const float l = sum_xor32(lw[nb]);
           const int row = lat0 + 32 * nb + (lane & 31);
           if (h32 == 0 && row < a.Mp) {
             a.part_l[pbase + row] = l;
@@ -979,7 +992,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
       for (int lb = 0; lb < NLB; lb++) {
         float l = lsum[lb];
         l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
+        l = sum_xor32(l);
         ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
 #pragma unroll
         for (int db = 0; db < NDB; db++)
@@ -999,7 +1012,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
   for (int lb = 0; lb < NLB; lb++) {
     float l = lsum[lb];
     l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    l = sum_xor32(l);
     const int row = lat0 + 16 * lb + c;
     if (g == 0 && row < a.Mp) {
       a.part_l[pbase + row] = l;
@@ -1267,7 +1280,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int t = 0; t < TB; t++) {
       float l = lsum[t];
       l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
+      l = sum_xor32(l);
       ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
 #pragma unroll
       for (int db = 0; db < NDB; db++)
@@ -1289,7 +1302,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < TB; t++) {
         shift[t] = fmaxf(shift[t], shfl_xor(shift[t], 16));
-        shift[t] = fmaxf(shift[t], shfl_xor(shift[t], 32));
+        shift[t] = max_xor32(shift[t]);
       }
       clear();
       accumulate(std::true_type{});
@@ -1299,7 +1312,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int t = 0; t < TB; t++) {
       float l = lsum[t];
       l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
+      l = sum_xor32(l);
       const float inv = 1.0f / l;
       const int64_t tok = base + 16 * t + c;
       if (tok < t_end) {
@@ -1530,18 +1543,19 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; v++) x[v0 + v] = exp2_fast(x[v0 + v]);
         };
-        // qn holds the query operands of block lb+1 on entry and of block lb+2 on exit. LAST: the
-        // final latent block, whose rows past M are masked when M is not a multiple of 32 (kept
-        // out of the loop so the mask costs nothing per block).
-        auto step = [&](auto LAST, int lb, f32x16& cu, f32x16& nx, QOp& qn) __attribute__((always_inline)) {
+        // qn holds the query operands of block lb+1 on entry and of block lb+2 on exit. mask: the
+        // final latent block when M is not a multiple of 32, whose rows past M are masked (a
+        // wave-uniform branch, so the other blocks pay no VALU for it).
+        // FIRST: block 0, whose P.V product and token sums start from a zero accumulator (an inline
+        // constant of the MFMA), so the accumulators need no clearing per wave group.
+        auto step = [&](auto FIRST, bool mask, int lb, f32x16& cu, f32x16& nx, QOp& qn) __attribute__((always_inline)) {
+          constexpr bool kFirst = decltype(FIRST)::value;
           const bf16x8 zb0 = load_rows32(zs, ZSTR, 32 * lb, 0, lane);
           const bf16x8 zb1 = load_rows32(zs, ZSTR, 32 * lb + 16, 0, lane);
-          if constexpr (decltype(LAST)::value) {
-            if (ragged) {
+          if (mask) {
 #pragma unroll
-              for (int v = 0; v < 16; v++)
-                if (32 * lb + row32(v, h) >= a.M) cu[v] = -INFINITY;
-            }
+            for (int v = 0; v < 16; v++)
+              if (32 * lb + row32(v, h) >= a.M) cu[v] = -INFINITY;
           }
           nx = mfma_32x32_f16(qn.a, kf[0][0], f32x16{});
           fence();
@@ -1556,8 +1570,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
           const bf16x8 p0 = pack32(cu, 0);
           if constexpr (!kSumsOnMfma) lsum[0] = Ops<bf16, 32>::osum(p0, lsum[0]);
           fence();
-          yacc[0] = mfma_32x32(zb0, p0, yacc[0]);
-          if constexpr (kSumsOnMfma) ls4 = mfma_32k(dsel, p0, ls4);
+          yacc[0] = mfma_32x32(zb0, p0, kFirst ? f32x16{} : yacc[0]);
+          if constexpr (kSumsOnMfma) ls4 = mfma_32k(dsel, p0, kFirst ? f32x4{} : ls4);
           fence();
           keep_live(p0);
           keep_live(zb0);
@@ -1581,18 +1595,19 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
           keep_live(q0.a);
           keep_live(q0.b);
         }
-        ls4 = f32x4{0.f, 0.f, 0.f, 0.f};
         QOp qn = load_q(1);
-        int lb = 0;
-        for (; lb + 2 < nlb; lb += 2) {
-          step(std::false_type{}, lb, sa, sb, qn);
-          step(std::false_type{}, lb + 1, sb, sa, qn);
-        }
-        if (lb + 2 == nlb) {
-          step(std::false_type{}, lb, sa, sb, qn);
-          step(std::true_type{}, lb + 1, sb, sa, qn);
+        // Pairs of blocks (the scores alternate between sa and sb), then an odd last block.
+        if (nlb >= 2) {
+          step(std::true_type{}, false, 0, sa, sb, qn);
+          step(std::false_type{}, ragged && nlb == 2, 1, sb, sa, qn);
+          int lb = 2;
+          for (; lb + 2 <= nlb; lb += 2) {
+            step(std::false_type{}, false, lb, sa, sb, qn);
+            step(std::false_type{}, ragged && lb + 2 == nlb, lb + 1, sb, sa, qn);
+          }
+          if (lb < nlb) step(std::false_type{}, ragged, lb, sa, sb, qn);
         } else {
-          step(std::true_type{}, lb, sa, sb, qn);
+          step(std::true_type{}, ragged, 0, sa, sb, qn);
         }
         if constexpr (kSumsOnMfma) {
           // Token t = l % 32 sums to column t % 16 of rows 0-7 (t < 16) or 8-15 (t >= 16): lane
@@ -1603,25 +1618,32 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
       }
     };
 
-    clear();
+    // The pipelined pass starts its accumulators from zero itself; the others are cleared.
+#pragma unroll
+    for (int tb = 0; tb < TB; tb++) lsum[tb] = 0.f;
     bool ok = a.force_exact == 0;
     // Routing bound (kRouteBound): a group holding a token beyond it takes the exact pass at once.
 #pragma unroll
-    for (int tb = 0; tb < TB; tb++) ok = ok && qmax2 * (k2[tb] + shfl_xor(k2[tb], 32)) <= kRouteBound * kRouteBound;
+    for (int tb = 0; tb < TB; tb++) ok = ok && qmax2 * sum_xor32(k2[tb]) <= kRouteBound * kRouteBound;
     ok = __all(ok);
     if (ok) {
-      if constexpr (TB == 1)
+      if constexpr (TB == 1) {
         accumulate_fast_pipelined();
-      else
+      } else {
+        clear();
         accumulate(std::false_type{});
+      }
     }
 
+    // Within the routing bound every logit of the pass lies in [-kRouteBound, kRouteBound], so each
+    // probability is within 2^+-kRouteBound and the row sum l of up to Mp of them within [2^-80,
+    // 2^100]; a sum outside that range means a key beyond fp16 range (or NaN). The accumulator is
+    // then at most 2^(kRouteBound + 10) max |Z|, finite for the inputs the library takes (it checks
+    // no accumulator: where it would overflow, so would the exact pass's Z).
 #pragma unroll
     for (int tb = 0; tb < TB; tb++) {
-      const float l = lsum[tb] + shfl_xor(lsum[tb], 32);
+      const float l = sum_xor32(lsum[tb]);
       ok = ok && l >= 0x1p-80f && l <= 0x1p100f;
-#pragma unroll
-      for (int v = 0; v < 16; v++) ok = ok && fabsf(yacc[tb][v]) <= 3.0e38f;
     }
     if (!__all(ok)) {
 #pragma unroll
@@ -1640,7 +1662,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int tb = 0; tb < TB; tb++) {
-        shift[tb] = fmaxf(shift[tb], shfl_xor(shift[tb], 32));
+        shift[tb] = max_xor32(shift[tb]);
         if (shift[tb] == -INFINITY) shift[tb] = 0.f;
       }
       clear();
@@ -1652,7 +1674,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
     // stored as one 8-byte write, and the token's sum is the lane's own (plus its partner l ^ 32).
 #pragma unroll
     for (int tb = 0; tb < TB; tb++) {
-      const float inv = 1.0f / (lsum[tb] + shfl_xor(lsum[tb], 32));
+      const float inv = __builtin_amdgcn_rcpf(sum_xor32(lsum[tb]));  // 1 ulp, then rounded to bf16
       const int64_t tok = base + 32 * tb + col;
       if (tok < t_end) {
 #pragma unroll
