@@ -278,13 +278,16 @@ struct Ops<float, D> {
 
 
 // LDS layout of a tile whose rows (tokens or latents) run along the k-range of a P.V operand:
-// bf16 keeps the rows (read with transposed loads), fp32 stores the transpose. The bf16 row stride
-// puts rows 4 apart 32 bytes apart modulo the LDS banks, so the transposed reads of a 16-lane
-// group (4 rows x 32 bytes) do not conflict.
-template <typename T, int D>
+// bf16 keeps the rows (read with transposed loads), fp32 stores the transpose. gfx950's LDS serves
+// 64 banks of 4 bytes per cycle, 32 lanes of a transposed 8-byte read: for D = 32 those lanes read
+// rows r0..r0+3 at bytes 0-31 and 32-63 of each, which unpadded 64-byte rows spread over all 256
+// bytes (SQ_LDS_BANK_CONFLICT per 32x32 tile of the partial kernels: 10 with 96-byte rows, 1 with
+// these). PAD: elements added per row (the decode keeps 16, which measured faster there).
+constexpr int kDecodeZPad = 16;  // decode_wide_kernel's Z rows: 96 bytes
+template <typename T, int D, int PAD = (D == 32 ? 0 : 8)>
 struct RowTile {
   static constexpr bool kTransposed = sizeof(T) == 4;
-  static constexpr int kRowStride = D + (D == 32 ? 16 : 8);
+  static constexpr int kRowStride = D + PAD;
   __host__ __device__ static constexpr int tstride(int rows) { return rows + 4; }
   __host__ __device__ static constexpr int elems(int rows) { return kTransposed ? D * tstride(rows) : rows * kRowStride; }
   __host__ __device__ static constexpr int stride(int rows) { return kTransposed ? tstride(rows) : kRowStride; }
@@ -292,9 +295,9 @@ struct RowTile {
 
 
 // Store one 16-byte chunk (elements col .. col + 16/sizeof(T) - 1 of row `row`) into a RowTile.
-template <typename T, int D>
+template <typename T, int D, int PAD = (D == 32 ? 0 : 8)>
 __device__ __forceinline__ void rowtile_store(T* tile, int rows, int row, int col, const Chunk& ck) {
-  using RT = RowTile<T, D>;
+  using RT = RowTile<T, D, PAD>;
   if constexpr (RT::kTransposed) {
     float x[4];
     chunk_to_float<T>(ck, x);
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 #pragma unroll
           for (int j = 0; j < CH; j++) ss += x[j] * x[j];
           ss = group_sum<CPR>(ss);
-          const float inv = 1.0f / sqrtf(ss * (1.0f / D) + kRmsEps);
+          const float inv = rsqrtf(ss * (1.0f / D) + kRmsEps);  // v_rsq_f32 (1 ulp)
           float kx[CH];
 #pragma unroll
           for (int j = 0; j < CH; j++) {
@@ -1349,7 +1352,7 @@ template <int NW, int TB, bool PREF = true>
 __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
   constexpr int D = 32;
   constexpr int QHS = D + 8;  // fp16 query row stride in LDS (80 bytes: conflict-free row reads)
-  using ZT = RowTile<bf16, D>;
+  using ZT = RowTile<bf16, D, kDecodeZPad>;
   constexpr int NT = NW * 64;
   constexpr int TG = 32 * TB;
 
@@ -1374,7 +1377,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
     const Chunk qc = *reinterpret_cast<const Chunk*>(qsrc + (int64_t)row * kQRow<bf16> * D + 2 * D + part * 8);
     *reinterpret_cast<Chunk*>(qh + row * QHS + part * 8) = qc;
     q2 = fmaxf(q2, group_sum<4>(sumsq_f16x8(__builtin_bit_cast(f16x8, qc))));
-    rowtile_store<bf16, D>(zs, Mp, row, part * 8, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * 8));
+    rowtile_store<bf16, D, kDecodeZPad>(zs, Mp, row, part * 8, *reinterpret_cast<const Chunk*>(zsrc + (int64_t)row * D + part * 8));
   }
   for (int q = tid; q < 32 * 4; q += NT) *reinterpret_cast<Chunk*>(qh + (Mp + (q >> 2)) * QHS + (q & 3) * 8) = Chunk{0u, 0u, 0u, 0u};
   float* qred = reinterpret_cast<float*>(zs + ZT::elems(Mp));  // [NW]
@@ -1814,7 +1817,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int nw, int gx, int gy, h
 
 static size_t decode_wide_lds(int Mp) {
   // fp16 query rows (and a zero block), the Z tile, and one float per wave (up to 16).
-  return (size_t)(Mp + 32) * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32>::elems(Mp) * sizeof(bf16) +
+  return (size_t)(Mp + 32) * (32 + 8) * sizeof(_Float16) + (size_t)RowTile<bf16, 32, kDecodeZPad>::elems(Mp) * sizeof(bf16) +
          16 * sizeof(float);
 }
 
