@@ -32,6 +32,13 @@ def test_committed_profiles_match_the_kernel_sources(profile, key, srcs, kernel)
     assert t is not None and t > 0
 
 
+def test_committed_backward_profile_matches_the_kernel_sources():
+    # The backward's dominant kernel: its roofline fraction is also reported on the committed trace's
+    # average duration while that trace matches the sources.
+    us = bench.profiled_kernel_us("bwd_token_decode", bench.BWD_PROFILE, "backward_sources_sha256", bench.BWD_SRCS)
+    assert us is not None and us > 0
+
+
 def test_profiled_traffic_is_null_for_another_source(tmp_path):
     sha = bench.kernel_source_hash()
     rec = {"forward_sources_sha256": sha, "per_launch_bytes": {"decode": 123.0}}
