@@ -236,6 +236,8 @@ def microbench():
     L.flarepp_mb_compute.restype = i32
     L.flarepp_mb_stream.argtypes = [vp, vp, i64, i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
     L.flarepp_mb_stream.restype = i32
+    L.flarepp_mb_fanout.argtypes = [vp, vp, i64, i32, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]
+    L.flarepp_mb_fanout.restype = i32
     L.flarepp_mb_kind_name.argtypes = [i32]
     L.flarepp_mb_kind_name.restype = ctypes.c_char_p
     props = torch.cuda.get_device_properties(0)
@@ -286,6 +288,17 @@ def microbench():
         ms = ctypes.c_double()
         rc = L.flarepp_mb_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(0 if d is None else d.data_ptr()),
                                  nbytes, sgrid, 5, ctypes.c_void_p(red.data_ptr()), stream, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"microbenchmark {name}: HIP error {rc}")
+        res[name + "_gbs"] = round(moved / (ms.value * 1e-3) * 1e-9, 1)
+    # Writes alone, and the front projection's mix: one tensor read, three of its size written.
+    del dst
+    nfan = 2 ** 29
+    fdst = torch.empty(3 * nfan // 4, dtype=torch.float32, device="cuda")
+    for name, s_ptr, copies, moved in (("hbm_write", 0, 1, nfan), ("hbm_read1_write3", src.data_ptr(), 3, 4 * nfan)):
+        ms = ctypes.c_double()
+        rc = L.flarepp_mb_fanout(ctypes.c_void_p(s_ptr), ctypes.c_void_p(fdst.data_ptr()), nfan, copies, sgrid, 5,
+                                 stream, ctypes.byref(ms))
         if rc != 0:
             raise RuntimeError(f"microbenchmark {name}: HIP error {rc}")
         res[name + "_gbs"] = round(moved / (ms.value * 1e-3) * 1e-9, 1)

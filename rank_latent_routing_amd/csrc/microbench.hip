@@ -277,6 +277,30 @@ __global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ s
   if (!dst) out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)fold;
 }
 
+// Each 16-byte chunk i of `src` (or, with src null, a value made from i) written to `copies`
+// destinations dst + j n16: the traffic mix of a kernel that reads one tensor and writes several.
+__global__ __launch_bounds__(256) void fan_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                  int64_t n16, int copies) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int64_t k = i + u * stride;
+      v[u] = src ? src[k] : make_uint4((uint32_t)k, (uint32_t)(k >> 32), 1u, 2u);
+    }
+    for (int j = 0; j < copies; j++) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) dst[i + u * stride + j * n16] = v[u];
+    }
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src ? src[i] : make_uint4((uint32_t)i, (uint32_t)(i >> 32), 1u, 2u);
+    for (int j = 0; j < copies; j++) dst[i + j * n16] = v;
+  }
+}
+
 template <int KIND>
 hipError_t launch_compute(int grid, float* out, int iters, hipStream_t st) {
   hipLaunchKernelGGL(compute_kernel<KIND>, dim3(grid), dim3(256), 0, st, out, iters, 0.5f);
@@ -354,6 +378,36 @@ int flarepp_mb_compute(int kind, int grid, int iters, int reps, float* out, hipS
   if ((e = hipEventCreate(&b)) != hipSuccess) { (void)hipEventDestroy(a); return (int)e; }
   (void)hipEventRecord(a, st);
   for (int r = 0; r < reps && e == hipSuccess; r++) e = launch_kind(kind, grid, out, iters, st);
+  (void)hipEventRecord(b, st);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float t = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&t, a, b);
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  *ms = (double)t / reps;
+  return (int)e;
+}
+
+// Reads `bytes` (a multiple of 16) from `src` (null: writes only) and writes them `copies` (1-4)
+// times, to dst, dst + bytes, ...; timing as flarepp_mb_compute.
+int flarepp_mb_fanout(const void* src, void* dst, int64_t bytes, int copies, int grid, int reps, hipStream_t st,
+                      double* ms) {
+  if (!dst || bytes <= 0 || (bytes & 15) || copies < 1 || copies > 4 || grid < 1 || reps < 1 || !ms)
+    return (int)hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const uint4* s = static_cast<const uint4*>(src);
+  uint4* d = static_cast<uint4*>(dst);
+  hipLaunchKernelGGL(fan_kernel, dim3(grid), dim3(256), 0, st, s, d, n16, copies);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipEvent_t a, b;
+  if ((e = hipEventCreate(&a)) != hipSuccess) return (int)e;
+  if ((e = hipEventCreate(&b)) != hipSuccess) { (void)hipEventDestroy(a); return (int)e; }
+  (void)hipEventRecord(a, st);
+  for (int r = 0; r < reps && e == hipSuccess; r++) {
+    hipLaunchKernelGGL(fan_kernel, dim3(grid), dim3(256), 0, st, s, d, n16, copies);
+    e = hipGetLastError();
+  }
   (void)hipEventRecord(b, st);
   if (e == hipSuccess) e = hipEventSynchronize(b);
   float t = 0.f;

@@ -256,7 +256,8 @@ def test_microbenchmark_library_loads_and_validates():
     # any launch (no GPU needed).
     from rank_latent_routing_amd.build import MB_LIB
     M = ctypes.CDLL(MB_LIB)
-    for n in ("flarepp_mb_compute", "flarepp_mb_stream", "flarepp_mb_kind_name", "flarepp_mb_num_kinds"):
+    for n in ("flarepp_mb_compute", "flarepp_mb_stream", "flarepp_mb_fanout", "flarepp_mb_kind_name",
+              "flarepp_mb_num_kinds"):
         assert hasattr(M, n), n
     M.flarepp_mb_kind_name.restype = ctypes.c_char_p
     kinds = [M.flarepp_mb_kind_name(i).decode() for i in range(M.flarepp_mb_num_kinds())]
@@ -266,6 +267,10 @@ def test_microbenchmark_library_loads_and_validates():
     vp = ctypes.c_void_p
     assert M.flarepp_mb_compute(0, 0, 16, 1, vp(0x1000), vp(0), ctypes.byref(ms)) != 0
     assert M.flarepp_mb_stream(vp(0x1000), vp(0x2000), ctypes.c_int64(15), 1, 1, vp(0), vp(0), ctypes.byref(ms)) != 0
+    M.flarepp_mb_fanout.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                    ctypes.POINTER(ctypes.c_double)]
+    assert M.flarepp_mb_fanout(vp(0x1000), vp(0x2000), 15, 1, 1, 1, vp(0), ctypes.byref(ms)) != 0
+    assert M.flarepp_mb_fanout(vp(0x1000), vp(0x2000), 16, 5, 1, 1, vp(0), ctypes.byref(ms)) != 0
 
 
 def _host_inputs(B=1, H=2, N=40, M=8, D=16, dtype=None):
