@@ -50,7 +50,9 @@ namespace {
 // v on lanes l and l ^ 32 combined, on every lane, through one swap of the wave's halves
 // (v_permlane32_swap: the first result holds lanes 0-31 of v in both halves, the second lanes
 // 32-63): no LDS permute and no lane-index arithmetic. Sums and maxima are commutative, so every
-// lane gets exactly v_l + v_(l^32) (or the max), as a shfl_xor by 32 would give.
+// lane gets exactly v_l + v_(l^32) (or the max), as a shfl_xor by 32 would give. The swap reads the
+// partner lane whether or not it is active, so callers run it with all 64 lanes active (every use
+// sits in wave-uniform control flow).
 __device__ __forceinline__ float sum_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
