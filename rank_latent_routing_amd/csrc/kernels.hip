@@ -62,6 +62,25 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// x0 - hi0 and x1 - hi1, where hp holds hi0 (low half) and hi1 (high half), the bf16 roundings of
+// x0 and x1: one bf16 dot product per value (x + hi * -1 + other * 0), exact as x - hi is a float.
+// The selectors (-1, 0) and (0, -1) sit in registers as literals: an inline-constant encoding of a
+// packed bf16 operand need not place the value in the half the vector names.
+typedef float residual2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t literal_u32(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+__device__ __forceinline__ residual2_t bf16_residual2(uint32_t hp, float x0, float x1) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 h = __builtin_bit_cast(b2, hp);
+  const b2 m0 = __builtin_bit_cast(b2, literal_u32(0x0000bf80u));  // element 0: -1, element 1: 0
+  const b2 m1 = __builtin_bit_cast(b2, literal_u32(0xbf800000u));  // element 0: 0, element 1: -1
+  return residual2_t{__builtin_amdgcn_fdot2_f32_bf16(h, m0, x0, false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h, m1, x1, false)};
+}
+
 // A priori bounds on the logits (log2 units) of the zero-shift passes with fp16 score operands. The
 // fp16 rounding of a computed score operand (the synthesis keys c N0(s), the routing queries c Q)
 // moves a logit by at most 2^-11 of the bound, and the output's sensitivity to that error grows
@@ -691,12 +710,14 @@ __global__ __launch_bounds__(NW * 64) void partial_kernel(PartialArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; db++) zacc[lb][db] = O::pv(pa, vb[db], zacc[lb][db]);
         if constexpr (HILO) {
-          f32x4 r0, r1;
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            r0[i] = s0v[lb][i] - (float)pa[i];
-            r1[i] = s1v[lb][i] - (float)pa[4 + i];
-          }
+          // Residuals s - bf16(s), two per packed word of pa (bf16_residual2).
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 pw = __builtin_bit_cast(u32x4, pa);
+          const residual2_t a0 = bf16_residual2(pw[0], s0v[lb][0], s0v[lb][1]);
+          const residual2_t a1 = bf16_residual2(pw[1], s0v[lb][2], s0v[lb][3]);
+          const residual2_t b0 = bf16_residual2(pw[2], s1v[lb][0], s1v[lb][1]);
+          const residual2_t b1 = bf16_residual2(pw[3], s1v[lb][2], s1v[lb][3]);
+          const f32x4 r0 = {a0[0], a0[1], a1[0], a1[1]}, r1 = {b0[0], b0[1], b1[0], b1[1]};
           const Oct pl = O::pack(r0, r1);
           lsum[lb] = O::osum(pl, lsum[lb]);
 #pragma unroll
