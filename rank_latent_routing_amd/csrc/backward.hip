@@ -812,7 +812,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
   T* tiles = reinterpret_cast<T*>(smem);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), hh = lane >> 5;
   const int bh = blockIdx.y;
   {
     const T* qsrc = reinterpret_cast<const T*>(a.Qrows) + (int64_t)bh * Mp * kQRow<T> * D;
@@ -968,12 +968,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
     });
     if (valid) {
       // dK_dec = (1/sqrt(D)) dS Q = ln 2 * dS (c*Q); slot v holds dim row32(v, l / 32).
-      float* dk = a.dKdec + ((int64_t)bh * a.N + tok) * D;
+      float* dk = a.dKdec + ((int64_t)bh * a.N + base) * D;
 #pragma unroll
       for (int gq = 0; gq < 4; gq++) {
         const int d0 = row32(4 * gq, hh);
         if (d0 < D)
-          *reinterpret_cast<f32x4*>(dk + d0) = f32x4{accK[4 * gq] * kLn2, accK[4 * gq + 1] * kLn2,
+          *reinterpret_cast<f32x4*>(dk + (lane & 31) * D + d0) = f32x4{accK[4 * gq] * kLn2, accK[4 * gq + 1] * kLn2,
                                                     accK[4 * gq + 2] * kLn2, accK[4 * gq + 3] * kLn2};
       }
     }
@@ -1371,8 +1371,7 @@ size_t bwd_token_lds_bytes(int dtype, int D, int Mp, int kind) {
   return D == 32 ? bwd_token_lds_t<float, 32>(Mp, kind) : bwd_token_lds_t<float, 16>(Mp, kind);
 }
 
-// NW waves per workgroup for the encode and synthesis kernels; the decode kernel always runs 8 (it
-// would spill at 12, which allow at most 168 registers per lane).
+// NW waves per workgroup (8 or 12) for every token-side kernel.
 template <typename T, int D, int NW>
 static hipError_t launch_bwd_token_t(const BwdTokenArgs& a, int kind, int gx, int BH, hipStream_t st) {
   const size_t lds = bwd_token_lds_t<T, D>(a.Mp, kind);
@@ -1383,7 +1382,10 @@ static hipError_t launch_bwd_token_t(const BwdTokenArgs& a, int kind, int gx, in
     return hipGetLastError();
   };
   switch (kind) {
-    case kBwdTokDecode: return go(bwd_token_decode_kernel<T, D, kBwdTokenWaves>, kBwdTokenWaves);
+    case kBwdTokDecode:
+      // fp32 with 32 channels has no 12-wave instance (it would spill): it runs 8.
+      if constexpr (std::is_same<T, float>::value && D == 32 && NW == 12) return hipErrorInvalidValue;
+      else return go(bwd_token_decode_kernel<T, D, NW>, NW);
     case kBwdTokEncode: return go(bwd_token_encode_kernel<T, D, NW>, NW);
     default: return go(bwd_token_synthesis_kernel<T, D, NW>, NW);
   }

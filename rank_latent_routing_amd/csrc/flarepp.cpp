@@ -460,6 +460,7 @@ struct BwdPlan {
   int64_t lat_chunk = 0;
   int tok_gx = 0;
   int tok_nw = flarepp::kBwdTokenWavesWide;  // waves per workgroup of the token encode and synthesis kernels
+  int tok_dec_nw = flarepp::kBwdTokenWaves;  // ... and of the token decode kernel
   int64_t tok_tpw = 0;
   size_t off_qd = 0, off_z32 = 0, off_lsyn = 0, off_lenc = 0, off_zc = 0, off_zc_lo = 0, off_ldec = 0;
   size_t off_cd = 0, off_dkdec = 0, off_p0 = 0, off_p1 = 0, off_dz32 = 0, off_dzop = 0, off_dzop_lo = 0;
@@ -487,9 +488,13 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.lat_nchunk = (int)ceil_div(N, p.lat_chunk);
   p.lat_gx = p.lat_nlg == 1 ? p.lat_nchunk : (int)(ceil_div(p.lat_nchunk, 8) * 8 * p.lat_nlg);
   // Token side: about 512 workgroups, 32-token blocks. The latent tensors in LDS leave room for one
-  // workgroup per CU: 8 waves for the decode kernel, 12 (3 per SIMD) for encode and synthesis.
+  // workgroup per CU: 12 waves (3 per SIMD) for encode and synthesis, and for the decode kernel
+  // where its registers allow (bwd_decode_waves).
   const int tok_env = env_int("FLAREPP_BWD_TOKEN_WAVES", 0);
   if (tok_env == 8 || tok_env == 12) p.tok_nw = tok_env;
+  p.tok_dec_nw = flarepp::bwd_decode_waves(dtype);
+  const int dec_env = env_int("FLAREPP_BWD_DECODE_WAVES", 0);
+  if (dec_env == 8 || (dec_env == 12 && dtype == FLAREPP_BF16)) p.tok_dec_nw = dec_env;
   const int64_t tok_target = env_int("FLAREPP_BWD_TOKEN_WORKGROUPS", 512);
   int64_t gx = ceil_div(tok_target, (int64_t)BH);
   const int64_t max_gx = ceil_div(N, (int64_t)32 * flarepp::kBwdTokenWaves);
@@ -584,7 +589,7 @@ int enqueue_backward_from_saved(const void* K, const void* V, const void* S, con
   ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
   ta.lsyn = sv.lsyn; ta.cs = F(p.off_cs); ta.dK = dK; ta.dV = dV; ta.dS = dS; ta.N = N;
   ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H; ta.force_exact = g_force_exact.load() ? 1 : 0;
-  if (run_kernel(7, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokDecode, p.tok_nw, p.tok_gx, BH, st); }) != hipSuccess)
+  if (run_kernel(7, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokDecode, p.tok_dec_nw, p.tok_gx, BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
   flarepp::BwdLatentArgs la{};

@@ -184,8 +184,11 @@ struct BwdCenterArgs {
 constexpr int bwd_stage_t(bool bf16, int nw) { return bf16 ? (nw == 8 ? 256 : 128) : 64; }
 inline int bwd_stage(int dtype, int nw) { return bwd_stage_t(dtype == 1, nw); }
 inline int bwd_latent_waves(int Mp) { return Mp >= 256 ? 8 : 4; }
-constexpr int kBwdTokenWaves = 8;       // token decode kernel
+constexpr int kBwdTokenWaves = 8;       // smallest token-side workgroup (the token split is sized for it)
 constexpr int kBwdTokenWavesWide = 12;  // token encode and synthesis kernels (8 also built)
+// Token decode kernel: 12 waves (3 per SIMD, at most 168 registers per lane) for bf16; fp32 keeps
+// 8, as its 32-channel instance would spill at 12 (no such instance is built).
+inline int bwd_decode_waves(int dtype) { return dtype == 1 ? 12 : 8; }
 
 hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, hipStream_t st);
 hipError_t launch_bwd_latent(const BwdLatentArgs& a, int dtype, int D, int call, int nw, int grid_x, int BH,
