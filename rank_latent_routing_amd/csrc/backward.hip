@@ -778,12 +778,13 @@ __device__ __forceinline__ void fill_blocked(T* lds, int j, const T* src, int st
   }
 }
 template <int NT>
-__device__ __forceinline__ void fill_stats(float* sl, float* sc, const float* l, const float* c, int Mp) {
+__device__ __forceinline__ void fill_stats(float* sl, float* sc, const float* l, const float* c, int Mp,
+                                           float c_factor = 1.f) {
   // Negated: the score and dP products start from -L and -c, so they come out as l - L and dP - c.
   for (int m = threadIdx.x; m < Mp; m += NT) {
     const int p = stat_pos(m);
     sl[p] = -l[m];
-    sc[p] = -c[m];
+    sc[p] = -c[m] * c_factor;
   }
 }
 
@@ -1114,7 +1115,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
 // normalized keys Sn = N0(S) as keys and values,
 //   dSn_n = (1/sqrt(D)) sum_m dS[m][n] Qseed_m + sum_m P[m][n] G_m,   dS = N0'(S)^T dSn,
 // where N0'(s)^T u = r u - r^3 s mean(s * u), r = (mean(s^2) + eps)^(-1/2). LDS holds the seeds, G / c
-// (a pair) and the per-latent L and c of the call.
+// and the per-latent L and c of the call.
+// bf16: sum_m P G enters the matrix unit as one fp16 product, P (<= 1) against G / c scaled by a
+// power of two per (batch, head) so that its largest element lies in (2^13, 2^14]; the end takes the
+// factor out exactly. dP = G . c Sn keeps both as bf16 pairs: near a one-hot row, dP - c is a
+// difference of nearly equal terms, and fp16 there put dS at the bar with seeds x6.
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenArgs a) {
   using F = Frag<T>;
@@ -1124,25 +1129,67 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
   constexpr int NT = NW * 64;
   constexpr int NP = F::kLo ? 2 : 1;
 
-  // Block-major LDS (fill_blocked): per 32 latents, the seeds (rows >= M zero), G / c hi, [lo];
-  // then the stats.
-  constexpr int NTILE = 1 + NP;
-  constexpr int TQS = 0, TGH = 1, TGL = 2;
+  // Block-major LDS (fill_blocked): per 32 latents, the seeds (rows >= M zero), G / c hi, [lo], [G / c
+  // in fp16, scaled]; then the stats.
+  constexpr bool kH = F::kLo;
+  constexpr int NTILE = kH ? 4 : 2;
+  constexpr int TQS = 0, TGH = 1, TGL = 2, TG16 = 3;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
   T* tiles = reinterpret_cast<T*>(smem);
   float* sl = reinterpret_cast<float*>(tiles + NTILE * Mp * D);  // [Mp] L_syn, stat_pos order
   float* sc = sl + Mp;                                            // [Mp] c_syn
+  float* gred = sc + Mp;                                          // [NW] (bf16)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int bh = blockIdx.y, h = bh % a.H;
+  float g_unscale = 1.f;  // bf16: 2^-e, with G / c scaled by 2^e
   {
     fill_blocked<T, D, NT, NTILE>(tiles, TQS, reinterpret_cast<const T*>(a.Qseed) + (int64_t)h * a.M * D, D, a.M, Mp);
-    fill_blocked<T, D, NT, NTILE>(tiles, TGH, reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D, D, Mp, Mp);
-    if constexpr (F::kLo)
-      fill_blocked<T, D, NT, NTILE>(tiles, TGL, reinterpret_cast<const T*>(a.G_lo) + (int64_t)bh * Mp * D, D, Mp, Mp);
+    const T* gh = reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D;
+    fill_blocked<T, D, NT, NTILE>(tiles, TGH, gh, D, Mp, Mp);
     fill_stats<NT>(sl, sc, a.lsyn + (int64_t)bh * Mp, a.cs + (int64_t)bh * Mp, Mp);
+    if constexpr (kH) {
+      constexpr int CPR = D / 8;
+      const T* gl = reinterpret_cast<const T*>(a.G_lo) + (int64_t)bh * Mp * D;
+      fill_blocked<T, D, NT, NTILE>(tiles, TGL, gl, D, Mp, Mp);
+      auto chunk_vals = [&](int q, float* v) __attribute__((always_inline)) {
+        float hv[8], lv[8];
+        chunk_to_float<T>(*reinterpret_cast<const Chunk*>(gh + q * 8), hv);
+        chunk_to_float<T>(*reinterpret_cast<const Chunk*>(gl + q * 8), lv);
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = hv[e] + lv[e];
+      };
+      float mx = 0.f;
+      for (int q = tid; q < Mp * CPR; q += NT) {
+        float v[8];
+        chunk_vals(q, v);
+#pragma unroll
+        for (int e = 0; e < 8; e++) mx = fmaxf(mx, fabsf(v[e]));
+      }
+      mx = wave_max(mx);
+      if (lane == 0) gred[wave] = mx;
+      __syncthreads();
+      mx = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; w++) mx = fmaxf(mx, gred[w]);
+      int e = 0;
+      (void)frexpf(mx, &e);  // mx < 2^e
+      const int sh = mx > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+      const float g_scale = ldexpf(1.f, sh);
+      g_unscale = ldexpf(1.f, -sh);
+      using Sw = Swz<T, D>;
+      for (int q = tid; q < Mp * CPR; q += NT) {
+        const int row = q / CPR, part = q % CPR;
+        float v[8];
+        chunk_vals(q, v);
+        f16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; i++) o[i] = (f16)(v[i] * g_scale);
+        *reinterpret_cast<f16x8*>(tiles + ((row >> 5) * NTILE + TG16) * 32 * D + Sw::off(row & 31, part * 8)) = o;
+      }
+    }
   }
   __syncthreads();
   const LaneOffs<T, D> lofs = lane_offsets<T, D>(lane);
@@ -1213,11 +1260,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
         accA = mma_ep<F>(qk, sk, accA);
         hold(accA, qk);
         hold<F>(accA, sk);
-        const Pair gk = krows_pair_at<F, D>(tile(lb, TGH) + 16 * t * D, tile(lb, TGL) + 16 * t * D, lofs);
-        const Pair pk = F::split(P, t);
-        accB = mma_pp<F>(gk, pk, accB);
-        hold<F>(accB, gk);
-        hold<F>(accB, pk);
+        if constexpr (kH) {
+          const Op gk = F::template krows_at<D>(tile(lb, TG16) + 16 * t * D, lofs);
+          f16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 8; e++) pk[e] = (f16)P[8 * t + e];
+          accB = mfma_32x32_f16(__builtin_bit_cast(f16x8, gk), pk, accB);
+          hold(accB, gk);
+          hold(accB, pk);
+        } else {
+          const Pair gk = krows_pair_at<F, D>(tile(lb, TGH) + 16 * t * D, tile(lb, TGL) + 16 * t * D, lofs);
+          const Pair pk = F::split(P, t);
+          accB = mma_pp<F>(gk, pk, accB);
+          hold<F>(accB, gk);
+          hold<F>(accB, pk);
+        }
       }
     };
     constexpr int UF = sizeof(T) == 2 ? 4 : 1;
@@ -1244,7 +1301,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int v = 4 * gq + i;
-        dsn[v] = accA[v] * s_scale + accB[v] * c_scale;
+        dsn[v] = accA[v] * s_scale + accB[v] * (c_scale * g_unscale);
         sv[v] = s4[i];
         if (d0 < D) t += sv[v] * dsn[v];
       }
@@ -1362,7 +1419,7 @@ static size_t bwd_token_lds_t(int Mp, int kind) {
   switch (kind) {
     case kBwdTokDecode: return 2 * NP * tile;
     case kBwdTokEncode: return 2 * NP * tile + stats;
-    default: return (1 + NP) * tile + stats;
+    default: return (1 + NP + (NP - 1)) * tile + stats + 16 * sizeof(float);  // seeds, G / c [, fp16]; stats; per-wave maxima
   }
 }
 
