@@ -758,8 +758,22 @@ __global__ __launch_bounds__(256) void bwd_center_kernel(BwdCenterArgs a) {
   mean /= (float)a.M;
   T* oh = reinterpret_cast<T*>(a.Zc) + (int64_t)bh * a.Mp * D;
   T* ol = reinterpret_cast<T*>(a.Zc_lo) + (int64_t)bh * a.Mp * D;
-  for (int m = r0; m < a.Mp; m += RPB)
-    store_pair<T>(oh, ol, (int64_t)m * D + d, m < a.M ? z[(int64_t)m * D + d] - mean : 0.f);
+  float mx = 0.f;
+  for (int m = r0; m < a.Mp; m += RPB) {
+    const float zc = m < a.M ? z[(int64_t)m * D + d] - mean : 0.f;
+    store_pair<T>(oh, ol, (int64_t)m * D + d, zc);
+    mx = fmaxf(mx, fabsf(zc));
+  }
+  if (a.zmax) {
+    __syncthreads();  // every thread has read part[] above
+    part[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) part[threadIdx.x] = fmaxf(part[threadIdx.x], part[threadIdx.x + w]);
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) a.zmax[bh] = part[0];
+  }
 }
 
 // Latent tensors of one (batch, head) in LDS, block-major: for every block of 32 latent rows, the
@@ -795,7 +809,11 @@ __device__ __forceinline__ void fill_stats(float* sl, float* sc, const float* l,
 //                                                     L_n = log2 sum_m 2^(l_nm),
 //                                                     c_n = sum_m 2^(l_nm - L_n) dP_nm;
 //   pass 2:  dK_dec,n = (1/sqrt(D)) sum_m P_nm (dP_nm - c_n) Q_m,  kept in fp32 for the encode kernel.
-// LDS holds c*Q and Zc (pairs).
+// LDS holds c*Q and Zc (pairs), and for bf16 c*Q in fp16 (the routing-query rows' third part).
+// bf16: the dK product takes dS and c*Q as single fp16 operands (no cancellation in that sum). dS is
+// scaled per token by a power of two 2^sh that keeps it below 2^14: |dP - c| <= 2 |dY_n|_1 max|Zc|,
+// and the factor enters at no cost through the second pass's start value -L + sh; the store takes it
+// out exactly.
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs a) {
   using F = Frag<T>;
@@ -804,10 +822,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
   constexpr int KB = D / 16;
   constexpr int NT = NW * 64;
   constexpr int NP = F::kLo ? 2 : 1;  // tiles per pair
+  constexpr bool kH = F::kLo;
 
-  // Block-major LDS (fill_blocked): per 32 latents, c*Q hi, [lo], Zc hi, [lo].
-  constexpr int NTILE = 2 * NP;
-  constexpr int TQH = 0, TQL = 1, TZH = NP, TZL = NP + 1;
+  // Block-major LDS (fill_blocked): per 32 latents, c*Q hi, [lo], Zc hi, [lo], [c*Q fp16].
+  constexpr int NTILE = 2 * NP + (kH ? 1 : 0);
+  constexpr int TQH = 0, TQL = 1, TZH = NP, TZL = NP + 1, TQ16 = 2 * NP;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
   T* tiles = reinterpret_cast<T*>(smem);
@@ -823,6 +842,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
     if constexpr (F::kLo) {
       fill_blocked<T, D, NT, NTILE>(tiles, TQL, qsrc + D, kQRow<T> * D, Mp, Mp);
       fill_blocked<T, D, NT, NTILE>(tiles, TZL, reinterpret_cast<const T*>(a.Zc_lo) + (int64_t)bh * Mp * D, D, Mp, Mp);
+      fill_blocked<T, D, NT, NTILE>(tiles, TQ16, qsrc + 2 * D, kQRow<T> * D, Mp, Mp);
     }
   }
   __syncthreads();
@@ -835,6 +855,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
   const bool ragged = (a.M & 31) != 0;
   const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
   const T* ybase = reinterpret_cast<const T*>(a.dY) + (int64_t)bh * a.N * D;
+  const float zmax = kH ? a.zmax[bh] : 0.f;
 
   for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
     const int64_t tok = base + (lane & 31);
@@ -943,12 +964,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       a.tc[(int64_t)bh * a.N + tok] = cd;
     }
 
-    // Second pass: the products start from the token's -L and -c (in every slot), so they come
-    // out as l - L and dP - c.
+    // Second pass: the products start from the token's -L (+ sh) and -c (in every slot), so they
+    // come out as l - L (+ sh) and dP - c.
+    int sh = 0;
+    if constexpr (kH) {
+      float y1 = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) y1 += fabsf((float)yb[kk][e]);
+      const float bound = 2.f * (y1 + shfl_xor(y1, 32)) * zmax;  // >= |dP - c| of the token
+      int e = 0;
+      (void)frexpf(bound, &e);  // bound < 2^e
+      sh = bound > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+    }
     f32x16 negL, negC;
 #pragma unroll
     for (int v = 0; v < 16; v++) {
-      negL[v] = -Ld;
+      negL[v] = (float)sh - Ld;
       negC[v] = -cd;
     }
     f32x16 accK = {};
@@ -960,22 +993,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       for (int v = 0; v < 16; v++) dS[v] = exp2_fast(E[v]) * dP[v];
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQL) + 16 * t * D, lofs);
-        const Pair sk = F::split(dS, t);
-        accK = mma_pp<F>(qk, sk, accK);
-        hold<F>(accK, qk);
-        hold<F>(accK, sk);
+        if constexpr (kH) {
+          const Op qk = F::template krows_at<D>(tile(lb, TQ16) + 16 * t * D, lofs);
+          f16x8 sk;
+#pragma unroll
+          for (int e = 0; e < 8; e++) sk[e] = (f16)dS[8 * t + e];
+          accK = mfma_32x32_f16(__builtin_bit_cast(f16x8, qk), sk, accK);
+          hold(accK, qk);
+          hold(accK, sk);
+        } else {
+          const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQL) + 16 * t * D, lofs);
+          const Pair sk = F::split(dS, t);
+          accK = mma_pp<F>(qk, sk, accK);
+          hold<F>(accK, qk);
+          hold<F>(accK, sk);
+        }
       }
     });
     if (valid) {
-      // dK_dec = (1/sqrt(D)) dS Q = ln 2 * dS (c*Q); slot v holds dim row32(v, l / 32).
+      // dK_dec = (1/sqrt(D)) dS Q = ln 2 * dS (c*Q), less the factor 2^sh; slot v holds dim
+      // row32(v, l / 32).
+      const float os = ldexpf(kLn2, -sh);
       float* dk = a.dKdec + ((int64_t)bh * a.N + base) * D;
 #pragma unroll
       for (int gq = 0; gq < 4; gq++) {
         const int d0 = row32(4 * gq, hh);
         if (d0 < D)
-          *reinterpret_cast<f32x4*>(dk + (lane & 31) * D + d0) = f32x4{accK[4 * gq] * kLn2, accK[4 * gq + 1] * kLn2,
-                                                    accK[4 * gq + 2] * kLn2, accK[4 * gq + 3] * kLn2};
+          *reinterpret_cast<f32x4*>(dk + (lane & 31) * D + d0) = f32x4{accK[4 * gq] * os, accK[4 * gq + 1] * os,
+                                                    accK[4 * gq + 2] * os, accK[4 * gq + 3] * os};
       }
     }
   }
@@ -1417,7 +1462,7 @@ static size_t bwd_token_lds_t(int Mp, int kind) {
   constexpr size_t NP = sizeof(T) == 2 ? 2 : 1;  // tiles per pair
   const size_t tile = (size_t)Mp * D * sizeof(T), stats = 2 * (size_t)Mp * sizeof(float);
   switch (kind) {
-    case kBwdTokDecode: return 2 * NP * tile;
+    case kBwdTokDecode: return (2 * NP + (NP - 1)) * tile;  // bf16: c*Q in fp16 as well
     case kBwdTokEncode: return 2 * NP * tile + stats;
     default: return (1 + NP + (NP - 1)) * tile + stats + 16 * sizeof(float);  // seeds, G / c [, fp16]; stats; per-wave maxima
   }

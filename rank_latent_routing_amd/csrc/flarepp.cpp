@@ -465,6 +465,7 @@ struct BwdPlan {
   size_t off_qd = 0, off_z32 = 0, off_lsyn = 0, off_lenc = 0, off_zc = 0, off_zc_lo = 0, off_ldec = 0;
   size_t off_cd = 0, off_dkdec = 0, off_p0 = 0, off_p1 = 0, off_dz32 = 0, off_dzop = 0, off_dzop_lo = 0;
   size_t off_ce = 0, off_dqdec = 0, off_dqf = 0, off_gop = 0, off_gop_lo = 0, off_cs = 0, off_rowdot = 0;
+  size_t off_zmax = 0;
   size_t total = 0;
 };
 
@@ -528,6 +529,7 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.off_gop_lo = off; off = align256(off + lat * D * es);
   p.off_cs = off;     off = align256(off + lat * 4);
   p.off_rowdot = off; off = align256(off + lat * 4);
+  p.off_zmax = off;   off = align256(off + (size_t)BH * 4);
   p.total = off;
   return p;
 }
@@ -579,13 +581,14 @@ int enqueue_backward_from_saved(const void* K, const void* V, const void* S, con
   float* dkdec = dtype == FLAREPP_BF16 ? F(p.off_dkdec) : static_cast<float*>(dK);
 
   flarepp::BwdCenterArgs ca{};
-  ca.Z32 = F(p.off_z32); ca.Zc = w + p.off_zc; ca.Zc_lo = w + p.off_zc_lo; ca.M = M; ca.Mp = p.Mp;
+  ca.Z32 = F(p.off_z32); ca.Zc = w + p.off_zc; ca.Zc_lo = w + p.off_zc_lo; ca.zmax = F(p.off_zmax); ca.M = M;
+  ca.Mp = p.Mp;
   if (run_kernel(6, st, [&] { return flarepp::launch_bwd_center(ca, dtype, D, BH, st); }) != hipSuccess)
     return FLAREPP_LAUNCH_FAILED;
 
   flarepp::BwdTokenArgs ta{};
   ta.K = K; ta.V = V; ta.dY = dY; ta.S = S; ta.tl = ldec; ta.tc = cd; ta.dKdec = dkdec; ta.Qrows = qrows;
-  ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
+  ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.zmax = F(p.off_zmax); ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
   ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
   ta.lsyn = sv.lsyn; ta.cs = F(p.off_cs); ta.dK = dK; ta.dV = dV; ta.dS = dS; ta.N = N;
   ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H; ta.force_exact = g_force_exact.load() ? 1 : 0;

@@ -157,6 +157,7 @@ struct BwdTokenArgs {
   float* dKdec;          // [BH][N][D] fp32: the decode call's dK (written by decode, read by encode)
   const void* Qrows;     // c*Q workspace rows [BH][Mp][R*D] (hi, lo parts)
   const void* Zc; const void* Zc_lo;      // [BH][Mp][D] dtype: Z minus its mean over latents
+  const float* zmax;                      // [BH] largest |Zc| element (bf16 decode's dK product)
   const void* dZop; const void* dZ_lo;    // [BH][Mp][D] dtype
   const float* lenc; const float* ce;     // [BH][Mp]
   const void* Qseed;                      // [H][M][D] dtype
@@ -176,6 +177,7 @@ struct BwdCenterArgs {
   const float* Z32;  // [BH][M][D]
   void* Zc;          // [BH][Mp][D] dtype hi part (rows >= M zero)
   void* Zc_lo;       // lo part
+  float* zmax;       // optional [BH]: the largest |Zc| element
   int M, Mp;
 };
 
