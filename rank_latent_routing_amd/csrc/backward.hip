@@ -1031,7 +1031,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
 //   dK_n = dK_dec,n + (1/sqrt(D)) sum_m P_mn (dP_mn - c_m) Q_m,   dV_n = sum_m P_mn dZ_m.
 // LDS holds c*Q and dZ (pairs) and the per-latent L and c. Score tiles are C[latent][token]
 // (lane = token); the products over latents are computed transposed, R[d][token], so that each lane
-// ends with 16 dims of its own token.
+// ends with 16 dims of its own token. fp32 runs this kernel; bf16 runs bwd_token_encode_h_kernel
+// below.
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs a) {
   using F = Frag<T>;
@@ -1150,6 +1151,271 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
           store4<T>(dk + d0, kd[0] + accK[4 * gq] * kLn2, kd[1] + accK[4 * gq + 1] * kLn2,
                     kd[2] + accK[4 * gq + 2] * kLn2, kd[3] + accK[4 * gq + 3] * kLn2);
           store4<T>(dv + d0, accV[4 * gq], accV[4 * gq + 1], accV[4 * gq + 2], accV[4 * gq + 3]);
+        }
+      }
+    }
+  }
+}
+
+// The encode call's token-side cotangents for bf16 inputs, with fp16 operands in place of the bf16
+// pairs of the kernel above. fp16's 11 significant bits against bf16's 8 let single values replace
+// pairs in the two products that sum over latents, and the fp16 pairs (22 bits) carry the score and
+// dP products at the pairs' accuracy, so the four latent tiles fit in LDS as before:
+//   c*Q as an fp16 pair: the workspace's bf16 pair hi + lo is exact in fp32 and splits exactly into
+//     fp16 hi + lo, so the logits equal those of the recomputed forward (whose normalizers L are
+//     used here) up to the order of the fp32 sums. The hi part alone is the dK product's operand.
+//   dZ as an fp16 pair, scaled per (batch, head) by 2^g so that its largest element lies in
+//     (2^13, 2^14]; c_m = <dZ_m, Z_m> is formed here from that pair, so that dP - c sees the very
+//     operands of dP. The hi part alone is the dV product's operand.
+//   K and V in fp16, exact for bf16 values of magnitude in [2^-14, 2^15). A 32-token group whose
+//     largest |K| or |V| lies beyond 2^15 (or whose V all lie below 2^-6) takes them scaled by a power
+//     of two and undoes the scale on the products (a wave-uniform branch, not taken by ordinary data).
+//   P in fp16 as 2^14 P (the score product starts from 14 - L), at most 2^14.
+//   dS in fp16, scaled per token by a power of two 2^sh that keeps it below 2^14, from the bound
+//     |dP - c| = |dZ_m . (V_n - Z_m)| <= max_m |dZ_m|_1 (max |V_n| + max |Z|).
+// The products over latents take one MFMA each per 32x32x16 step (three with pairs) and the pairs'
+// splits are gone; the stores take the scale factors out exactly.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_token_encode_h_kernel(BwdTokenArgs a) {
+  using F = Frag<bf16>;
+  using Op = typename F::Op;
+  constexpr int KB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 8;
+  using Sw = Swz<bf16, D>;
+
+  // Block-major LDS: per 32 latents, c*Q hi, c*Q lo, 2^g dZ hi, 2^g dZ lo (fp16); then the stats
+  // (14 - L and -2^g c, stat_pos order) and per-wave maxima.
+  constexpr int NTILE = 4;
+  constexpr int TQH = 0, TQL = 1, TZH = 2, TZL = 3;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;
+  f16* tiles = reinterpret_cast<f16*>(smem);
+  float* sl = reinterpret_cast<float*>(tiles + NTILE * Mp * D);  // [Mp]
+  float* sc = sl + Mp;                                            // [Mp]
+  float* red = sc + Mp;                                           // [3][16]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int bh = blockIdx.y;
+  auto tile = [&](int lb, int j) __attribute__((always_inline)) { return tiles + (lb * NTILE + j) * 32 * D; };
+  auto tile_at = [&](int row, int j, int part) __attribute__((always_inline)) {
+    return tiles + ((row >> 5) * NTILE + j) * 32 * D + Sw::off(row & 31, part * 8);
+  };
+  auto block_max = [&](float v, int slot) __attribute__((always_inline)) {
+    v = wave_max(v);
+    if (lane == 0) red[16 * slot + wave] = v;
+    __syncthreads();
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) m = fmaxf(m, red[16 * slot + w]);
+    return m;
+  };
+  // Power of two 2^s with x 2^s < 2^14 (x > 0), clamped to the fp32 range of the factors.
+  auto scale_exp = [](float x) __attribute__((always_inline)) {
+    int e = 0;
+    (void)frexpf(x, &e);  // x < 2^e
+    return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+  };
+
+  const float* dz = a.dZ32 + (int64_t)bh * Mp * D;
+  const float* zz = a.Z32 + (int64_t)bh * a.M * D;
+  int g = 0;
+  float A1 = 0.f, ZM = 0.f;
+  {
+    const bf16* qsrc = reinterpret_cast<const bf16*>(a.Qrows) + (int64_t)bh * Mp * kQRow<bf16> * D;
+    for (int q = tid; q < Mp * CPR; q += NT) {
+      const int row = q / CPR, part = q % CPR;
+      const bf16* r = qsrc + (int64_t)row * kQRow<bf16> * D + part * 8;
+      float hv[8], lv[8];
+      chunk_to_float<bf16>(*reinterpret_cast<const Chunk*>(r), hv);
+      chunk_to_float<bf16>(*reinterpret_cast<const Chunk*>(r + D), lv);
+      f16x8 oh, ol;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float v = hv[e] + lv[e];
+        const f16 h = (f16)v;
+        oh[e] = h;
+        ol[e] = (f16)(v - (float)h);
+      }
+      *reinterpret_cast<f16x8*>(tile_at(row, TQH, part)) = oh;
+      *reinterpret_cast<f16x8*>(tile_at(row, TQL, part)) = ol;
+    }
+    float mx = 0.f;
+    for (int i = tid; i < a.M * D; i += NT) mx = fmaxf(mx, fabsf(dz[i]));
+    g = scale_exp(block_max(mx, 0));
+    const float gs = ldexpf(1.f, g);
+    float a1 = 0.f, zm = 0.f;
+    for (int row = tid; row < Mp; row += NT) {
+      const bool valid = row < a.M;
+      float c = 0.f, n1 = 0.f;
+#pragma unroll
+      for (int part = 0; part < CPR; part++) {
+        f16x8 oh, ol;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int d = 8 * part + e;
+          const float v = valid ? dz[(int64_t)row * D + d] * gs : 0.f;
+          const f16 h = (f16)v, l = (f16)(v - (float)h);
+          oh[e] = h;
+          ol[e] = l;
+          const float pv = (float)h + (float)l;
+          const float zv = valid ? zz[(int64_t)row * D + d] : 0.f;
+          c += pv * zv;
+          n1 += fabsf(pv);
+          zm = fmaxf(zm, fabsf(zv));
+        }
+        *reinterpret_cast<f16x8*>(tile_at(row, TZH, part)) = oh;
+        *reinterpret_cast<f16x8*>(tile_at(row, TZL, part)) = ol;
+      }
+      a1 = fmaxf(a1, n1);
+      const int p = stat_pos(row);
+      sl[p] = 14.f - a.lenc[(int64_t)bh * Mp + row];
+      sc[p] = -c;
+    }
+    A1 = block_max(a1, 1);
+    ZM = block_max(zm, 2);
+  }
+  __syncthreads();
+  const LaneOffs<bf16, D> lofs = lane_offsets<bf16, D>(lane);
+  auto row16 = [&](int lb, int j, int kk) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x8, F::template row_at<D>(reinterpret_cast<const bf16*>(tile(lb, j)), lofs, kk));
+  };
+  auto krows16 = [&](int lb, int j, int t) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x8, F::template krows_at<D>(reinterpret_cast<const bf16*>(tile(lb, j) + 16 * t * D), lofs));
+  };
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const int nlb = Mp / 32;
+  const bf16* kbase = reinterpret_cast<const bf16*>(a.K) + (int64_t)bh * a.N * D;
+  const bf16* vbase = reinterpret_cast<const bf16*>(a.V) + (int64_t)bh * a.N * D;
+  const float bound0 = 16384.f * A1;  // 2^14 max_m |2^g dZ_m|_1
+
+  for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
+    const int64_t tok = base + (lane & 31);
+    const bool valid = tok < t_end;
+    float kx[KB][8], vx[KB][8];
+    float kmx = 0.f, vmx = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      const int64_t o = tok * D + 16 * kk + 8 * hh;
+      F::to_float(valid ? F::gload(kbase + o) : F::zero(), kx[kk]);
+      F::to_float(valid ? F::gload(vbase + o) : F::zero(), vx[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        kmx = fmaxf(kmx, fabsf(kx[kk][e]));
+        vmx = fmaxf(vmx, fabsf(vx[kk][e]));
+      }
+    }
+    vmx = fmaxf(vmx, shfl_xor(vmx, 32));  // the token's largest |V|
+    // Wave-uniform scales of K and V (1 unless the group's values leave fp16's exact range).
+    const float wk = wave_max(kmx), wv = wave_max(vmx);
+    const int ek = wk >= 32768.f ? scale_exp(wk) : 0;
+    const int ev = (wv >= 32768.f || (wv > 0.f && wv < 0x1p-6f)) ? scale_exp(wv) : 0;
+    const bool rare = (ek | ev) != 0;
+    const float fk = ldexpf(1.f, ek), fv = ldexpf(1.f, ev);
+    if (rare) {
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          kx[kk][e] *= fk;
+          vx[kk][e] *= fv;
+        }
+    }
+    f16x8 k16[KB], v16[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        k16[kk][e] = (f16)kx[kk][e];
+        v16[kk][e] = (f16)vx[kk][e];
+      }
+    const int sh = scale_exp(bound0 * (vmx + ZM));
+    const float dsc = ldexpf(1.f, sh);
+    const float ifk = ldexpf(1.f, -ek), ifv = ldexpf(1.f, -ev);
+
+    f32x16 accK = {}, accV = {};
+    auto block = [&](int lb) __attribute__((always_inline)) {
+      f16x8 qh[KB], ql[KB], zh[KB], zl[KB];
+      // The products start from 14 - L and -2^g c: E = l - L + 14, dP = 2^g (dP - c). With K or V
+      // scaled by 2^ek or 2^ev, so are their start values, and the results are scaled back.
+      f32x16 E = load_stats16(sl + 32 * lb, hh), dP = load_stats16(sc + 32 * lb, hh);
+      if (rare) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          E[v] *= fk;
+          dP[v] *= fv;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        qh[kk] = row16(lb, TQH, kk);
+        ql[kk] = row16(lb, TQL, kk);
+        zh[kk] = row16(lb, TZH, kk);
+        zl[kk] = row16(lb, TZL, kk);
+        E = mfma_32x32_f16(ql[kk], k16[kk], E);
+        E = mfma_32x32_f16(qh[kk], k16[kk], E);
+        dP = mfma_32x32_f16(zl[kk], v16[kk], dP);
+        dP = mfma_32x32_f16(zh[kk], v16[kk], dP);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        hold(E, qh[kk]);
+        hold(E, ql[kk]);
+        hold(E, k16[kk]);
+        hold(dP, zh[kk]);
+        hold(dP, zl[kk]);
+        hold(dP, v16[kk]);
+      }
+      if (rare) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          E[v] *= ifk;
+          dP[v] *= ifv;
+        }
+      }
+      f16x8 pk[2], sk[2];
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const float p = exp2_fast(E[v]);  // 2^14 P
+        pk[v >> 3][v & 7] = (f16)p;
+        sk[v >> 3][v & 7] = (f16)(p * dP[v] * dsc);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const f16x8 qk = krows16(lb, TQH, t);
+        accK = mfma_32x32_f16(qk, sk[t], accK);
+        hold(accK, qk);
+        hold(accK, sk[t]);
+        const f16x8 zk = krows16(lb, TZH, t);
+        accV = mfma_32x32_f16(zk, pk[t], accV);
+        hold(accV, zk);
+        hold(accV, pk[t]);
+      }
+    };
+    int lb = 0;
+    for (; lb + 4 <= nlb; lb += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) block(lb + u);
+    }
+    for (; lb < nlb; lb++) block(lb);
+    if (valid) {
+      // dK = dK_dec + ln 2 * dS (c*Q) and dV = P^T dZ, less the factors 2^(14 + g + sh) and 2^(14 + g).
+      const float ok = ldexpf(kLn2, -(14 + g + sh)), ov = ldexpf(1.f, -(14 + g));
+      const int64_t to = ((int64_t)bh * a.N + tok) * D;
+      bf16* dk = reinterpret_cast<bf16*>(a.dK) + to;
+      bf16* dv = reinterpret_cast<bf16*>(a.dV) + to;
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int d0 = row32(4 * gq, hh);
+        if (d0 < D) {
+          const f32x4 kd = *reinterpret_cast<const f32x4*>(a.dKdec + to + d0);
+          store4<bf16>(dk + d0, kd[0] + accK[4 * gq] * ok, kd[1] + accK[4 * gq + 1] * ok,
+                       kd[2] + accK[4 * gq + 2] * ok, kd[3] + accK[4 * gq + 3] * ok);
+          store4<bf16>(dv + d0, accV[4 * gq] * ov, accV[4 * gq + 1] * ov, accV[4 * gq + 2] * ov,
+                       accV[4 * gq + 3] * ov);
         }
       }
     }
@@ -1463,7 +1729,7 @@ static size_t bwd_token_lds_t(int Mp, int kind) {
   const size_t tile = (size_t)Mp * D * sizeof(T), stats = 2 * (size_t)Mp * sizeof(float);
   switch (kind) {
     case kBwdTokDecode: return (2 * NP + (NP - 1)) * tile;  // bf16: c*Q in fp16 as well
-    case kBwdTokEncode: return 2 * NP * tile + stats;
+    case kBwdTokEncode: return 2 * NP * tile + stats + (sizeof(T) == 2 ? 48 * sizeof(float) : 0);  // bf16: per-wave maxima
     default: return (1 + NP + (NP - 1)) * tile + stats + 16 * sizeof(float);  // seeds, G / c [, fp16]; stats; per-wave maxima
   }
 }
@@ -1488,7 +1754,9 @@ static hipError_t launch_bwd_token_t(const BwdTokenArgs& a, int kind, int gx, in
       // fp32 with 32 channels has no 12-wave instance (it would spill): it runs 8.
       if constexpr (std::is_same<T, float>::value && D == 32 && NW == 12) return hipErrorInvalidValue;
       else return go(bwd_token_decode_kernel<T, D, NW>, NW);
-    case kBwdTokEncode: return go(bwd_token_encode_kernel<T, D, NW>, NW);
+    case kBwdTokEncode:
+      if constexpr (sizeof(T) == 2) return go(bwd_token_encode_h_kernel<D, NW>, NW);
+      else return go(bwd_token_encode_kernel<T, D, NW>, NW);
     default: return go(bwd_token_synthesis_kernel<T, D, NW>, NW);
   }
 }

@@ -589,7 +589,7 @@ int enqueue_backward_from_saved(const void* K, const void* V, const void* S, con
   flarepp::BwdTokenArgs ta{};
   ta.K = K; ta.V = V; ta.dY = dY; ta.S = S; ta.tl = ldec; ta.tc = cd; ta.dKdec = dkdec; ta.Qrows = qrows;
   ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.zmax = F(p.off_zmax); ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
-  ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
+  ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.dZ32 = F(p.off_dz32); ta.Z32 = F(p.off_z32); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
   ta.lsyn = sv.lsyn; ta.cs = F(p.off_cs); ta.dK = dK; ta.dV = dV; ta.dS = dS; ta.N = N;
   ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H; ta.force_exact = g_force_exact.load() ? 1 : 0;
   if (run_kernel(7, st, [&] { return flarepp::launch_bwd_token(ta, dtype, D, flarepp::kBwdTokDecode, p.tok_dec_nw, p.tok_gx, BH, st); }) != hipSuccess)

@@ -160,6 +160,8 @@ struct BwdTokenArgs {
   const float* zmax;                      // [BH] largest |Zc| element (bf16 decode's dK product)
   const void* dZop; const void* dZ_lo;    // [BH][Mp][D] dtype
   const float* lenc; const float* ce;     // [BH][Mp]
+  const float* dZ32;                      // [BH][Mp][D] fp32 dZ (bf16 encode kernel's fp16 operands)
+  const float* Z32;                       // [BH][M][D] fp32 Z of the forward
   const void* Qseed;                      // [H][M][D] dtype
   const void* Gop; const void* G_lo;      // [BH][Mp][D] dtype: G / c
   const float* lsyn; const float* cs;     // [BH][Mp]

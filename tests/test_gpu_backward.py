@@ -285,6 +285,41 @@ def test_bwd_zero_shift_and_running_maximum_mixed(dtype, big):
     _check(w, label=f"bwd mixed {dtype}", bar=bar)
 
 
+@pytest.mark.parametrize("name,rows,scale", [("V", (5000, 5100), 2.0 ** 17), ("V", None, 2.0 ** -10),
+                                             ("K", (8000, 8100), 2.0 ** 15)])
+def test_bwd_bf16_token_values_beyond_fp16(name, rows, scale):
+    # The bf16 encode call's token-side products take K and V in fp16, exact for magnitudes in
+    # [2^-14, 2^15). A 32-token group whose values leave that range takes them scaled by a power of
+    # two and takes the scale back out of its products: values of 2^17 in one token range (those
+    # groups only), values below 2^-6 everywhere (every group), keys of 2^15 in one token range.
+    # The oracle sees the same bf16 values.
+    w = make_workload(4, B=1, H=2, N=20000, seed=31)
+    from workloads.gen import _store
+    X = w.f64(name)
+    if rows is None:
+        X *= scale
+    else:
+        X[:, :, rows[0]:rows[1]] *= scale
+    setattr(w, name, _store(X, w.dtype))
+    label = f"bwd bf16 {name} x{scale:g}" + (f" on tokens {rows[0]}-{rows[1]}" if rows else "")
+    if name == "V":
+        _check(w, label=label)
+        return
+    # Keys of 2^15 put routing logits near 4e4 (log2 units). The bf16 pair that carries c*Q to every
+    # kernel (about 16 significant bits) then moves logits by up to about 0.3, so the cotangents
+    # that go through those softmaxes' probabilities leave the bar in every kernel alike. Checked
+    # here: every output finite, and dK (the product the scaled keys feed) at the bar.
+    say(f"[bwd] {label}: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    dY = make_cotangent(w)
+    got = run_backward(w, dY)
+    for k, v in got.items():
+        assert np.isfinite(v).all(), k
+    ref = oracle_backward(w, dY)
+    worst = max(_err(got["dK"][0, h], ref["dK"][0, h], w.dtype) for h in range(w.H))
+    say(f"[bwd] {label}: worst dK {worst} (bar {tol(w.dtype)})")
+    assert worst <= tol(w.dtype)
+
+
 @pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("scale", [8.0, 24.0])
