@@ -35,7 +35,10 @@
 // synthesis call's as <G, Qd> likewise), and the recomputed forward takes the exact hi/lo path, so
 // that its normalizers match the logits computed here; its P.V products take P (and the synthesis
 // values N0(S)) as pairs too, so that Z and Qd, and with them those c, are as exact as the products
-// here.
+// here. The token-side kernels of bf16 runs take fp16 instead (11 significant bits against bf16's
+// 8) where a product over latents carries no cancellation: single fp16 operands, scaled by powers
+// of two into fp16's range, and fp16 pairs (about 22 bits) in place of the bf16 pairs elsewhere, so
+// that their latent tensors still fit in LDS (see each kernel).
 //
 // Layout of the 32x32x16 MFMA C[i][j] += sum_k A[i][k] B[k][j]: lane l supplies row l % 32 of A and
 // column l % 32 of B with k = 8 (l / 32) + e (e = 0..7) and receives column l % 32, rows
@@ -1035,16 +1038,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
 // below.
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs a) {
+  static_assert(sizeof(T) == 4, "bf16 runs bwd_token_encode_h_kernel");
   using F = Frag<T>;
   using Op = typename F::Op;
   using Pair = typename F::Pair;
   constexpr int KB = D / 16;
   constexpr int NT = NW * 64;
-  constexpr int NP = F::kLo ? 2 : 1;
 
-  // Block-major LDS (fill_blocked): per 32 latents, c*Q hi, [lo], dZ hi, [lo]; then the stats.
-  constexpr int NTILE = 2 * NP;
-  constexpr int TQH = 0, TQL = 1, TZH = NP, TZL = NP + 1;
+  // Block-major LDS (fill_blocked): per 32 latents, c*Q and dZ; then the stats.
+  constexpr int NTILE = 2;
+  constexpr int TQH = 0, TZH = 1;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
   T* tiles = reinterpret_cast<T*>(smem);
@@ -1058,10 +1061,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
     const T* qsrc = reinterpret_cast<const T*>(a.Qrows) + (int64_t)bh * Mp * kQRow<T> * D;
     fill_blocked<T, D, NT, NTILE>(tiles, TQH, qsrc, kQRow<T> * D, Mp, Mp);
     fill_blocked<T, D, NT, NTILE>(tiles, TZH, reinterpret_cast<const T*>(a.dZop) + (int64_t)bh * Mp * D, D, Mp, Mp);
-    if constexpr (F::kLo) {
-      fill_blocked<T, D, NT, NTILE>(tiles, TQL, qsrc + D, kQRow<T> * D, Mp, Mp);
-      fill_blocked<T, D, NT, NTILE>(tiles, TZL, reinterpret_cast<const T*>(a.dZ_lo) + (int64_t)bh * Mp * D, D, Mp, Mp);
-    }
     fill_stats<NT>(sl, sc, a.lenc + (int64_t)bh * Mp, a.ce + (int64_t)bh * Mp, Mp);
   }
   __syncthreads();
@@ -1085,8 +1084,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
       vb[kk] = valid ? F::gload(vbase + o) : F::zero();
     }
     f32x16 accK = {}, accV = {};
-    // One latent block; the loop below runs four per iteration (bf16), so that the LDS reads of the
-    // second to fourth address their tiles by the instructions' immediate offsets.
+    // One latent block.
     auto block = [&](int lb) __attribute__((always_inline)) {
       Pair qa[KB], za[KB];
       // Latents past M: zero rows of c*Q and dZ, L = +inf, c = 0, so P and dS vanish there. The
@@ -1094,8 +1092,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
       f32x16 E = load_stats16(sl + 32 * lb, hh), dP = load_stats16(sc + 32 * lb, hh);
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
-        qa[kk] = row_pair_at<F, D>(tile(lb, TQH), tile(lb, TQL), lofs, kk);
-        za[kk] = row_pair_at<F, D>(tile(lb, TZH), tile(lb, TZL), lofs, kk);
+        qa[kk] = row_pair_at<F, D>(tile(lb, TQH), tile(lb, TQH), lofs, kk);
+        za[kk] = row_pair_at<F, D>(tile(lb, TZH), tile(lb, TZH), lofs, kk);
         E = mma_pe<F>(qa[kk], kb[kk], E);
         dP = mma_pe<F>(za[kk], vb[kk], dP);
       }
@@ -1115,29 +1113,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_kernel(BwdTokenArgs 
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQL) + 16 * t * D, lofs);
+        const Pair qk = krows_pair_at<F, D>(tile(lb, TQH) + 16 * t * D, tile(lb, TQH) + 16 * t * D, lofs);
         const Pair sk = F::split(dS, t);
         accK = mma_pp<F>(qk, sk, accK);
         hold<F>(accK, qk);
         hold<F>(accK, sk);
-        const Pair zk = krows_pair_at<F, D>(tile(lb, TZH) + 16 * t * D, tile(lb, TZL) + 16 * t * D, lofs);
+        const Pair zk = krows_pair_at<F, D>(tile(lb, TZH) + 16 * t * D, tile(lb, TZH) + 16 * t * D, lofs);
         const Pair pk = F::split(P, t);
         accV = mma_pp<F>(zk, pk, accV);
         hold<F>(accV, zk);
         hold<F>(accV, pk);
       }
     };
-    constexpr int UF = sizeof(T) == 2 ? 4 : 1;  // fp32 operands leave no registers for it
-    if constexpr (UF > 1) {
-      int lb = 0;
-      for (; lb + UF <= nlb; lb += UF) {
-#pragma unroll
-        for (int u = 0; u < UF; u++) block(lb + u);
-      }
-      for (; lb < nlb; lb++) block(lb);
-    } else {
-      for (int lb = 0; lb < nlb; lb++) block(lb);
-    }
+    for (int lb = 0; lb < nlb; lb++) block(lb);
     if (valid) {
       // dK = dK_dec + (1/sqrt(D)) dS Q = dK_dec + ln 2 * dS (c*Q).
       const int64_t to = ((int64_t)bh * a.N + tok) * D;
@@ -1426,81 +1414,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_h_kernel(BwdTokenArg
 // normalized keys Sn = N0(S) as keys and values,
 //   dSn_n = (1/sqrt(D)) sum_m dS[m][n] Qseed_m + sum_m P[m][n] G_m,   dS = N0'(S)^T dSn,
 // where N0'(s)^T u = r u - r^3 s mean(s * u), r = (mean(s^2) + eps)^(-1/2). LDS holds the seeds, G / c
-// and the per-latent L and c of the call.
-// bf16: sum_m P G enters the matrix unit as one fp16 product, P (<= 1) against G / c scaled by a
-// power of two per (batch, head) so that its largest element lies in (2^13, 2^14]; the end takes the
-// factor out exactly. dP = G . c Sn keeps both as bf16 pairs: near a one-hot row, dP - c is a
-// difference of nearly equal terms, and fp16 there put dS at the bar with seeds x6.
+// and the per-latent L and c of the call. fp32 runs this kernel; bf16 runs
+// bwd_token_synthesis_h_kernel below.
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenArgs a) {
+  static_assert(sizeof(T) == 4, "bf16 runs bwd_token_synthesis_h_kernel");
   using F = Frag<T>;
   using Op = typename F::Op;
   using Pair = typename F::Pair;
   constexpr int KB = D / 16;
   constexpr int NT = NW * 64;
-  constexpr int NP = F::kLo ? 2 : 1;
 
-  // Block-major LDS (fill_blocked): per 32 latents, the seeds (rows >= M zero), G / c hi, [lo], [G / c
-  // in fp16, scaled]; then the stats.
-  constexpr bool kH = F::kLo;
-  constexpr int NTILE = kH ? 4 : 2;
-  constexpr int TQS = 0, TGH = 1, TGL = 2, TG16 = 3;
+  // Block-major LDS (fill_blocked): per 32 latents, the seeds (rows >= M zero) and G / c; then the
+  // stats.
+  constexpr int NTILE = 2;
+  constexpr int TQS = 0, TGH = 1;
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mp = a.Mp;
   T* tiles = reinterpret_cast<T*>(smem);
   float* sl = reinterpret_cast<float*>(tiles + NTILE * Mp * D);  // [Mp] L_syn, stat_pos order
   float* sc = sl + Mp;                                            // [Mp] c_syn
-  float* gred = sc + Mp;                                          // [NW] (bf16)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int bh = blockIdx.y, h = bh % a.H;
-  float g_unscale = 1.f;  // bf16: 2^-e, with G / c scaled by 2^e
   {
     fill_blocked<T, D, NT, NTILE>(tiles, TQS, reinterpret_cast<const T*>(a.Qseed) + (int64_t)h * a.M * D, D, a.M, Mp);
-    const T* gh = reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D;
-    fill_blocked<T, D, NT, NTILE>(tiles, TGH, gh, D, Mp, Mp);
+    fill_blocked<T, D, NT, NTILE>(tiles, TGH, reinterpret_cast<const T*>(a.Gop) + (int64_t)bh * Mp * D, D, Mp, Mp);
     fill_stats<NT>(sl, sc, a.lsyn + (int64_t)bh * Mp, a.cs + (int64_t)bh * Mp, Mp);
-    if constexpr (kH) {
-      constexpr int CPR = D / 8;
-      const T* gl = reinterpret_cast<const T*>(a.G_lo) + (int64_t)bh * Mp * D;
-      fill_blocked<T, D, NT, NTILE>(tiles, TGL, gl, D, Mp, Mp);
-      auto chunk_vals = [&](int q, float* v) __attribute__((always_inline)) {
-        float hv[8], lv[8];
-        chunk_to_float<T>(*reinterpret_cast<const Chunk*>(gh + q * 8), hv);
-        chunk_to_float<T>(*reinterpret_cast<const Chunk*>(gl + q * 8), lv);
-#pragma unroll
-        for (int e = 0; e < 8; e++) v[e] = hv[e] + lv[e];
-      };
-      float mx = 0.f;
-      for (int q = tid; q < Mp * CPR; q += NT) {
-        float v[8];
-        chunk_vals(q, v);
-#pragma unroll
-        for (int e = 0; e < 8; e++) mx = fmaxf(mx, fabsf(v[e]));
-      }
-      mx = wave_max(mx);
-      if (lane == 0) gred[wave] = mx;
-      __syncthreads();
-      mx = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; w++) mx = fmaxf(mx, gred[w]);
-      int e = 0;
-      (void)frexpf(mx, &e);  // mx < 2^e
-      const int sh = mx > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
-      const float g_scale = ldexpf(1.f, sh);
-      g_unscale = ldexpf(1.f, -sh);
-      using Sw = Swz<T, D>;
-      for (int q = tid; q < Mp * CPR; q += NT) {
-        const int row = q / CPR, part = q % CPR;
-        float v[8];
-        chunk_vals(q, v);
-        f16x8 o;
-#pragma unroll
-        for (int i = 0; i < 8; i++) o[i] = (f16)(v[i] * g_scale);
-        *reinterpret_cast<f16x8*>(tiles + ((row >> 5) * NTILE + TG16) * 32 * D + Sw::off(row & 31, part * 8)) = o;
-      }
-    }
   }
   __syncthreads();
   const LaneOffs<T, D> lofs = lane_offsets<T, D>(lane);
@@ -1537,7 +1478,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
       sb[kk] = F::split8(y);
     }
     f32x16 accA = {}, accB = {};
-    // One latent block; four per loop iteration for bf16, as in the encode kernel.
+    // One latent block.
     auto block = [&](int lb) __attribute__((always_inline)) {
       Op qa[KB];
       Pair ga[KB];
@@ -1546,7 +1487,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
 #pragma unroll
       for (int kk = 0; kk < KB; kk++) {
         qa[kk] = F::template row_at<D>(tile(lb, TQS), lofs, kk);
-        ga[kk] = row_pair_at<F, D>(tile(lb, TGH), tile(lb, TGL), lofs, kk);
+        ga[kk] = row_pair_at<F, D>(tile(lb, TGH), tile(lb, TGH), lofs, kk);
         A = mma_ep<F>(qa[kk], sb[kk], A);
         dP = mma_pp<F>(ga[kk], sb[kk], dP);
       }
@@ -1571,34 +1512,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
         accA = mma_ep<F>(qk, sk, accA);
         hold(accA, qk);
         hold<F>(accA, sk);
-        if constexpr (kH) {
-          const Op gk = F::template krows_at<D>(tile(lb, TG16) + 16 * t * D, lofs);
-          f16x8 pk;
-#pragma unroll
-          for (int e = 0; e < 8; e++) pk[e] = (f16)P[8 * t + e];
-          accB = mfma_32x32_f16(__builtin_bit_cast(f16x8, gk), pk, accB);
-          hold(accB, gk);
-          hold(accB, pk);
-        } else {
-          const Pair gk = krows_pair_at<F, D>(tile(lb, TGH) + 16 * t * D, tile(lb, TGL) + 16 * t * D, lofs);
-          const Pair pk = F::split(P, t);
-          accB = mma_pp<F>(gk, pk, accB);
-          hold<F>(accB, gk);
-          hold<F>(accB, pk);
-        }
+        const Pair gk = krows_pair_at<F, D>(tile(lb, TGH) + 16 * t * D, tile(lb, TGH) + 16 * t * D, lofs);
+        const Pair pk = F::split(P, t);
+        accB = mma_pp<F>(gk, pk, accB);
+        hold<F>(accB, gk);
+        hold<F>(accB, pk);
       }
     };
-    constexpr int UF = sizeof(T) == 2 ? 4 : 1;
-    if constexpr (UF > 1) {
-      int lb = 0;
-      for (; lb + UF <= nlb; lb += UF) {
-#pragma unroll
-        for (int u = 0; u < UF; u++) block(lb + u);
-      }
-      for (; lb < nlb; lb++) block(lb);
-    } else {
-      for (int lb = 0; lb < nlb; lb++) block(lb);
-    }
+    for (int lb = 0; lb < nlb; lb++) block(lb);
     // dSn in slot v: dim row32(v, l / 32) of the lane's token; with S at the same dims, the N0
     // backward needs one sum over the token's D dims (this lane's and lane l ^ 32's).
     const float s_scale = rsqrtf((float)D);
@@ -1612,7 +1533,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int v = 4 * gq + i;
-        dsn[v] = accA[v] * s_scale + accB[v] * (c_scale * g_unscale);
+        dsn[v] = accA[v] * s_scale + accB[v] * c_scale;
         sv[v] = s4[i];
         if (d0 < D) t += sv[v] * dsn[v];
       }
@@ -1628,6 +1549,254 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_kernel(BwdTokenAr
           const int v = 4 * gq;
           store4<T>(ds + d0, rn * dsn[v] - r3 * sv[v], rn * dsn[v + 1] - r3 * sv[v + 1],
                     rn * dsn[v + 2] - r3 * sv[v + 2], rn * dsn[v + 3] - r3 * sv[v + 3]);
+        }
+      }
+    }
+  }
+}
+
+// The synthesis call's token-side cotangent for bf16 inputs, with fp16 operands (as in the encode
+// kernel above):
+//   the seeds in fp16, exact for bf16 values of magnitude in [2^-14, 2^15) (a head with seeds of
+//     2^15 or more takes them scaled by a power of two, and the products' start values alike);
+//   c*N0(S) per token as the bf16 pair the recompute's logits used (hi truncated, lo rounded),
+//     carried exactly by an fp16 pair, so the logits match the normalizers L;
+//   G / c as an fp16 pair scaled per (batch, head) by 2^q so that its largest element lies in
+//     (2^13, 2^14] (the bf16 pair hi + lo splits exactly), the dP operand; its hi part is the
+//     operand of sum_m P G;
+//   P in fp16 as 2^14 P (the score product starts from 14 - L), at most 2^14 and clear of fp16's
+//     subnormals down to P = 2^-28;
+//   dS in fp16 against the seeds, scaled per (batch, head) from the bound
+//     |dP - c| = |G_m . (N0(s_n) - Qd_m)| <= max_m |G_m|_1 2 sqrt(D), which keeps it below 2^14.
+// dP = G . c N0(S) keeps the pairs: near a one-hot synthesis row, dP - c is a difference of nearly
+// equal terms.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_h_kernel(BwdTokenArgs a) {
+  using F = Frag<bf16>;
+  using Op = typename F::Op;
+  constexpr int KB = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 8;
+  using Sw = Swz<bf16, D>;
+
+  // Block-major LDS: per 32 latents, the seeds (rows >= M zero), 2^q G / c hi and lo (fp16); then
+  // the stats (14 - L and -2^q c, stat_pos order) and per-wave maxima.
+  constexpr int NTILE = 3;
+  constexpr int TQS = 0, TGH = 1, TGL = 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int Mp = a.Mp;
+  f16* tiles = reinterpret_cast<f16*>(smem);
+  float* sl = reinterpret_cast<float*>(tiles + NTILE * Mp * D);  // [Mp]
+  float* sc = sl + Mp;                                            // [Mp]
+  float* red = sc + Mp;                                           // [3][16]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int bh = blockIdx.y, h = bh % a.H;
+  auto tile = [&](int lb, int j) __attribute__((always_inline)) { return tiles + (lb * NTILE + j) * 32 * D; };
+  auto tile_at = [&](int row, int j, int part) __attribute__((always_inline)) {
+    return tiles + ((row >> 5) * NTILE + j) * 32 * D + Sw::off(row & 31, part * 8);
+  };
+  auto block_max = [&](float v, int slot) __attribute__((always_inline)) {
+    v = wave_max(v);
+    if (lane == 0) red[16 * slot + wave] = v;
+    __syncthreads();
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) m = fmaxf(m, red[16 * slot + w]);
+    return m;
+  };
+  auto scale_exp = [](float x) __attribute__((always_inline)) {  // x 2^s < 2^14 (x > 0)
+    int e = 0;
+    (void)frexpf(x, &e);
+    return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+  };
+
+  const bf16* seeds = reinterpret_cast<const bf16*>(a.Qseed) + (int64_t)h * a.M * D;
+  const bf16* gh = reinterpret_cast<const bf16*>(a.Gop) + (int64_t)bh * Mp * D;
+  const bf16* gl = reinterpret_cast<const bf16*>(a.G_lo) + (int64_t)bh * Mp * D;
+  int q = 0, es = 0;
+  float A1 = 0.f;
+  {
+    float smx = 0.f, gmx = 0.f;
+    for (int i = tid; i < a.M * D; i += NT) smx = fmaxf(smx, fabsf((float)seeds[i]));
+    for (int i = tid; i < Mp * D; i += NT) gmx = fmaxf(gmx, fabsf((float)gh[i] + (float)gl[i]));
+    smx = block_max(smx, 0);
+    gmx = block_max(gmx, 1);
+    es = smx >= 32768.f ? scale_exp(smx) : 0;
+    q = scale_exp(gmx);
+    const float fs = ldexpf(1.f, es), gs = ldexpf(1.f, q);
+    float a1 = 0.f;
+    for (int row = tid; row < Mp; row += NT) {
+      float n1 = 0.f;
+#pragma unroll
+      for (int part = 0; part < CPR; part++) {
+        float sv[8], hv[8], lv[8];
+        if (row < a.M) chunk_to_float<bf16>(*reinterpret_cast<const Chunk*>(seeds + (int64_t)row * D + part * 8), sv);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; e++) sv[e] = 0.f;
+        }
+        chunk_to_float<bf16>(*reinterpret_cast<const Chunk*>(gh + (int64_t)row * D + part * 8), hv);
+        chunk_to_float<bf16>(*reinterpret_cast<const Chunk*>(gl + (int64_t)row * D + part * 8), lv);
+        f16x8 os, oh, ol;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          os[e] = (f16)(sv[e] * fs);
+          const float v = (hv[e] + lv[e]) * gs;
+          const f16 x = (f16)v;
+          oh[e] = x;
+          ol[e] = (f16)(v - (float)x);
+          n1 += fabsf((float)oh[e] + (float)ol[e]);
+        }
+        *reinterpret_cast<f16x8*>(tile_at(row, TQS, part)) = os;
+        *reinterpret_cast<f16x8*>(tile_at(row, TGH, part)) = oh;
+        *reinterpret_cast<f16x8*>(tile_at(row, TGL, part)) = ol;
+      }
+      a1 = fmaxf(a1, n1);
+      const int p = stat_pos(row);
+      sl[p] = 14.f - a.lsyn[(int64_t)bh * Mp + row];
+      sc[p] = -a.cs[(int64_t)bh * Mp + row] * gs;
+    }
+    A1 = block_max(a1, 2);
+  }
+  __syncthreads();
+  const bool rare = es != 0;  // uniform over the workgroup
+  const float fs = ldexpf(1.f, es), ifs = ldexpf(1.f, -es);
+  // dS' = 2^14 P 2^q (dP - c) is at most 2^14 A1 2 log2(e); ksc keeps it below 2^14.
+  const int ke = scale_exp(16384.f * A1 * (2.f * kLog2e));
+  const float ksc = ldexpf(1.f, ke);
+  const LaneOffs<bf16, D> lofs = lane_offsets<bf16, D>(lane);
+  auto row16 = [&](int lb, int j, int kk) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x8, F::template row_at<D>(reinterpret_cast<const bf16*>(tile(lb, j)), lofs, kk));
+  };
+  auto krows16 = [&](int lb, int j, int t) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x8, F::template krows_at<D>(reinterpret_cast<const bf16*>(tile(lb, j) + 16 * t * D), lofs));
+  };
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = (t_begin + a.tokens_per_wg < a.N) ? t_begin + a.tokens_per_wg : a.N;
+  const int nlb = Mp / 32;
+  const float c_scale = kLog2e * rsqrtf((float)D);
+  const bf16* sbase = reinterpret_cast<const bf16*>(a.S) + (int64_t)bh * a.N * D;
+
+  for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
+    const int64_t tok = base + (lane & 31);
+    const bool valid = tok < t_end;
+    // c * N0(S) of the lane's token: dims 16 kk + 8 (l / 32) .. + 7 here, the rest in lane l ^ 32;
+    // rounded to the bf16 pair (hi by truncation, lo to nearest) and carried as an fp16 pair.
+    float x[KB][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++) {
+      F::to_float(valid ? F::gload(sbase + tok * D + 16 * kk + 8 * hh) : F::zero(), x[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss += x[kk][e] * x[kk][e];
+    }
+    ss += shfl_xor(ss, 32);
+    const float rn = 1.0f / sqrtf(ss * (1.0f / D) + kRmsEps);
+    f16x8 sbh[KB], sbl[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; kk++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float y = x[kk][e] * (rn * c_scale);
+        const float yh = __uint_as_float(__float_as_uint(y) & 0xffff0000u);
+        const float w = yh + (float)(bf16)(y - yh);
+        const f16 wh = (f16)w;
+        sbh[kk][e] = wh;
+        sbl[kk][e] = (f16)(w - (float)wh);
+      }
+    f32x16 accA = {}, accB = {};
+    auto block = [&](int lb) __attribute__((always_inline)) {
+      f16x8 qa[KB], gha[KB], gla[KB];
+      // The products start from 14 - L and -2^q c: A = l - L + 14, dP = 2^q (dP - c).
+      f32x16 A = load_stats16(sl + 32 * lb, hh), dP = load_stats16(sc + 32 * lb, hh);
+      if (rare) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) A[v] *= fs;
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        qa[kk] = row16(lb, TQS, kk);
+        gha[kk] = row16(lb, TGH, kk);
+        gla[kk] = row16(lb, TGL, kk);
+        A = mfma_32x32_f16(qa[kk], sbl[kk], A);
+        A = mfma_32x32_f16(qa[kk], sbh[kk], A);
+        dP = mfma_32x32_f16(gla[kk], sbh[kk], dP);
+        dP = mfma_32x32_f16(gha[kk], sbl[kk], dP);
+        dP = mfma_32x32_f16(gha[kk], sbh[kk], dP);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        hold(A, qa[kk]);
+        hold(A, sbh[kk]);
+        hold(A, sbl[kk]);
+        hold(dP, gha[kk]);
+        hold(dP, gla[kk]);
+        hold(dP, sbh[kk]);
+        hold(dP, sbl[kk]);
+      }
+      if (rare) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) A[v] *= ifs;
+      }
+      f16x8 pk[2], sk[2];
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const float p = exp2_fast(A[v]);  // 2^14 P
+        pk[v >> 3][v & 7] = (f16)p;
+        sk[v >> 3][v & 7] = (f16)(p * dP[v] * ksc);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const f16x8 qk = krows16(lb, TQS, t);
+        accA = mfma_32x32_f16(qk, sk[t], accA);
+        hold(accA, qk);
+        hold(accA, sk[t]);
+        const f16x8 gk = krows16(lb, TGH, t);
+        accB = mfma_32x32_f16(gk, pk[t], accB);
+        hold(accB, gk);
+        hold(accB, pk[t]);
+      }
+    };
+    int lb = 0;
+    for (; lb + 4 <= nlb; lb += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) block(lb + u);
+    }
+    for (; lb < nlb; lb++) block(lb);
+    // dSn = (1/sqrt(D)) sum_m dS Qseed + c sum_m P (G / c), less the factors: accA carries
+    // 2^(14 + q + ke + es), accB 2^(14 + q). Slot v holds dim row32(v, l / 32) of the lane's token;
+    // with S at the same dims, the N0 backward needs one sum over the token's D dims (this lane's
+    // and lane l ^ 32's).
+    const float fa = ldexpf(rsqrtf((float)D), -(14 + q + ke + es)), fb = ldexpf(c_scale, -(14 + q));
+    float dsn[16], sv[16];
+    float t = 0.f;
+#pragma unroll
+    for (int gq = 0; gq < 4; gq++) {
+      const int d0 = row32(4 * gq, hh);
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (d0 < D && valid) load4<bf16>(sbase + tok * D + d0, s4);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int v = 4 * gq + i;
+        dsn[v] = accA[v] * fa + accB[v] * fb;
+        sv[v] = s4[i];
+        if (d0 < D) t += sv[v] * dsn[v];
+      }
+    }
+    t += shfl_xor(t, 32);
+    if (valid) {
+      bf16* ds = reinterpret_cast<bf16*>(a.dS) + ((int64_t)bh * a.N + tok) * D;
+      const float r3 = rn * rn * rn * t * (1.0f / D);
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int d0 = row32(4 * gq, hh);
+        if (d0 < D) {
+          const int v = 4 * gq;
+          store4<bf16>(ds + d0, rn * dsn[v] - r3 * sv[v], rn * dsn[v + 1] - r3 * sv[v + 1],
+                       rn * dsn[v + 2] - r3 * sv[v + 2], rn * dsn[v + 3] - r3 * sv[v + 3]);
         }
       }
     }
@@ -1730,7 +1899,8 @@ static size_t bwd_token_lds_t(int Mp, int kind) {
   switch (kind) {
     case kBwdTokDecode: return (2 * NP + (NP - 1)) * tile;  // bf16: c*Q in fp16 as well
     case kBwdTokEncode: return 2 * NP * tile + stats + (sizeof(T) == 2 ? 48 * sizeof(float) : 0);  // bf16: per-wave maxima
-    default: return (1 + NP + (NP - 1)) * tile + stats + 16 * sizeof(float);  // seeds, G / c [, fp16]; stats; per-wave maxima
+    default:  // seeds and G / c (bf16: both fp16, G / c as a pair; fp32: plain), stats, per-wave maxima
+      return sizeof(T) == 2 ? 3 * tile + stats + 48 * sizeof(float) : 2 * tile + stats;
   }
 }
 
@@ -1757,7 +1927,9 @@ static hipError_t launch_bwd_token_t(const BwdTokenArgs& a, int kind, int gx, in
     case kBwdTokEncode:
       if constexpr (sizeof(T) == 2) return go(bwd_token_encode_h_kernel<D, NW>, NW);
       else return go(bwd_token_encode_kernel<T, D, NW>, NW);
-    default: return go(bwd_token_synthesis_kernel<T, D, NW>, NW);
+    default:
+      if constexpr (sizeof(T) == 2) return go(bwd_token_synthesis_h_kernel<D, NW>, NW);
+      else return go(bwd_token_synthesis_kernel<T, D, NW>, NW);
   }
 }
 

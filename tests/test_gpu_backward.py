@@ -320,6 +320,18 @@ def test_bwd_bf16_token_values_beyond_fp16(name, rows, scale):
     assert worst <= tol(w.dtype)
 
 
+@pytest.mark.parametrize("dtype,seeds", [("bf16", 3.0), ("bf16", 6.0), ("fp32", 6.0)])
+def test_bwd_seed_scales(dtype, seeds):
+    # The seeds' learned scale sets the synthesis call's temperature (Appendix A.3, Eq. 14). At x6
+    # every synthesis row is nearly one-hot over the tokens, so its cotangent P (dP - c) is a
+    # difference of nearly equal terms, and the routing queries inherit the synthesis output's
+    # rounding at full weight.
+    w = make_workload(3, B=1, H=2, N=3000, M=64, dtype=dtype, seed=13)
+    from workloads.gen import _store
+    w.Qseed = _store(w.f64("Qseed") * seeds, dtype)
+    _check(w, label=f"bwd seeds x{seeds:g} {dtype}")
+
+
 @pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("scale", [8.0, 24.0])
