@@ -356,6 +356,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int CH = 16 / sizeof(T), CPR = D / CH;
   constexpr int NCH = ST * CPR;  // chunks per tensor per stage
   constexpr bool DEC = CALL == kBwdDecode, SYN = CALL == kBwdSynthesis;
+  // bf16 decode call: both products over tokens take single fp16 operands (no cancellation in
+  // either sum): K and dY scaled per (batch, head) into fp16's range (by max |K| and by
+  // max_n |dY_n|_1 >= max |dY|), in fp16 copies of the stage tiles; P as 2^14 P (the score product
+  // starts from 14 - L); dS scaled per (batch, head) from the bound
+  // |dP - c| <= 2 max_n |dY_n|_1 max |Zc| below 2^14. The maxima come from the token decode kernel's
+  // waves. The stores take the factors out exactly.
+  constexpr bool H16 = DEC && sizeof(T) == 2;
   // Stage tiles: X and W (decode, encode), or the hi and lo parts of c*N0(S) (synthesis).
   constexpr int NLOAD = SYN ? NCH : 2 * NCH;
   constexpr int PER = (NLOAD + NT - 1) / NT;
@@ -365,6 +372,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   T* xs = reinterpret_cast<T*>(smem);                          // [2][ST * D]
   T* ws = xs + 2 * ST * D;                                     // [2][ST * D]: W, or the lo part of X
   float* tst = reinterpret_cast<float*>(ws + 2 * ST * D);      // [2][2][ST] decode token stats
+  f16* xs16 = reinterpret_cast<f16*>(tst + 4 * ST);             // H16: [2][ST * D] 2^sk K
+  f16* ws16 = xs16 + 2 * ST * D;                                // H16: [2][ST * D] 2^sy dY
+  float* mred = reinterpret_cast<float*>(ws16 + 2 * ST * D);    // H16: [2][NW] maxima
 
   int chunk_id, lg;
   if (a.nlg == 1) {
@@ -430,6 +440,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     negC[v] = -Lc;
   }
 
+  // H16: per-(batch, head) scales 2^sk (K), 2^sy (dY) and 2^sd (dS, with P as 2^14 P).
+  int sk = 0, sy = 0, sd = 0;
+  if constexpr (H16) {
+    float m[2] = {0.f, 0.f};
+    const float* tm = a.tmax + (int64_t)bh * a.ntmax * 2;
+    for (int i = tid; i < a.ntmax; i += NT) {
+#pragma unroll
+      for (int j = 0; j < 2; j++) m[j] = fmaxf(m[j], tm[2 * i + j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      m[j] = wave_max(m[j]);
+      if (lane == 0) mred[j * NW + wave] = m[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      m[j] = 0.f;
+      for (int w = 0; w < NW; w++) m[j] = fmaxf(m[j], mred[j * NW + w]);
+    }
+    auto scale_exp = [](float x) __attribute__((always_inline)) {  // x 2^s < 2^14 (x > 0)
+      int e = 0;
+      (void)frexpf(x, &e);
+      return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+    };
+    sk = scale_exp(m[0]);
+    sy = scale_exp(m[1]);  // |dY| <= |dY_n|_1
+    sd = scale_exp(16384.f * 2.f * m[1] * a.zmax[bh]);
+  }
+  const float fk = ldexpf(1.f, sk), fy = ldexpf(1.f, sy), fd = ldexpf(1.f, sd);
+
   Chunk rg[PER];
   float tsl = 0.f, tsc = 0.f;
   auto load = [&](int stage) __attribute__((always_inline)) {
@@ -484,14 +525,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (q < NLOAD) {
           const bool isw = q >= NCH;
           const int qq = isw ? q - NCH : q;
-          *reinterpret_cast<Chunk*>((isw ? ws : xs) + buf * ST * D + Sw::off(qq / CPR, (qq % CPR) * CH)) = rg[i];
+          const int o = buf * ST * D + Sw::off(qq / CPR, (qq % CPR) * CH);
+          *reinterpret_cast<Chunk*>((isw ? ws : xs) + o) = rg[i];
+          if constexpr (H16) {
+            float x[CH];
+            chunk_to_float<T>(rg[i], x);
+            const float f = isw ? fy : fk;
+            f16x8 h;
+#pragma unroll
+            for (int j = 0; j < CH; j++) h[j] = (f16)(x[j] * f);
+            *reinterpret_cast<f16x8*>((isw ? ws16 : xs16) + o) = h;
+          }
         }
       }
     }
     if constexpr (DEC) {
       if (tid < ST) {
         const int p = stat_pos(tid);
-        tst[(2 * buf) * ST + p] = -tsl;  // negated: the decode products start from -L and -c
+        // Negated: the decode products start from -L and -c (H16: 14 - L, so that P comes out as
+        // 2^14 P).
+        tst[(2 * buf) * ST + p] = (H16 ? 14.f : 0.f) - tsl;
         tst[(2 * buf + 1) * ST + p] = -tsc;
       }
     }
@@ -563,7 +616,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if constexpr (decltype(MASKED)::value)
           if (r0 + row32(v, hh) >= nvalid) p = 0.f;
         P[v] = p;
-        dS[v] = p * dp[v];
+        dS[v] = H16 ? p * dp[v] * fd : p * dp[v];
+      }
+      if constexpr (H16) {
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          f16x8 dsk, pk;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            dsk[e] = (f16)dS[8 * t + e];
+            pk[e] = (f16)P[8 * t + e];
+          }
+          const f16x8 xk = __builtin_bit_cast(
+              f16x8, F::template krows_at<D>(reinterpret_cast<const T*>(xs16 + buf * ST * D + (r0 + 16 * t) * D), lofs));
+          acc1 = mfma_32x32_f16(xk, dsk, acc1);
+          hold(acc1, xk);
+          hold(acc1, dsk);
+          const f16x8 wk = __builtin_bit_cast(
+              f16x8, F::template krows_at<D>(reinterpret_cast<const T*>(ws16 + buf * ST * D + (r0 + 16 * t) * D), lofs));
+          acc0 = mfma_32x32_f16(wk, pk, acc0);
+          hold(acc0, wk);
+          hold(acc0, pk);
+        }
+        continue;
       }
 #pragma unroll
       for (int t = 0; t < 2; t++) {
@@ -614,7 +689,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   if (!active) return;
   // Result slot v of lane l: dim row32(v, l / 32) of latent lrow; four consecutive dims per store.
+  // H16: less the factors 2^(sk + 14 + sd) (acc1) and 2^(sy + 14) (acc0).
   const int64_t prow = ((int64_t)bh * a.nchunk + chunk_id) * a.Mp + lrow;
+  if constexpr (H16) {
+    const float o1 = ldexpf(1.f, -(sk + 14 + sd)), o0 = ldexpf(1.f, -(sy + 14));
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      acc1[v] *= o1;
+      acc0[v] *= o0;
+    }
+  }
 #pragma unroll
   for (int gq = 0; gq < 4; gq++) {
     const int d0 = row32(4 * gq, hh);
@@ -859,6 +943,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
   const T* kbase = reinterpret_cast<const T*>(a.K) + (int64_t)bh * a.N * D;
   const T* ybase = reinterpret_cast<const T*>(a.dY) + (int64_t)bh * a.N * D;
   const float zmax = kH ? a.zmax[bh] : 0.f;
+  // bf16: the largest |K| (as bf16 magnitude bits) and |dY_n|_1 of the wave's tokens, for the
+  // scales of the decode call's latent-side fp16 products.
+  uint32_t kmx = 0;
+  float y1m = 0.f;
 
   for (int64_t base = t_begin + (int64_t)wave * 32; base < t_end; base += (int64_t)NW * 32) {
     const int64_t tok = base + (lane & 31);
@@ -976,7 +1064,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       for (int kk = 0; kk < KB; kk++)
 #pragma unroll
         for (int e = 0; e < 8; e++) y1 += fabsf((float)yb[kk][e]);
-      const float bound = 2.f * (y1 + shfl_xor(y1, 32)) * zmax;  // >= |dP - c| of the token
+#pragma unroll
+      for (int kk = 0; kk < KB; kk++) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 kw = __builtin_bit_cast(u32x4, kb[kk]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const uint32_t m = kw[i] & 0x7fff7fffu;
+          kmx = max(kmx, max(m & 0xffffu, m >> 16));
+        }
+      }
+      y1 += shfl_xor(y1, 32);
+      y1m = fmaxf(y1m, y1);
+      const float bound = 2.f * y1 * zmax;  // >= |dP - c| of the token
       int e = 0;
       (void)frexpf(bound, &e);  // bound < 2^e
       sh = bound > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
@@ -1025,6 +1125,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
           *reinterpret_cast<f32x4*>(dk + (lane & 31) * D + d0) = f32x4{accK[4 * gq] * os, accK[4 * gq + 1] * os,
                                                     accK[4 * gq + 2] * os, accK[4 * gq + 3] * os};
       }
+    }
+  }
+  if constexpr (kH) {
+    const float km = wave_max(__uint_as_float(kmx << 16));
+    y1m = wave_max(y1m);
+    if (lane == 0) {
+      float* o = a.tmax + (((int64_t)bh * gridDim.x + blockIdx.x) * NW + wave) * 2;
+      o[0] = km;
+      o[1] = y1m;
     }
   }
 }
@@ -1842,7 +1951,8 @@ hipError_t launch_bwd_center(const BwdCenterArgs& a, int dtype, int D, int BH, h
 template <typename T, int D, int CALL, int NW>
 static hipError_t launch_bwd_latent_t(const BwdLatentArgs& a, int gx, int BH, hipStream_t st) {
   const size_t stage = (size_t)bwd_stage_t(sizeof(T) == 2, NW);
-  const size_t lds = 4 * stage * D * sizeof(T) + (CALL == kBwdDecode ? 4 * stage * sizeof(float) : 0);
+  const size_t lds = 4 * stage * D * sizeof(T) + (CALL == kBwdDecode ? 4 * stage * sizeof(float) : 0) +
+                     (CALL == kBwdDecode && sizeof(T) == 2 ? 4 * stage * D * sizeof(f16) + 2 * NW * sizeof(float) : 0);
   hipError_t e = allow_lds_bwd(bwd_latent_kernel<T, D, CALL, NW>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_latent_kernel<T, D, CALL, NW>), dim3(gx, BH), dim3(NW * 64), lds, st, a);

@@ -464,6 +464,7 @@ struct BwdPlan {
   int64_t tok_tpw = 0;
   size_t off_qd = 0, off_z32 = 0, off_lsyn = 0, off_lenc = 0, off_zc = 0, off_zc_lo = 0, off_ldec = 0;
   size_t off_cd = 0, off_dkdec = 0, off_p0 = 0, off_p1 = 0, off_dz32 = 0, off_dzop = 0, off_dzop_lo = 0;
+  size_t off_tmax = 0;
   size_t off_ce = 0, off_dqdec = 0, off_dqf = 0, off_gop = 0, off_gop_lo = 0, off_cs = 0, off_rowdot = 0;
   size_t off_zmax = 0;
   size_t total = 0;
@@ -530,6 +531,7 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.off_cs = off;     off = align256(off + lat * 4);
   p.off_rowdot = off; off = align256(off + lat * 4);
   p.off_zmax = off;   off = align256(off + (size_t)BH * 4);
+  p.off_tmax = off;   off = align256(off + (size_t)BH * p.tok_gx * p.tok_dec_nw * 2 * 4);
   p.total = off;
   return p;
 }
@@ -588,7 +590,7 @@ int enqueue_backward_from_saved(const void* K, const void* V, const void* S, con
 
   flarepp::BwdTokenArgs ta{};
   ta.K = K; ta.V = V; ta.dY = dY; ta.S = S; ta.tl = ldec; ta.tc = cd; ta.dKdec = dkdec; ta.Qrows = qrows;
-  ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.zmax = F(p.off_zmax); ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
+  ta.Zc = w + p.off_zc; ta.Zc_lo = w + p.off_zc_lo; ta.zmax = F(p.off_zmax); ta.tmax = F(p.off_tmax); ta.dZop = w + p.off_dzop; ta.dZ_lo = w + p.off_dzop_lo;
   ta.lenc = sv.lenc; ta.ce = F(p.off_ce); ta.dZ32 = F(p.off_dz32); ta.Z32 = F(p.off_z32); ta.Qseed = Qseed; ta.Gop = w + p.off_gop; ta.G_lo = w + p.off_gop_lo;
   ta.lsyn = sv.lsyn; ta.cs = F(p.off_cs); ta.dK = dK; ta.dV = dV; ta.dS = dS; ta.N = N;
   ta.tokens_per_wg = p.tok_tpw; ta.M = M; ta.Mp = p.Mp; ta.H = H; ta.force_exact = g_force_exact.load() ? 1 : 0;
@@ -598,6 +600,7 @@ int enqueue_backward_from_saved(const void* K, const void* V, const void* S, con
   flarepp::BwdLatentArgs la{};
   la.N = N; la.chunk = p.lat_chunk; la.nchunk = p.lat_nchunk; la.nlg = p.lat_nlg; la.M = M; la.Mp = p.Mp; la.H = H;
   la.part0 = F(p.off_p0); la.part1 = F(p.off_p1);
+  la.tmax = F(p.off_tmax); la.zmax = F(p.off_zmax); la.ntmax = p.tok_gx * p.tok_dec_nw;
   flarepp::BwdReduceArgs ra{};
   ra.part0 = la.part0; ra.part1 = la.part1; ra.nchunk = p.lat_nchunk; ra.M = M; ra.Mp = p.Mp; ra.H = H; ra.B = B;
   ra.Z32 = F(p.off_z32); ra.dZ32 = F(p.off_dz32); ra.dZop = w + p.off_dzop; ra.dZop_lo = w + p.off_dzop_lo;

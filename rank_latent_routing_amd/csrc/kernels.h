@@ -116,6 +116,9 @@ struct BwdLatentArgs {
                      // dP operand carries them (rows >= M: 0)
   float* part0;      // decode: [BH][nchunk][Mp][D] sum_n P dY
   float* part1;      // [BH][nchunk][Mp][D] sum_n dS X
+  const float* tmax; // bf16 decode: [BH][ntmax][2] maxima of the token decode kernel's waves
+  const float* zmax; // bf16 decode: [BH] largest |Zc| element
+  int ntmax;
   int64_t N;
   int64_t chunk;     // tokens per chunk (a multiple of the stage)
   int nchunk, nlg, M, Mp, H;
@@ -157,6 +160,7 @@ struct BwdTokenArgs {
   float* dKdec;          // [BH][N][D] fp32: the decode call's dK (written by decode, read by encode)
   const void* Qrows;     // c*Q workspace rows [BH][Mp][R*D] (hi, lo parts)
   const void* Zc; const void* Zc_lo;      // [BH][Mp][D] dtype: Z minus its mean over latents
+  float* tmax;  // bf16 decode: [BH][gridDim.x * NW][2] per-wave max |K| and max_n |dY_n|_1
   const float* zmax;                      // [BH] largest |Zc| element (bf16 decode's dK product)
   const void* dZop; const void* dZ_lo;    // [BH][Mp][D] dtype
   const float* lenc; const float* ce;     // [BH][Mp]
