@@ -169,10 +169,12 @@ int flarepp_mix_simplified_ws(const void* K, const void* V, const void* Sk, cons
  *   dQseed, dQf [H, M, D]    dtype  (summed over the batch, as the seeds and Qf are shared);
  *   dg          [H]          fp32   (the cotangent of the gate value g, summed over the batch).
  * The forward pass is recomputed inside the call (nothing has to be kept from flarepp_mix).
- * Accumulation is fp32. In bf16 runs every operand the library computes (probabilities, score
- * cotangents, the routing queries, Z, dZ and the other latent cotangents) enters the matrix unit
- * as a pair of bf16 values hi + lo, so that the cotangents carry about 16 significant bits until
- * they are stored in bf16. Support as for flarepp_mix. Every output is written fully and must not
+ * Accumulation is fp32. In bf16 runs the operands the library computes (probabilities, score
+ * cotangents, the routing queries, Z, dZ and the other latent cotangents) enter the matrix unit as
+ * pairs hi + lo (bf16, or fp16 in the token-side kernels; at least 16 significant bits) wherever a
+ * product's terms cancel, and as single fp16 values (11 bits) scaled by powers of two into fp16's
+ * range where they do not: the token-side products over latents and the decode call's products over
+ * tokens. Support as for flarepp_mix. Every output is written fully and must not
  * overlap any other argument buffer; inputs are read-only. With B*H*N == 0 the shared parameters'
  * cotangents are set to zero. Deterministic (no atomics), asynchronous on `stream`.
  * flarepp_mix_backward allocates its workspace stream-ordered; flarepp_mix_backward_ws takes the
