@@ -320,6 +320,31 @@ def test_bwd_bf16_token_values_beyond_fp16(name, rows, scale):
     assert worst <= tol(w.dtype)
 
 
+def test_bwd_bf16_seeds_beyond_fp16():
+    # The bf16 synthesis call's token-side products take the seeds in fp16, exact below 2^15; a head
+    # whose seeds reach 2^15 takes them scaled by a power of two, with the score product's start
+    # values scaled alike. One seed row of head 0 at 2^15 sends that head there; its synthesis
+    # logits for that row reach about 4e4 (log2 units), where the pairs carrying c N0(S) move them
+    # by up to about 0.3, as with keys of 2^15 (above). Checked: every output finite, and head 1
+    # (ordinary seeds) at the bars.
+    w = make_workload(3, B=1, H=2, N=3000, M=64, seed=17)
+    from workloads.gen import _store
+    Qs = w.f64("Qseed")
+    Qs[0, 5] *= 2.0 ** 15
+    w.Qseed = _store(Qs, w.dtype)
+    say(f"[bwd] bf16 seeds at 2^15 in head 0: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    dY = make_cotangent(w)
+    got = run_backward(w, dY)
+    for k, v in got.items():
+        assert np.isfinite(v).all(), k
+    ref = oracle_backward(w, dY)
+    worst = {k: _err(got[k][0, 1], ref[k][0, 1], w.dtype) for k in ("dK", "dV", "dS")}
+    worst.update({k: _err(got[k][1], ref[k][1], w.dtype) for k in ("dQseed", "dQf")})
+    say(f"[bwd] bf16 seeds at 2^15, head 1: worst {worst} (bar {tol(w.dtype)})")
+    for k, e in worst.items():
+        assert e <= tol(w.dtype), (k, e)
+
+
 @pytest.mark.parametrize("dtype,seeds", [("bf16", 3.0), ("bf16", 6.0), ("fp32", 6.0)])
 def test_bwd_seed_scales(dtype, seeds):
     # The seeds' learned scale sets the synthesis call's temperature (Appendix A.3, Eq. 14). At x6
