@@ -205,6 +205,33 @@ def test_bwd_full_cfg5_one_head():
         assert e <= tol(w.dtype), (k, e)
 
 
+def test_bwd_saved_full_cfg5_bitwise():
+    # The benchmark times flarepp_mix_forward_saved + flarepp_mix_backward_saved at the 1M-token
+    # workload; at that size they return the self-contained backward's cotangents bit for bit
+    # (which test_bwd_full_cfg5_one_head checks against the oracle), and the saved forward's output
+    # is within the forward's bar of the inference forward's.
+    import rank_latent_routing_amd as fl
+    w = make_workload(5)
+    dY = make_cotangent(w)
+    say(f"[bwd] cfg5 full, saved state against recompute: B={w.B} H={w.H} N={w.N} M={w.M} D={w.D} {w.dtype}")
+    dev = to_device(w)
+    args = (dev["K"], dev["V"], dev["S"], dev["Qseed"], dev["Qf"], dev["g"])
+    dy = _device(dY, w.dtype)
+    ref = fl.flarepp_mix_backward(*args, dy)
+    need = fl.flarepp_backward_workspace_bytes(w.B, w.H, w.N, w.M, w.D, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y_saved = fl.flarepp_mix_forward_saved(*args, workspace=ws)
+    got = fl.flarepp_mix_backward_saved(*args, dy, workspace=ws)
+    y = fl.flarepp_mix(*args)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+    d = (y_saved.float() - y.float()).abs().max().item()
+    rms = y.float().pow(2).mean().sqrt().item()
+    say(f"[bwd] cfg5 full: saved == recompute bitwise; saved forward against forward {d / rms:.4g} of RMS")
+    assert d <= 2 * tol(w.dtype) * rms
+
+
 def test_bwd_determinism_and_entry_points_agree():
     w = make_workload(4, B=1, H=2, N=5000, M=200, seed=9)
     dY = make_cotangent(w)
