@@ -328,6 +328,15 @@ __device__ __forceinline__ f32x16 load_stats16(const float* base, int hh) {
   return out;
 }
 
+// Exponent s of the power of two 2^s that brings x (> 0) below 2^14 (x 2^s < 2^14 <= 2x 2^s), clamped
+// to [-100, 100] so that 2^s and 2^-s stay normal floats; 0 for x = 0. The fp16 operands of the
+// bf16 backward are scaled by such factors into fp16's range and the results scaled back exactly.
+__device__ __forceinline__ int pow2_below_2e14(float x) {
+  int e = 0;
+  (void)frexpf(x, &e);  // x < 2^e
+  return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+}
+
 // ------------------------------------------------------------------------------------------
 // Latent-side kernel of one routing call (Appendix B.5, Eq. 46-49, the sums over tokens).
 //
@@ -460,14 +469,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       m[j] = 0.f;
       for (int w = 0; w < NW; w++) m[j] = fmaxf(m[j], mred[j * NW + w]);
     }
-    auto scale_exp = [](float x) __attribute__((always_inline)) {  // x 2^s < 2^14 (x > 0)
-      int e = 0;
-      (void)frexpf(x, &e);
-      return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
-    };
-    sk = scale_exp(m[0]);
-    sy = scale_exp(m[1]);  // |dY| <= |dY_n|_1
-    sd = scale_exp(16384.f * 2.f * m[1] * a.zmax[bh]);
+    sk = pow2_below_2e14(m[0]);
+    sy = pow2_below_2e14(m[1]);  // |dY| <= |dY_n|_1
+    sd = pow2_below_2e14(16384.f * 2.f * m[1] * a.zmax[bh]);
   }
   const float fk = ldexpf(1.f, sk), fy = ldexpf(1.f, sy), fd = ldexpf(1.f, sd);
 
@@ -1076,10 +1080,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_decode_kernel(BwdTokenArgs 
       }
       y1 += shfl_xor(y1, 32);
       y1m = fmaxf(y1m, y1);
-      const float bound = 2.f * y1 * zmax;  // >= |dP - c| of the token
-      int e = 0;
-      (void)frexpf(bound, &e);  // bound < 2^e
-      sh = bound > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
+      sh = pow2_below_2e14(2.f * y1 * zmax);  // the bound >= |dP - c| of the token
     }
     f32x16 negL, negC;
 #pragma unroll
@@ -1309,11 +1310,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_h_kernel(BwdTokenArg
     return m;
   };
   // Power of two 2^s with x 2^s < 2^14 (x > 0), clamped to the fp32 range of the factors.
-  auto scale_exp = [](float x) __attribute__((always_inline)) {
-    int e = 0;
-    (void)frexpf(x, &e);  // x < 2^e
-    return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
-  };
 
   const float* dz = a.dZ32 + (int64_t)bh * Mp * D;
   const float* zz = a.Z32 + (int64_t)bh * a.M * D;
@@ -1340,7 +1336,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_h_kernel(BwdTokenArg
     }
     float mx = 0.f;
     for (int i = tid; i < a.M * D; i += NT) mx = fmaxf(mx, fabsf(dz[i]));
-    g = scale_exp(block_max(mx, 0));
+    g = pow2_below_2e14(block_max(mx, 0));
     const float gs = ldexpf(1.f, g);
     float a1 = 0.f, zm = 0.f;
     for (int row = tid; row < Mp; row += NT) {
@@ -1408,8 +1404,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_h_kernel(BwdTokenArg
     vmx = fmaxf(vmx, shfl_xor(vmx, 32));  // the token's largest |V|
     // Wave-uniform scales of K and V (1 unless the group's values leave fp16's exact range).
     const float wk = wave_max(kmx), wv = wave_max(vmx);
-    const int ek = wk >= 32768.f ? scale_exp(wk) : 0;
-    const int ev = (wv >= 32768.f || (wv > 0.f && wv < 0x1p-6f)) ? scale_exp(wv) : 0;
+    const int ek = wk >= 32768.f ? pow2_below_2e14(wk) : 0;
+    const int ev = (wv >= 32768.f || (wv > 0.f && wv < 0x1p-6f)) ? pow2_below_2e14(wv) : 0;
     const bool rare = (ek | ev) != 0;
     const float fk = ldexpf(1.f, ek), fv = ldexpf(1.f, ev);
     if (rare) {
@@ -1429,7 +1425,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_encode_h_kernel(BwdTokenArg
         k16[kk][e] = (f16)kx[kk][e];
         v16[kk][e] = (f16)vx[kk][e];
       }
-    const int sh = scale_exp(bound0 * (vmx + ZM));
+    const int sh = pow2_below_2e14(bound0 * (vmx + ZM));
     const float dsc = ldexpf(1.f, sh);
     const float ifk = ldexpf(1.f, -ek), ifv = ldexpf(1.f, -ev);
 
@@ -1715,11 +1711,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_h_kernel(BwdToken
     for (int w = 0; w < NW; w++) m = fmaxf(m, red[16 * slot + w]);
     return m;
   };
-  auto scale_exp = [](float x) __attribute__((always_inline)) {  // x 2^s < 2^14 (x > 0)
-    int e = 0;
-    (void)frexpf(x, &e);
-    return x > 0.f ? (14 - e < -100 ? -100 : 14 - e > 100 ? 100 : 14 - e) : 0;
-  };
 
   const bf16* seeds = reinterpret_cast<const bf16*>(a.Qseed) + (int64_t)h * a.M * D;
   const bf16* gh = reinterpret_cast<const bf16*>(a.Gop) + (int64_t)bh * Mp * D;
@@ -1732,8 +1723,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_h_kernel(BwdToken
     for (int i = tid; i < Mp * D; i += NT) gmx = fmaxf(gmx, fabsf((float)gh[i] + (float)gl[i]));
     smx = block_max(smx, 0);
     gmx = block_max(gmx, 1);
-    es = smx >= 32768.f ? scale_exp(smx) : 0;
-    q = scale_exp(gmx);
+    es = smx >= 32768.f ? pow2_below_2e14(smx) : 0;
+    q = pow2_below_2e14(gmx);
     const float fs = ldexpf(1.f, es), gs = ldexpf(1.f, q);
     float a1 = 0.f;
     for (int row = tid; row < Mp; row += NT) {
@@ -1773,7 +1764,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_token_synthesis_h_kernel(BwdToken
   const bool rare = es != 0;  // uniform over the workgroup
   const float fs = ldexpf(1.f, es), ifs = ldexpf(1.f, -es);
   // dS' = 2^14 P 2^q (dP - c) is at most 2^14 A1 2 log2(e); ksc keeps it below 2^14.
-  const int ke = scale_exp(16384.f * A1 * (2.f * kLog2e));
+  const int ke = pow2_below_2e14(16384.f * A1 * (2.f * kLog2e));
   const float ksc = ldexpf(1.f, ke);
   const LaneOffs<bf16, D> lofs = lane_offsets<bf16, D>(lane);
   auto row16 = [&](int lb, int j, int kk) __attribute__((always_inline)) {
