@@ -372,6 +372,18 @@ def test_bwd_bf16_seeds_beyond_fp16():
         assert e <= tol(w.dtype), (k, e)
 
 
+@pytest.mark.parametrize("scale", [2.0 ** -24, 2.0 ** 16])
+def test_bwd_bf16_cotangent_scales(scale):
+    # Cotangents far from unit size (a loss's gradients are often tiny): the bf16 kernels that take
+    # fp16 operands scale dY, dZ, G and dS into fp16's range by powers of two from their maxima, so
+    # the cotangents, which are linear in dY, meet the same relative bars at any scale.
+    w = make_workload(4, B=1, H=2, N=20000, seed=23)
+    from workloads.gen import _store
+    from workloads import to_float64
+    dY = _store(to_float64(make_cotangent(w), w.dtype) * scale, w.dtype)
+    _check(w, dY=dY, label=f"bwd bf16 dY x{scale:g}")
+
+
 @pytest.mark.parametrize("dtype,seeds", [("bf16", 3.0), ("bf16", 6.0), ("fp32", 6.0)])
 def test_bwd_seed_scales(dtype, seeds):
     # The seeds' learned scale sets the synthesis call's temperature (Appendix A.3, Eq. 14). At x6
