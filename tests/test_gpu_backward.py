@@ -437,6 +437,28 @@ def test_bwd_random_shapes(i, dtype, D, M, N, B, H):
     _check(w, label=f"random {i}: {dtype} D={D} M={M} N={N} B={B} H={H}")
 
 
+def _random_bf16_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([16, 32]))
+        M = int(rng.choice([1, 31, 32, 64, 95, 200, 256, 300, 511, 512]))
+        N = int(rng.choice([1, 31, 32, 33, 500, 1023, 4097, 20000]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        kind = str(rng.choice(["gauss", "cube"]))
+        cases.append((i, D, M, N, B, H, kind))
+    return cases
+
+
+@pytest.mark.parametrize("i,D,M,N,B,H,kind", _random_bf16_cases(8, 5150))
+def test_bwd_random_shapes_bf16(i, D, M, N, B, H, kind):
+    # More seeded shapes for the bf16 kernels with fp16 operands (token encode and synthesis, the
+    # decode call's latent side): ragged latent blocks, ragged token groups and stages, both widths.
+    w = make_workload(1 if kind == "gauss" else 2, B=B, H=H, N=N, M=M, D=D, dtype="bf16", kind=kind,
+                      seed=9100 + i)
+    _check(w, label=f"random bf16 {i}: D={D} M={M} N={N} B={B} H={H} {kind}")
+
+
 @pytest.mark.parametrize("dtype,N", [("fp32", 2), ("fp32", 3), ("bf16", 2), ("bf16", 3)])
 def test_bwd_tiny_token_counts(dtype, N):
     """Two or three tokens against 257 latents, at the usual bars. A softmax row over two tokens
