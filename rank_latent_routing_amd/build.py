@@ -3,7 +3,7 @@
 ``rank_latent_routing_amd/libflarepp_microbench.so`` (a library of their own, used only by the
 benchmark script).
 
-Usage: ``python -m rank_latent_routing_amd.build`` (or ``__graft_entry__.build()``).
+Usage: ``python -m rank_latent_routing_amd.build``.
 """
 from __future__ import annotations
 
