@@ -717,8 +717,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ------------------------------------------------------------------------------------------
-// Reductions. One thread per (latent, channel); blocks of 256 / D latent rows x D channels, so that
-// a row's D channels sit in consecutive lanes of one wave for the row sums.
+// Reductions. Each wave covers 64 consecutive (latent, channel) entries, 64 / D whole latent rows,
+// so that a row's D channels sit in consecutive lanes for the row sums. With many chunks
+// (BwdReduceArgs::split = 4) the four waves of a block share one such range, each summing a quarter
+// of the chunk partials, and wave 0 adds the quarters in a fixed order and finishes the entries;
+// with few (split = 1) each wave sums all chunks of its own range. Sums run with eight loads in
+// flight, in an order fixed by the shapes alone, so the results are the same on every call.
 template <int D>
 __device__ __forceinline__ float row_sum(float v) {
 #pragma unroll
@@ -726,26 +730,80 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// p[c * stride] summed over c in [c0, c1): eight independent partial sums, combined pairwise.
+__device__ __forceinline__ float strided_sum(const float* p, int64_t stride, int c0, int c1) {
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int c = c0;
+  for (; c + 8 <= c1; c += 8) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) s[k] += p[(int64_t)(c + k) * stride];
+  }
+#pragma unroll
+  for (int k = 0; k < 7; k++)
+    if (c + k < c1) s[k] += p[(int64_t)(c + k) * stride];
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
+// The same over the items j in [j0, j1) of runs of n items, run r starting at item (n + skip) r:
+// item j sits at p[(j + (j / n) skip) * stride].
+__device__ __forceinline__ float run_sum(const float* p, int64_t stride, int n, int skip, int j0, int j1) {
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int j = j0;
+  for (; j + 8 <= j1; j += 8) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) s[k] += p[(int64_t)(j + k + ((j + k) / n) * skip) * stride];
+  }
+#pragma unroll
+  for (int k = 0; k < 7; k++)
+    if (j + k < j1) s[k] += p[(int64_t)(j + k + ((j + k) / n) * skip) * stride];
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
+// How a reduction block's waves split the work: `part` of `split` parts of the chunks, for entry
+// group `eg` of the block's 4 / split groups of 64 entries.
+struct RedSplit {
+  int part, eg, first;  // first: the wave's first entry
+  __device__ RedSplit(int split) {
+    const int wave = threadIdx.x >> 6, groups = 4 / split;
+    part = wave / groups;
+    eg = wave % groups;
+    first = (blockIdx.x * groups + eg) * 64;
+  }
+  // The part [c0, c1) of n chunks this wave sums.
+  __device__ int c0(int n, int split) const { return n * part / split; }
+  __device__ int c1(int n, int split) const { return n * (part + 1) / split; }
+};
+
+// Adds the parts' values v of each lane's entry in a fixed order; the total is valid in the waves of
+// part 0.
+__device__ __forceinline__ float add_parts(float (*red)[64], float v, int split) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (split == 1) return v;
+  red[wave][lane] = v;
+  __syncthreads();
+  return (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+}
+
 // After the decode call: dZ = sum of the P^T dY partials (kept as a pair for the encode call), dQ_dec
 // = sum of the dS^T K partials over sqrt(D), and the encode call's c_m = <dZ_m, Z_m> with dZ as the
 // pair carries it.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_reduce_decode_kernel(BwdReduceArgs a) {
+  __shared__ float red[2][4][64];
   const int bh = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const RedSplit w(a.split);
+  const int idx = w.first + (threadIdx.x & 63);
   const int row = idx / D, d = idx % D;
-  if (row >= a.Mp) return;  // whole rows
   const bool valid = row < a.M;
   const int64_t cs = (int64_t)a.Mp * D;
   const int64_t base = ((int64_t)bh * a.nchunk * a.Mp + row) * D + d;
-  float z = 0.f, q = 0.f;
-  if (valid) {
-    for (int c = 0; c < a.nchunk; c++) {
-      z += a.part0[base + c * cs];
-      q += a.part1[base + c * cs];
-    }
-    q *= rsqrtf((float)D);
-  }
+  const int c0 = w.c0(a.nchunk, a.split), c1 = w.c1(a.nchunk, a.split);
+  float z = valid ? strided_sum(a.part0 + base, cs, c0, c1) : 0.f;
+  float q = valid ? strided_sum(a.part1 + base, cs, c0, c1) : 0.f;
+  z = add_parts(red[0], z, a.split);
+  q = add_parts(red[1], q, a.split);
+  if (w.part != 0 || row >= a.Mp) return;  // whole rows
+  q *= rsqrtf((float)D);
   const int64_t o = ((int64_t)bh * a.Mp + row) * D + d;
   T* zh = reinterpret_cast<T*>(a.dZop);
   T* zl = reinterpret_cast<T*>(a.dZop_lo);
@@ -763,19 +821,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_decode_kernel(BwdReduceArgs a)
 // (G as the pair carries it).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_reduce_gate_kernel(BwdReduceArgs a) {
+  __shared__ float red[4][64];
   const int bh = blockIdx.y, h = bh % a.H;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const RedSplit w(a.split);
+  const int idx = w.first + (threadIdx.x & 63);
   const int row = idx / D, d = idx % D;
-  if (row >= a.Mp) return;
   const bool valid = row < a.M;
   const int64_t cs = (int64_t)a.Mp * D;
   const int64_t base = ((int64_t)bh * a.nchunk * a.Mp + row) * D + d;
+  float q = valid ? strided_sum(a.part1 + base, cs, w.c0(a.nchunk, a.split), w.c1(a.nchunk, a.split)) : 0.f;
+  q = add_parts(red, q, a.split);
+  if (w.part != 0 || row >= a.Mp) return;
   const int64_t o = ((int64_t)bh * a.Mp + row) * D + d;
-  float q = 0.f;
-  if (valid) {
-    for (int c = 0; c < a.nchunk; c++) q += a.part1[base + c * cs];
-    q = a.dQdec[o] + q * rsqrtf((float)D);
-  }
+  if (valid) q = a.dQdec[o] + q * rsqrtf((float)D);
   const float f = valid ? to_f(reinterpret_cast<const T*>(a.Qf)[((int64_t)h * a.M + row) * D + d]) : 0.f;
   const float ss = row_sum<D>(f * f);
   const float tq = row_sum<D>(f * q);
@@ -801,8 +859,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_gate_kernel(BwdReduceArgs a) {
 // entries of one head (y); block 0 of each head also sums dg.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_reduce_synthesis_kernel(BwdReduceArgs a) {
+  __shared__ float red[4][64];
   const int h = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const RedSplit w(a.split);
+  const int idx = w.first + (threadIdx.x & 63);
   const int row = idx / D, d = idx % D;
   if (blockIdx.x == 0) {
     __shared__ float part[4];
@@ -817,22 +877,24 @@ __global__ __launch_bounds__(256) void bwd_reduce_synthesis_kernel(BwdReduceArgs
     __syncthreads();
     if (threadIdx.x == 0) a.dg[h] = (part[0] + part[1]) + (part[2] + part[3]);
   }
-  if (row >= a.M) return;
+  const bool valid = row < a.M;
   const int64_t cs = (int64_t)a.Mp * D;
-  float qs = 0.f, qf = 0.f;
-  for (int b = 0; b < a.B; b++) {
-    const int64_t bh = (int64_t)b * a.H + h;
-    const int64_t base = (bh * a.nchunk * a.Mp + row) * D + d;
-    for (int c = 0; c < a.nchunk; c++) qs += a.part1[base + c * cs];
-    qf += a.dQf_bh[(bh * a.Mp + row) * D + d];
-  }
+  // The partials of head h: nchunk chunks per batch element, the other heads' chunks in between.
+  const int nb = a.B * a.nchunk;
+  const float qs = add_parts(
+      red, valid ? run_sum(a.part1 + ((int64_t)h * a.nchunk * a.Mp + row) * D + d, cs, a.nchunk,
+                           (a.H - 1) * a.nchunk, w.c0(nb, a.split), w.c1(nb, a.split))
+                 : 0.f, a.split);
+  if (w.part != 0 || !valid) return;
+  const float qf = strided_sum(a.dQf_bh + ((int64_t)h * a.Mp + row) * D + d, (int64_t)a.H * a.Mp * D, 0, a.B);
   const int64_t o = ((int64_t)h * a.M + row) * D + d;
   reinterpret_cast<T*>(a.dQseed)[o] = (T)(qs * kLn2);
   reinterpret_cast<T*>(a.dQf)[o] = (T)qf;
 }
 
 // ------------------------------------------------------------------------------------------
-// Zc = Z - mean_m Z per (b, h), as a pair: one block per (b, h), the column sums through LDS.
+// Zc = Z - mean_m Z per (b, h), as a pair: one block per (b, h), the column sums through LDS. Each
+// thread's rows go in batches of eight, loads ahead of the stores.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_center_kernel(BwdCenterArgs a) {
   constexpr int RPB = 256 / D;  // rows per pass
@@ -840,8 +902,7 @@ __global__ __launch_bounds__(256) void bwd_center_kernel(BwdCenterArgs a) {
   const int bh = blockIdx.x;
   const int d = threadIdx.x % D, r0 = threadIdx.x / D;
   const float* z = a.Z32 + (int64_t)bh * a.M * D;
-  float s = 0.f;
-  for (int m = r0; m < a.M; m += RPB) s += z[(int64_t)m * D + d];
+  const float s = strided_sum(z + (int64_t)r0 * D + d, (int64_t)RPB * D, 0, r0 < a.M ? (a.M - r0 + RPB - 1) / RPB : 0);
   part[threadIdx.x] = s;
   __syncthreads();
   float mean = 0.f;
@@ -850,10 +911,22 @@ __global__ __launch_bounds__(256) void bwd_center_kernel(BwdCenterArgs a) {
   T* oh = reinterpret_cast<T*>(a.Zc) + (int64_t)bh * a.Mp * D;
   T* ol = reinterpret_cast<T*>(a.Zc_lo) + (int64_t)bh * a.Mp * D;
   float mx = 0.f;
-  for (int m = r0; m < a.Mp; m += RPB) {
-    const float zc = m < a.M ? z[(int64_t)m * D + d] - mean : 0.f;
-    store_pair<T>(oh, ol, (int64_t)m * D + d, zc);
-    mx = fmaxf(mx, fabsf(zc));
+  for (int m0 = r0; m0 < a.Mp; m0 += 8 * RPB) {
+    float zv[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int m = m0 + k * RPB;
+      zv[k] = m < a.M ? z[(int64_t)m * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int m = m0 + k * RPB;
+      if (m < a.Mp) {
+        const float zc = m < a.M ? zv[k] - mean : 0.f;
+        store_pair<T>(oh, ol, (int64_t)m * D + d, zc);
+        mx = fmaxf(mx, fabsf(zc));
+      }
+    }
   }
   if (a.zmax) {
     __syncthreads();  // every thread has read part[] above
@@ -1975,16 +2048,22 @@ hipError_t launch_bwd_latent(const BwdLatentArgs& a, int dtype, int D, int call,
 
 template <typename T, int D>
 static hipError_t launch_bwd_reduce_t(const BwdReduceArgs& a, int call, int BH, hipStream_t st) {
+  // Four waves per range of 64 entries when there are 16 or more chunk partials per entry (the batch's
+  // included for the synthesis call), else one.
+  BwdReduceArgs r = a;
   if (call == kBwdSynthesis) {
-    const unsigned gx = (unsigned)((a.M * D + 255) / 256);
-    hipLaunchKernelGGL((bwd_reduce_synthesis_kernel<T, D>), dim3(gx, a.H), dim3(256), 0, st, a);
+    r.split = a.B * a.nchunk >= 16 ? 4 : 1;
+    const int per_block = 64 * (4 / r.split);
+    const unsigned gx = (unsigned)((a.M * D + per_block - 1) / per_block);
+    hipLaunchKernelGGL((bwd_reduce_synthesis_kernel<T, D>), dim3(gx, a.H), dim3(256), 0, st, r);
     return hipGetLastError();
   }
-  const unsigned gx = (unsigned)((a.Mp * D + 255) / 256);
+  r.split = a.nchunk >= 16 ? 4 : 1;
+  const unsigned gx = (unsigned)(a.Mp * D / (64 * (4 / r.split)));  // Mp is a multiple of 32, D of 16
   if (call == kBwdDecode)
-    hipLaunchKernelGGL((bwd_reduce_decode_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_reduce_decode_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, r);
   else
-    hipLaunchKernelGGL((bwd_reduce_gate_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_reduce_gate_kernel<T, D>), dim3(gx, BH), dim3(256), 0, st, r);
   return hipGetLastError();
 }
 

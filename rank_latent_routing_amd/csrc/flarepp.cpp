@@ -475,12 +475,13 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.f = make_plan(B, H, N, M, D, dtype);
   const int BH = p.f.BH;
   p.Mp = p.f.Mp32;
-  // Latent side: one wave per 32 latents, groups of 4 or 8 waves; about 1024 (8-wave) or 2048
-  // (4-wave) workgroups over the token chunks.
+  // Latent side: one wave per 32 latents, groups of 4 or 8 waves; about 512 workgroups over the token
+  // chunks (a sweep of 256-4096 at the four bf16 workloads: 512 was within 2% of the best at each;
+  // more chunks cost the latent kernels and their reductions more than they gain in occupancy).
   p.lat_nw = flarepp::bwd_latent_waves(p.Mp);
 
   p.lat_nlg = (int)ceil_div(p.Mp, 32 * p.lat_nw);
-  const int64_t target = env_int("FLAREPP_BWD_LATENT_WORKGROUPS", p.lat_nw == 8 ? 1024 : 2048);
+  const int64_t target = env_int("FLAREPP_BWD_LATENT_WORKGROUPS", 512);
   int64_t nchunk = ceil_div(target, (int64_t)BH * p.lat_nlg);
   const int64_t stage = flarepp::bwd_stage(dtype, p.lat_nw);
   const int64_t max_chunks = ceil_div(N, stage);
@@ -489,7 +490,7 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.lat_chunk = ceil_div(ceil_div(N, nchunk), stage) * stage;
   p.lat_nchunk = (int)ceil_div(N, p.lat_chunk);
   p.lat_gx = p.lat_nlg == 1 ? p.lat_nchunk : (int)(ceil_div(p.lat_nchunk, 8) * 8 * p.lat_nlg);
-  // Token side: about 512 workgroups, 32-token blocks. The latent tensors in LDS leave room for one
+  // Token side: 256 or 512 workgroups, 32-token blocks. The latent tensors in LDS leave room for one
   // workgroup per CU: 12 waves (3 per SIMD) for encode and synthesis, and for the decode kernel
   // where its registers allow (bwd_decode_waves).
   const int tok_env = env_int("FLAREPP_BWD_TOKEN_WAVES", 0);
@@ -497,7 +498,10 @@ BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   p.tok_dec_nw = flarepp::bwd_decode_waves(dtype);
   const int dec_env = env_int("FLAREPP_BWD_DECODE_WAVES", 0);
   if (dec_env == 8 || (dec_env == 12 && dtype == FLAREPP_BF16)) p.tok_dec_nw = dec_env;
-  const int64_t tok_target = env_int("FLAREPP_BWD_TOKEN_WORKGROUPS", 512);
+  // One workgroup per CU (256) unless each (b, h) has more than 2^27 token-latent pairs; there two
+  // rounds of 512 ran 2-4% faster (a sweep of 128-1024 at the four bf16 workloads).
+  const int64_t tok_target =
+      env_int("FLAREPP_BWD_TOKEN_WORKGROUPS", N * (int64_t)p.Mp > ((int64_t)1 << 27) ? 512 : 256);
   int64_t gx = ceil_div(tok_target, (int64_t)BH);
   const int64_t max_gx = ceil_div(N, (int64_t)32 * flarepp::kBwdTokenWaves);
   if (gx > max_gx) gx = max_gx;

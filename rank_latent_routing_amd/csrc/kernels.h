@@ -129,6 +129,7 @@ struct BwdReduceArgs {
   const float* part0;
   const float* part1;
   int nchunk, M, Mp, H, B;
+  int split;          // waves per range of 64 entries (1 or 4), set by the launcher
   // decode -> encode
   const float* Z32;   // [BH][M][D] fp32 Z
   float* dZ32;        // [BH][Mp][D]
