@@ -174,6 +174,18 @@ def test_bwd_cfg5_shape_one_head():
     _check(make_workload(5, H=1, N=65536), label="cfg5 N=65536 H=1")
 
 
+@pytest.mark.parametrize("tok,lat", [("32", "8"), ("2048", "4096")])
+def test_bwd_launch_plans(monkeypatch, tok, lat):
+    # Workgroup counts other than the defaults: one token chunk per latent group (every reduction
+    # sums one partial per entry, one wave per 64 entries) or 79 chunks (the four waves of a
+    # reduction block split them), with few or many token-side workgroups.
+    monkeypatch.setenv("FLAREPP_BWD_TOKEN_WORKGROUPS", tok)
+    monkeypatch.setenv("FLAREPP_BWD_LATENT_WORKGROUPS", lat)
+    w = make_workload(4, B=2, H=2, N=20000, M=300, seed=78)
+    _check(w, label=f"bwd plan tok={tok} lat={lat}")
+    _check(w, label=f"bwd plan tok={tok} lat={lat} saved", runner=run_saved)
+
+
 def test_bwd_full_cfg5_one_head():
     # The 1M-token workload at its full size (B = 1, H = 8, N = 2^20, M = 512), in the launch
     # configuration the benchmark times; head 3 against the token-blocked oracle: dK, dV and dS at
