@@ -61,7 +61,9 @@ struct Plan {
   size_t off_acc = 0, off_l = 0, off_m = 0, off_q = 0, off_z = 0, total = 0;
 };
 
-Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
+// hilo: the plan of the backward's recompute and of the saved forward, whose partial kernels take the
+// hi/lo instance.
+Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype, bool hilo = false) {
   Plan p;
   p.BH = B * H;
   p.H = H;
@@ -76,12 +78,15 @@ Plan make_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   if (plan_env >= 0 && plan_env <= 3 && !(plan_env == 3 && dtype == FLAREPP_FP32)) p.part_plan = plan_env;
   const flarepp::PartialShape ps = flarepp::partial_plan_shape(p.part_plan);
   p.nlg = (int)ceil_div(p.Mp16, (int64_t)ps.lpw * ps.nw);
-  // Workgroups over the token chunks: 256 for 16-wave groups (1 per CU: one round), 512 for 8- and
-  // 4-wave groups (2 and 4 per CU). Fewer chunks make the merges cheaper, which outweighs the
-  // partials' lower occupancy. Measured per call: 1M-token workload 2.04 -> 2.02 ms (against 512),
-  // M = 256 (8-wave) 0.219 -> 0.200 ms and M = 128 (4-wave) 0.174 -> 0.161 ms (against 1024 and
-  // 2048), M = 64 (4-wave) 0.068 -> 0.059 ms.
-  const int64_t target = env_int("FLAREPP_PARTIAL_WORKGROUPS", ps.nw == 16 ? 256 : 512);
+  // Workgroups over the token chunks: 256 for 16-wave groups (1 per CU), and for the 8-wave groups of
+  // the plain forward (2 per CU); 512 otherwise. Fewer chunks make the merges cheaper, which
+  // outweighs the partials' lower occupancy down to these counts. Measured per call: 1M-token
+  // workload 2.04 -> 2.02 ms (against 512), M = 256 (8-wave) 0.219 -> 0.200 ms (512 against 1024 and
+  // 2048) and 0.214-0.222 -> 0.204-0.210 ms (256 against 512, same box; the hi/lo instances there
+  // took 103 + 93 us at 512 and 112 + 99 us at 256), M = 128 (4-wave) 0.174 -> 0.161 ms (512
+  // against 1024 and 2048; 256 took 0.174), M = 64 (4-wave) 0.068 -> 0.059 ms (512; 256 took 0.071).
+  const int64_t target =
+      env_int("FLAREPP_PARTIAL_WORKGROUPS", ps.nw == 16 || (ps.nw == 8 && !hilo) ? 256 : 512);
   int64_t nchunk = ceil_div(target, (int64_t)p.BH * p.nlg);
   nchunk = nchunk < 1 ? 1 : nchunk;
   // At most 2048 chunks: the merge keeps a row block's chunk weights in LDS (16 rows x 2048 x 4 B).
@@ -472,7 +477,7 @@ struct BwdPlan {
 
 BwdPlan make_bwd_plan(int B, int H, int64_t N, int M, int D, int dtype) {
   BwdPlan p;
-  p.f = make_plan(B, H, N, M, D, dtype);
+  p.f = make_plan(B, H, N, M, D, dtype, true);
   const int BH = p.f.BH;
   p.Mp = p.f.Mp32;
   // Latent side: one wave per 32 latents, groups of 4 or 8 waves; about 512 workgroups over the token
