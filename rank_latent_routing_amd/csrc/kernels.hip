@@ -1561,9 +1561,14 @@ __global__ __launch_bounds__(NW * 64) void decode_wide_kernel(DecodeArgs a) {
         const bf16x8 dsel = kSumsOnMfma ? sum_selector(lane) : bf16x8{};
         auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
         struct QOp { f16x8 a, b; };
+        // The lane's query row in block 0 as an LDS address; block lb adds a wave-uniform offset
+        // (one 32-bit add per block instead of a generic-pointer multiply-add).
+        typedef __attribute__((address_space(3))) const f16x8 lds_f16x8;
+        typedef __attribute__((address_space(3))) const char lds_char;
+        lds_char* const qlane = (lds_char*)(qh + col * QHS + 8 * h);
         auto load_q = [&](int lb) __attribute__((always_inline)) {
-          const f16* qrow = qh + (32 * lb + col) * QHS + 8 * h;
-          return QOp{*reinterpret_cast<const f16x8*>(qrow), *reinterpret_cast<const f16x8*>(qrow + 16)};
+          lds_f16x8* qrow = (lds_f16x8*)(qlane + lb * (32 * QHS * (int)sizeof(f16)));
+          return QOp{qrow[0], qrow[2]};
         };
         auto exps = [&](f32x16& x, int v0) __attribute__((always_inline)) {
 #pragma unroll
